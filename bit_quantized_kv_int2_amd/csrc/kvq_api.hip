@@ -1,0 +1,318 @@
+// Host side of the C ABI: argument checks (before any HIP call), split
+// planning, workspace carving and kernel launches on the caller's stream.
+#include <math.h>
+#include <string.h>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+static thread_local int32_t g_last_hip_error = 0;
+
+static kvq_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return KVQ_OK;
+  g_last_hip_error = (int32_t)e;
+  return KVQ_ERR_HIP;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+extern "C" {
+
+const char* kvq_status_string(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_NULL_POINTER: return "null pointer";
+    case KVQ_ERR_BAD_FORMAT: return "unsupported format";
+    case KVQ_ERR_BAD_SHAPE: return "bad shape";
+    case KVQ_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
+    case KVQ_ERR_WORKSPACE: return "workspace too small";
+    case KVQ_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t kvq_last_hip_error(void) { return g_last_hip_error; }
+
+uint32_t kvq_layout_version(void) { return KVQ_LAYOUT_VERSION; }
+
+kvq_status kvq_check_format(const kvq_format* f) {
+  if (!f) return KVQ_ERR_NULL_POINTER;
+  if (f->layout_version != KVQ_LAYOUT_VERSION) return KVQ_ERR_BAD_FORMAT;
+  if (f->bits != 2 && f->bits != 4) return KVQ_ERR_BAD_FORMAT;
+  if (f->k_axis != KVQ_TOKEN_WISE && f->k_axis != KVQ_CHANNEL_WISE) return KVQ_ERR_BAD_FORMAT;
+  if (f->v_axis != KVQ_TOKEN_WISE && f->v_axis != KVQ_CHANNEL_WISE) return KVQ_ERR_BAD_FORMAT;
+  if (f->group != kGroup || f->head_dim != kHeadDim) return KVQ_ERR_BAD_FORMAT;
+  if (f->num_kv_heads < 1 || f->num_kv_heads > 65535) return KVQ_ERR_BAD_FORMAT;
+  if (f->num_q_heads != kGqa * f->num_kv_heads) return KVQ_ERR_BAD_FORMAT;
+  if (f->page_size != 0 && f->page_size != kPage) return KVQ_ERR_BAD_FORMAT;
+  return KVQ_OK;
+}
+
+static int padded_len(int max_len) { return ((max_len + kGroup - 1) / kGroup) * kGroup; }
+
+kvq_status kvq_cache_sizes(const kvq_format* f, int32_t batch, int32_t max_len,
+                           int32_t num_pages, size_t bytes[4]) {
+  kvq_status st = kvq_check_format(f);
+  if (st != KVQ_OK) return st;
+  if (!bytes) return KVQ_ERR_NULL_POINTER;
+  const size_t H = (size_t)f->num_kv_heads, D = kHeadDim, b = (size_t)f->bits;
+  size_t tokens;  // token rows per head-slot array
+  size_t groups;  // channel-wise pair rows
+  if (f->page_size == 0) {
+    if (batch < 0 || max_len < 0) return KVQ_ERR_BAD_SHAPE;
+    tokens = (size_t)batch * H * (size_t)padded_len(max_len);
+    groups = (size_t)batch * H * (size_t)(padded_len(max_len) / kGroup);
+  } else {
+    if (num_pages < 0) return KVQ_ERR_BAD_SHAPE;
+    tokens = (size_t)num_pages * H * kPage;
+    groups = (size_t)num_pages * H;
+  }
+  bytes[0] = tokens * D * b / 8;
+  bytes[1] = tokens * D * b / 8;
+  bytes[2] = (f->k_axis == KVQ_TOKEN_WISE ? tokens * 4 : groups * D * 4);
+  bytes[3] = (f->v_axis == KVQ_TOKEN_WISE ? tokens * 4 : groups * D * 4);
+  return KVQ_OK;
+}
+
+// Token split per (sequence, KV head): a multiple of kSplitQuantum tokens,
+// at most kMaxSplitTokens (the per-split fold operands sit in LDS), and
+// enough workgroups to fill 256 CUs several times over.
+static int plan_split_tokens(int batch, int num_kv_heads, int max_len, int num_splits) {
+  if (max_len <= 0) return kSplitQuantum;
+  const int quanta = (max_len + kSplitQuantum - 1) / kSplitQuantum;
+  if (num_splits <= 0) {
+    const long units = (long)batch * num_kv_heads;
+    const long want_groups = 1536;
+    long ns = (want_groups + units - 1) / units;
+    long ns_min = (max_len + kMaxSplitTokens - 1) / kMaxSplitTokens;
+    if (ns < ns_min) ns = ns_min;
+    if (ns > quanta) ns = quanta;
+    num_splits = (int)ns;
+  }
+  int q_per = (quanta + num_splits - 1) / num_splits;
+  int st = q_per * kSplitQuantum;
+  if (st > kMaxSplitTokens) st = kMaxSplitTokens;
+  return st;
+}
+
+static int splits_for(int max_len, int split_tokens) {
+  if (max_len <= 0) return 1;
+  return (max_len + split_tokens - 1) / split_tokens;
+}
+
+kvq_status kvq_plan_splits(const kvq_format* f, int32_t batch, int32_t max_len,
+                           int32_t* num_splits) {
+  kvq_status st = kvq_check_format(f);
+  if (st != KVQ_OK) return st;
+  if (!num_splits) return KVQ_ERR_NULL_POINTER;
+  if (batch < 0 || max_len < 0) return KVQ_ERR_BAD_SHAPE;
+  *num_splits = splits_for(max_len, plan_split_tokens(batch, f->num_kv_heads, max_len, 0));
+  return KVQ_OK;
+}
+
+static kvq_status resolve_splits(const kvq_format* f, int batch, int max_len, int req,
+                                 int* split_tokens, int* nsplit) {
+  if (req < 0) return KVQ_ERR_BAD_SHAPE;
+  int quanta = max_len > 0 ? (max_len + kSplitQuantum - 1) / kSplitQuantum : 1;
+  int min_splits = max_len > 0 ? (max_len + kMaxSplitTokens - 1) / kMaxSplitTokens : 1;
+  if (req > 0 && (req > quanta || req < min_splits)) return KVQ_ERR_BAD_SHAPE;
+  *split_tokens = plan_split_tokens(batch, f->num_kv_heads, max_len, req);
+  *nsplit = splits_for(max_len, *split_tokens);
+  return KVQ_OK;
+}
+
+static size_t workspace_bytes_for(const kvq_format* f, int batch, int nsplit) {
+  if (nsplit <= 1) return 0;
+  const size_t rows = (size_t)batch * f->num_q_heads;
+  return rows * nsplit * (kHeadDim + 2) * sizeof(float);
+}
+
+kvq_status kvq_workspace_size(const kvq_format* f, int32_t batch, int32_t max_len,
+                              int32_t num_splits, size_t* bytes) {
+  kvq_status st = kvq_check_format(f);
+  if (st != KVQ_OK) return st;
+  if (!bytes) return KVQ_ERR_NULL_POINTER;
+  if (batch < 0 || max_len < 0) return KVQ_ERR_BAD_SHAPE;
+  int split_tokens, nsplit;
+  st = resolve_splits(f, batch, max_len, num_splits, &split_tokens, &nsplit);
+  if (st != KVQ_OK) return st;
+  *bytes = workspace_bytes_for(f, batch, nsplit);
+  return KVQ_OK;
+}
+
+static kvq_status check_cache_ptrs(const kvq_cache* c) {
+  if (!c) return KVQ_ERR_NULL_POINTER;
+  if (!c->k_codes || !c->v_codes || !c->k_scale_offset || !c->v_scale_offset)
+    return KVQ_ERR_NULL_POINTER;
+  if (!aligned16(c->k_codes) || !aligned16(c->v_codes) || !aligned16(c->k_scale_offset) ||
+      !aligned16(c->v_scale_offset))
+    return KVQ_ERR_MISALIGNED;
+  return KVQ_OK;
+}
+
+static kvq_status check_common(const kvq_format* f, const int32_t* seq_lens,
+                               const int32_t* page_table, int32_t max_pages, int32_t batch,
+                               int32_t max_len) {
+  if (!seq_lens) return KVQ_ERR_NULL_POINTER;
+  if (!aligned16(seq_lens)) return KVQ_ERR_MISALIGNED;
+  if (batch < 0 || batch > 65535 || max_len < 0 || max_len > (1 << 30)) return KVQ_ERR_BAD_SHAPE;
+  if (f->page_size != 0) {
+    if (!page_table) return KVQ_ERR_NULL_POINTER;
+    if (!aligned16(page_table)) return KVQ_ERR_MISALIGNED;
+    if (max_pages < (max_len + kPage - 1) / kPage || max_pages < 1) return KVQ_ERR_BAD_SHAPE;
+  }
+  return KVQ_OK;
+}
+
+kvq_status kv_quantize_pack(const kvq_format* f, const float* k, const float* v,
+                            const int32_t* seq_lens, const int32_t* page_table,
+                            int32_t max_pages_per_seq, int32_t batch, int32_t max_len,
+                            const kvq_cache* out, void* stream) {
+  kvq_status st = kvq_check_format(f);
+  if (st != KVQ_OK) return st;
+  if (!k || !v) return KVQ_ERR_NULL_POINTER;
+  if (!aligned16(k) || !aligned16(v)) return KVQ_ERR_MISALIGNED;
+  st = check_cache_ptrs(out);
+  if (st != KVQ_OK) return st;
+  st = check_common(f, seq_lens, page_table, max_pages_per_seq, batch, max_len);
+  if (st != KVQ_OK) return st;
+  if (batch == 0 || max_len == 0) return KVQ_OK;
+  PackArgs a;
+  memset(&a, 0, sizeof a);
+  a.k = k;
+  a.v = v;
+  a.seq_lens = seq_lens;
+  a.page_table = f->page_size ? page_table : nullptr;
+  a.max_pages = max_pages_per_seq;
+  a.batch = batch;
+  a.max_len = max_len;
+  a.num_kv_heads = f->num_kv_heads;
+  a.bits = f->bits;
+  a.k_axis = f->k_axis;
+  a.v_axis = f->v_axis;
+  a.paged = f->page_size != 0;
+  a.padded_len = padded_len(max_len);
+  a.k_codes = (uint8_t*)out->k_codes;
+  a.v_words = (uint32_t*)out->v_codes;
+  a.k_sz = (uint16_t*)out->k_scale_offset;
+  a.v_sz = (uint16_t*)out->v_scale_offset;
+  return hip_status(launch_pack(a, (hipStream_t)stream));
+}
+
+static kvq_status check_out(const void* q, void* out, int32_t out_dtype) {
+  if (!q || !out) return KVQ_ERR_NULL_POINTER;
+  if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_MISALIGNED;
+  if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_BF16) return KVQ_ERR_BAD_FORMAT;
+  return KVQ_OK;
+}
+
+kvq_status decode_attention_quant(const kvq_format* f, const void* q, const kvq_cache* cache,
+                                  const int32_t* seq_lens, const int32_t* page_table,
+                                  int32_t max_pages_per_seq, int32_t batch, int32_t max_len,
+                                  float softmax_scale, void* out, int32_t out_dtype,
+                                  int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  kvq_status st = kvq_check_format(f);
+  if (st != KVQ_OK) return st;
+  st = check_out(q, out, out_dtype);
+  if (st != KVQ_OK) return st;
+  st = check_cache_ptrs(cache);
+  if (st != KVQ_OK) return st;
+  st = check_common(f, seq_lens, page_table, max_pages_per_seq, batch, max_len);
+  if (st != KVQ_OK) return st;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVQ_ERR_BAD_SHAPE;
+  int split_tokens, nsplit;
+  st = resolve_splits(f, batch, max_len, num_splits, &split_tokens, &nsplit);
+  if (st != KVQ_OK) return st;
+  size_t need = workspace_bytes_for(f, batch, nsplit);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KVQ_ERR_MISALIGNED;
+  }
+  if (batch == 0) return KVQ_OK;
+  DecodeArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = (const uint16_t*)q;
+  a.k_codes = (const uint8_t*)cache->k_codes;
+  a.v_words = (const uint32_t*)cache->v_codes;
+  a.k_sz = (const uint16_t*)cache->k_scale_offset;
+  a.v_sz = (const uint16_t*)cache->v_scale_offset;
+  a.seq_lens = seq_lens;
+  a.page_table = f->page_size ? page_table : nullptr;
+  a.max_pages = max_pages_per_seq;
+  a.batch = batch;
+  a.num_kv_heads = f->num_kv_heads;
+  a.max_len = max_len;
+  a.padded_len = padded_len(max_len);
+  a.split_tokens = split_tokens;
+  a.num_splits = nsplit;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.out = out;
+  a.out_bf16 = out_dtype == KVQ_OUT_BF16;
+  if (nsplit > 1) {
+    const size_t rows = (size_t)batch * f->num_q_heads;
+    a.part_o = (float*)workspace;
+    a.part_ml = a.part_o + rows * nsplit * kHeadDim;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  st = hip_status(launch_decode_quant(*f, a, s));
+  if (st != KVQ_OK || nsplit == 1) return st;
+  return hip_status(launch_combine(a.part_o, a.part_ml, batch * f->num_q_heads, nsplit, out,
+                                   a.out_bf16, s));
+}
+
+kvq_status decode_attention_bf16(const kvq_format* f, const void* q, const void* k,
+                                 const void* v, const int32_t* seq_lens,
+                                 const int32_t* page_table, int32_t max_pages_per_seq,
+                                 int32_t batch, int32_t max_len, float softmax_scale, void* out,
+                                 int32_t out_dtype, int32_t num_splits, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  kvq_status st = kvq_check_format(f);
+  if (st != KVQ_OK) return st;
+  st = check_out(q, out, out_dtype);
+  if (st != KVQ_OK) return st;
+  if (!k || !v) return KVQ_ERR_NULL_POINTER;
+  if (!aligned16(k) || !aligned16(v)) return KVQ_ERR_MISALIGNED;
+  st = check_common(f, seq_lens, page_table, max_pages_per_seq, batch, max_len);
+  if (st != KVQ_OK) return st;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVQ_ERR_BAD_SHAPE;
+  int split_tokens, nsplit;
+  st = resolve_splits(f, batch, max_len, num_splits, &split_tokens, &nsplit);
+  if (st != KVQ_OK) return st;
+  size_t need = workspace_bytes_for(f, batch, nsplit);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return KVQ_ERR_MISALIGNED;
+  }
+  if (batch == 0) return KVQ_OK;
+  Bf16Args a;
+  memset(&a, 0, sizeof a);
+  a.q = (const uint16_t*)q;
+  a.k = (const uint16_t*)k;
+  a.v = (const uint16_t*)v;
+  a.seq_lens = seq_lens;
+  a.page_table = f->page_size ? page_table : nullptr;
+  a.max_pages = max_pages_per_seq;
+  a.batch = batch;
+  a.num_kv_heads = f->num_kv_heads;
+  a.max_len = max_len;
+  a.page_size = f->page_size;
+  a.split_tokens = split_tokens;
+  a.num_splits = nsplit;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.out = out;
+  a.out_bf16 = out_dtype == KVQ_OUT_BF16;
+  if (nsplit > 1) {
+    const size_t rows = (size_t)batch * f->num_q_heads;
+    a.part_o = (float*)workspace;
+    a.part_ml = a.part_o + rows * nsplit * kHeadDim;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  st = hip_status(launch_decode_bf16(a, s));
+  if (st != KVQ_OK || nsplit == 1) return st;
+  return hip_status(launch_combine(a.part_o, a.part_ml, batch * f->num_q_heads, nsplit, out,
+                                   a.out_bf16, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,678 @@
+// Split-KV decode attention over INT2/INT4 quantised KV caches, gfx950.
+//
+// Method (FOSCAR, arXiv:2611.09722; rag-lover.com explainer, limits section):
+// the per-group affine map x = s*c + z is never applied per element.
+//   q.K^T contracts over channels:
+//     token-wise K   (acc-fold):     S_t = s_t * (q . c_t) + z_t * sum(q)
+//     channel-wise K (operand-fold): S_t = (q*s_i) . c_t + sum_d q_d z_{i,d}
+//   P.V contracts over tokens:
+//     token-wise V   (operand-fold): O   = sum_t (P_t s_t) c_t + sum_t P_t z_t
+//     channel-wise V (acc-fold):     O_d = sum_i s_{i,d} (sum_{t in i} P_t c_{t,d})
+//                                          + z_{i,d} sum_{t in i} P_t,
+//                                    scaled per 128-token group, never across groups.
+//
+// gfx950 mapping
+//   * Matrix unit: v_mfma_f32_16x16x32_f16. A = codes (16 rows x 32 k),
+//     B = folded query / probabilities (32 k x 16 columns); the 4 query heads
+//     of a KV head fill columns 0-3 and are repeated in columns 4-15.
+//   * Operand construction: a 2- or 4-bit code ANDed out of its packed 32-bit
+//     word, left at its bit offset inside a 16-bit lane with every other bit
+//     zero, is the binary16 subnormal c * 2^k * 2^-24 (k = the code's bit
+//     offset within its byte). Unpacking costs one AND per two codes plus one
+//     shift per word: 5 ops per 8 INT4 codes, 9 per 16 INT2 codes, no base
+//     constant to cancel later. The 2^k weight is divided out of the other
+//     operand (an exact power of two).
+//   * Consistent offsets: every offset term is computed from the rounded
+//     fp16 operand the matrix unit actually consumed, so rounding q*s or P*s
+//     to fp16 perturbs only the weights, not the cancellation between the
+//     code term and the offset term.
+//   * Token <-> tile maps are chosen so the QK^T accumulator layout is the PV
+//     B-operand layout: no cross-lane shuffles between the two products.
+//   * Per split (a multiple of 256 tokens, at most 2048), a prologue builds
+//     the fold operands in LDS: q*s per K group (channel-wise K) or q
+//     (token-wise K), per-token or per-group V coefficients. Four waves then
+//     stream 32 (INT4) or 64 (INT2) tokens per iteration each: 128-bit /
+//     64-bit coalesced code loads one iteration ahead, online softmax with a
+//     lazily moved maximum, and the (m, l, O) of the four waves are merged
+//     through LDS.
+//   * Extra PV tile: a 9th A tile whose rows hold hi/lo fp16 parts of the
+//     token-wise-V offset coefficient (or the subnormal "code 1" pattern for
+//     channel-wise V) gives sum_t P_t r_t (or sum_t P_t) from the same rounded
+//     P that feeds the data tiles.
+#include <math.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kThr = 8;          // lazy-max threshold in log2 units: P <= 2^kThr
+constexpr int kMaxGroups = kMaxSplitTokens / kGroup;
+
+__device__ inline h8 as_h8(u4 v) { return __builtin_bit_cast(h8, v); }
+__device__ inline f4 mfma(u4 a, u4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a), as_h8(b), c, 0, 0, 0);
+}
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline uint32_t pack_f16x2(float lo, float hi) {
+  _Float16 a = (_Float16)lo, b = (_Float16)hi;  // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ inline float f16lo(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFF)); }
+__device__ inline float f16hi(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16)); }
+__device__ inline float f16val(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
+__device__ inline float bf16val(uint16_t u) { return __builtin_bit_cast(float, (uint32_t)u << 16); }
+
+__device__ inline float wave_max(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ inline float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// exponent e with x < 2^e (x > 0), 0 for x == 0
+__device__ inline int exp_above(float x) { return x > 0.f ? ilogbf(x) + 1 : 0; }
+
+// Unpack one 32-bit word of INT4 codes into one k-step of fp16 subnormals:
+// VGPR m holds codes (m, m+4), weight 16^(m&1).
+__device__ inline u4 unpack4(uint32_t w) {
+  uint32_t t = w >> 8;
+  return u4{w & 0x000F000Fu, w & 0x00F000F0u, t & 0x000F000Fu, t & 0x00F000F0u};
+}
+// Unpack one 32-bit word of INT2 codes into two k-steps: sel 0 from w, sel 1
+// from w >> 8; VGPR m of sel holds codes (4 sel + m, 8 + 4 sel + m), weight 4^m.
+__device__ inline u4 unpack2(uint32_t w, int sel) {
+  uint32_t t = sel ? (w >> 8) : w;
+  return u4{t & 0x00030003u, t & 0x000C000Cu, t & 0x00300030u, t & 0x00C000C0u};
+}
+
+template <int BITS>
+struct Cfg {
+  static constexpr int TPW = 32 / BITS;        // tokens per V word
+  static constexpr int NT = TPW / 4;           // QK tiles per iteration
+  static constexpr int TIT = 4 * TPW;          // tokens per wave iteration
+  static constexpr int NK = TPW / 8;           // PV k-steps per iteration
+  static constexpr int KROW = kHeadDim * BITS / 8;  // bytes per K token row
+  static constexpr int SLOTS = 8 / BITS;       // codes per byte
+  // bit offset inside its byte of element (m, *) of a k-step: weight 2^(BITS*(m % SLOTS))
+  __device__ static inline float inv_w(int m) { return 1.0f / (float)(1 << (BITS * (m % SLOTS))); }
+  __device__ static inline float w(int m) { return (float)(1 << (BITS * (m % SLOTS))); }
+  // channel fed by element (m, hf) of k-step s in lane group g
+  __device__ static inline int k_channel(int s, int g, int m, int hf) {
+    if (BITS == 4) return 32 * g + 8 * s + m + 4 * hf;
+    return 32 * g + 16 * (s >> 1) + 4 * (s & 1) + m + 8 * hf;
+  }
+};
+
+// LDS layout (bytes), sized for the largest split.
+template <int KAX, int VAX>
+struct Lds {
+  static constexpr int QS = 0;                                   // float [4][128]
+  static constexpr int QB = QS + 4 * 128 * 4;                    // u4 [groups][4][4 s][4 g]
+  static constexpr int QB_BYTES = (KAX == KVQ_CHANNEL_WISE ? kMaxGroups : 1) * 4 * 16 * 16;
+  static constexpr int KB = QB + QB_BYTES;                       // chan-K bias [groups][4] / tok-K (s',z'') [tokens][2]
+  static constexpr int KB_BYTES = KAX == KVQ_CHANNEL_WISE ? kMaxGroups * 4 * 4 : kMaxSplitTokens * 8;
+  static constexpr int VA = KB + KB_BYTES;                       // tok-V coef [tokens] / chan-V (sigma,rho) [groups][128]
+  static constexpr int VA_BYTES = VAX == KVQ_TOKEN_WISE ? kMaxSplitTokens * 4 : kMaxGroups * 128 * 8;
+  static constexpr int VR = VA + VA_BYTES;                       // tok-V rho hi/lo, A-operand order, fp16 [2][tokens] + 16 B zero
+  static constexpr int VR_BYTES = VAX == KVQ_TOKEN_WISE ? 2 * kMaxSplitTokens * 2 + 16 : 0;
+  static constexpr int RED = VR + VR_BYTES;                      // float [16] reductions + [4] Q sums
+  static constexpr int TOTAL = RED + 32 * 4;
+  // merge area reuses the front of LDS after the main loop
+  static constexpr int MO = 0;                                   // float [4 waves][4 heads][128]
+  static constexpr int ML = MO + 4 * 4 * 128 * 4;                // float [4 waves][4 heads][2]
+  static_assert(ML + 4 * 4 * 2 * 4 <= RED, "merge area overlaps reductions");
+};
+
+template <int BITS, int KAX, int VAX, bool PAGED>
+__global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
+  using C = Cfg<BITS>;
+  using M = Lds<KAX, VAX>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[M::TOTAL];
+  float* qs = (float*)(lds + M::QS);
+  float* red = (float*)(lds + M::RED);
+
+  const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int H = a.num_kv_heads, Hq = H * kGqa;
+  const int L = min(max(a.seq_lens[b], 0), a.max_len);  // contract: 0 <= len <= max_len
+  const int tb = sp * a.split_tokens;
+  const int te = min(tb + a.split_tokens, L);
+  const long row0 = (long)b * Hq + (long)h * kGqa;  // first query head row of this KV head
+
+  if (te <= tb) {  // nothing in this split (or an empty sequence)
+    for (int e = tid; e < kGqa * kHeadDim; e += kThreads) {
+      int hh = e / kHeadDim, d = e % kHeadDim;
+      if (a.num_splits == 1) {
+        if (a.out_bf16) ((uint16_t*)a.out)[(row0 + hh) * kHeadDim + d] = 0;
+        else ((float*)a.out)[(row0 + hh) * kHeadDim + d] = 0.f;
+      } else {
+        a.part_o[((row0 + hh) * a.num_splits + sp) * kHeadDim + d] = 0.f;
+        if (d == 0) {
+          a.part_ml[((row0 + hh) * a.num_splits + sp) * 2] = -INFINITY;
+          a.part_ml[((row0 + hh) * a.num_splits + sp) * 2 + 1] = 0.f;
+        }
+      }
+    }
+    return;
+  }
+  const int ntok = te - tb;
+  const int ng = (ntok + kGroup - 1) / kGroup;
+  const float alpha = a.scale_log2;
+
+  // ---- cache addressing -------------------------------------------------
+  const long unit = (long)b * H + h;
+  auto chunk_of = [&](int t) -> long {  // 64-token chunk of token t
+    if (!PAGED) return unit * (a.padded_len / kPage) + t / kPage;
+    return (long)a.page_table[(long)b * a.max_pages + t / kPage] * H + h;
+  };
+  auto ksz_chan = [&](int t0, int d) -> const uint16_t* {  // pair of (group of t0, channel d)
+    if (!PAGED) return a.k_sz + ((unit * (a.padded_len / kGroup) + t0 / kGroup) * kHeadDim + d) * 2;
+    return a.k_sz + (chunk_of(t0) * kHeadDim + d) * 2;
+  };
+  auto vsz_chan = [&](int t0, int d) -> const uint16_t* {
+    if (!PAGED) return a.v_sz + ((unit * (a.padded_len / kGroup) + t0 / kGroup) * kHeadDim + d) * 2;
+    return a.v_sz + (chunk_of(t0) * kHeadDim + d) * 2;
+  };
+  auto ksz_tok = [&](int t) -> const uint16_t* { return a.k_sz + (chunk_of(t) * kPage + t % kPage) * 2; };
+  auto vsz_tok = [&](int t) -> const uint16_t* { return a.v_sz + (chunk_of(t) * kPage + t % kPage) * 2; };
+
+  // lane roles
+  const int n = lane & 15, g = lane >> 4, hh = n & 3;
+  const int ri = lane & 15;  // A-operand row
+
+  // ---- code loads for one iteration -----------------------------------
+  struct Codes {
+    uint32_t k[C::NT][BITS == 4 ? 4 : 2];
+    u4 v[2];
+  };
+  auto load_codes = [&](int t0, Codes& cd) {
+    const long ch = chunk_of(t0);
+    const int tt0 = t0 % kPage;
+    #pragma unroll
+    for (int T = 0; T < C::NT; ++T) {
+      const int tok = tt0 + C::TPW * (ri >> 2) + 4 * T + (ri & 3);
+      const unsigned char* p = a.k_codes + (ch * kPage + tok) * C::KROW;
+      if (BITS == 4) {
+        u4 x = *(const u4*)(p + 16 * g);
+        cd.k[T][0] = x[0]; cd.k[T][1] = x[1]; cd.k[T][2] = x[2]; cd.k[T][3] = x[3];
+      } else {
+        u2 x = *(const u2*)(p + 8 * g);
+        cd.k[T][0] = x[0]; cd.k[T][1] = x[1];
+      }
+    }
+    const uint32_t* vp = a.v_words + ((ch * (kPage / C::TPW) + tt0 / C::TPW + g) * kHeadDim + 8 * ri);
+    cd.v[0] = *(const u4*)vp;
+    cd.v[1] = *(const u4*)(vp + 4);
+  };
+
+  // first iteration's codes go out before the prologue
+  Codes cur;
+  {
+    const int t0 = tb + wv * C::TIT;
+    if (t0 < te) load_codes(t0, cur);
+  }
+
+  // ---- prologue pass 1: q, maxima -----------------------------------------
+  {
+    const int d = lane * 2;  // wave wv loads query head wv
+    uint32_t qq = *(const uint32_t*)(a.q + (row0 + wv) * kHeadDim + d);
+    float q0 = bf16val((uint16_t)(qq & 0xFFFF)), q1 = bf16val((uint16_t)(qq >> 16));
+    qs[wv * 128 + d] = q0;
+    qs[wv * 128 + d + 1] = q1;
+    float m = wave_max(fmaxf(fabsf(q0), fabsf(q1)));
+    float sum = wave_sum(q0 + q1);
+    if (lane == 0) { red[wv] = m; red[20 + wv] = sum; }
+  }
+  if (KAX == KVQ_CHANNEL_WISE) {
+    float m = 0.f;  // largest K scale of the split
+    for (int e = tid; e < ng * kHeadDim; e += kThreads) {
+      const uint16_t* p = ksz_chan(tb + (e / kHeadDim) * kGroup, e % kHeadDim);
+      m = fmaxf(m, f16val(p[0]));
+    }
+    m = wave_max(m);
+    if (lane == 0) red[4 + wv] = m;
+  }
+  if (VAX == KVQ_TOKEN_WISE) {
+    float m = 0.f;
+    for (int r = tid; r < ntok; r += kThreads) {
+      float s = f16val(vsz_tok(tb + r)[0]);
+      m = fmaxf(m, s != 0.f ? s : 1.f);
+    }
+    m = wave_max(m);
+    if (lane == 0) red[8 + wv] = m;
+  }
+  __syncthreads();
+  const float qmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  int E = 0;  // q'' = (alpha q s | q) * 2^-E, max |q''| < 2^14
+  if (KAX == KVQ_CHANNEL_WISE) {
+    const float smax = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
+    E = exp_above(alpha * qmax * smax) - 14;
+  } else {
+    E = exp_above(qmax) - 14;
+  }
+  int F = kThr - 14;  // P'' = P * coef * 2^-F, max P'' < 2^14
+  if (VAX == KVQ_TOKEN_WISE) {
+    const float smax = fmaxf(fmaxf(red[8], red[9]), fmaxf(red[10], red[11]));
+    F = exp_above(smax) + kThr - 14;
+  }
+  const float two_mE = ldexpf(1.f, -E), two_E = ldexpf(1.f, E);
+  const float two_mF = ldexpf(1.f, -F);
+
+  // ---- prologue pass 2: fold operands into LDS ------------------------------
+  u4* qB = (u4*)(lds + M::QB);
+  if (KAX == KVQ_CHANNEL_WISE) {
+    // combo = (group, head, s, g); 16 consecutive threads share (group, head)
+    float* kbias = (float*)(lds + M::KB);
+    for (int c0 = 0; c0 < ng * 64; c0 += kThreads) {
+      const int c = c0 + tid;
+      const int p = c & 15, s = p >> 2, gg = p & 3;
+      const int gh = c >> 4, gi = gh >> 2, qh = gh & 3;
+      float bias = 0.f;
+      uint32_t wds[4] = {0, 0, 0, 0};
+      if (gi < ng) {
+        #pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          float part[2];
+          float qq[2];
+          float raw[2];
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int d = C::k_channel(s, gg, m, hf);
+            const uint16_t* pz = ksz_chan(tb + gi * kGroup, d);
+            const float sv = f16val(pz[0]), zv = f16val(pz[1]);
+            const float aq = alpha * qs[qh * 128 + d];
+            // s == 0: every code is 0, the group is the constant z
+            qq[hf] = sv != 0.f ? aq * sv * two_mE * C::inv_w(m) : 0.f;
+            part[hf] = sv != 0.f ? zv / sv : 0.f;
+            raw[hf] = sv != 0.f ? 0.f : aq * zv;
+          }
+          uint32_t pk = pack_f16x2(qq[0], qq[1]);
+          wds[m] = pk;
+          // consistent offset: the rounded operand (times its slot weight and
+          // 2^E) times z/s, so rounding q*s moves only the weight of x^
+          bias += (f16lo(pk) * part[0] + f16hi(pk) * part[1]) * (C::w(m) * two_E) + raw[0] + raw[1];
+        }
+        qB[((gi * 4 + qh) * 4 + s) * 4 + gg] = u4{wds[0], wds[1], wds[2], wds[3]};
+      }
+      bias += __shfl_xor(bias, 1);
+      bias += __shfl_xor(bias, 2);
+      bias += __shfl_xor(bias, 4);
+      bias += __shfl_xor(bias, 8);
+      if (gi < ng && p == 0) kbias[gi * 4 + qh] = bias;
+    }
+  } else {
+    if (tid < 64) {
+      const int s = (tid & 15) >> 2, gg = tid & 3, qh = tid >> 4;
+      uint32_t wds[4];
+      #pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        float v0 = qs[qh * 128 + C::k_channel(s, gg, m, 0)] * two_mE * C::inv_w(m);
+        float v1 = qs[qh * 128 + C::k_channel(s, gg, m, 1)] * two_mE * C::inv_w(m);
+        wds[m] = pack_f16x2(v0, v1);
+      }
+      qB[(qh * 4 + s) * 4 + gg] = u4{wds[0], wds[1], wds[2], wds[3]};
+    }
+    float2* ktok = (float2*)(lds + M::KB);
+    const int npad = ((ntok + C::TIT - 1) / C::TIT) * C::TIT;
+    const float sc = alpha * ldexpf(1.f, E + 24);
+    for (int r = tid; r < npad; r += kThreads) {
+      float2 v = make_float2(0.f, 0.f);
+      if (r < ntok) {
+        const uint16_t* pz = ksz_tok(tb + r);
+        v = make_float2(f16val(pz[0]) * sc, f16val(pz[1]) * alpha);
+      }
+      ktok[r] = v;
+    }
+  }
+  if (VAX == KVQ_TOKEN_WISE) {
+    float* coef = (float*)(lds + M::VA);
+    _Float16* rh = (_Float16*)(lds + M::VR);
+    _Float16* rl = rh + kMaxSplitTokens;
+    const int npad = ((ntok + C::TIT - 1) / C::TIT) * C::TIT;
+    for (int r = tid; r < npad; r += kThreads) {
+      float cf = 0.f, rw = 0.f;
+      const int j = r % C::TPW;
+      const float wt = (float)(1 << (BITS * (j % C::SLOTS)));
+      if (r < ntok) {
+        const uint16_t* pz = vsz_tok(tb + r);
+        float sv = f16val(pz[0]), zv = f16val(pz[1]);
+        float sig = sv != 0.f ? sv : 1.f;
+        float rho = sv != 0.f ? zv / sv : zv;
+        cf = sig * two_mF / wt;
+        rw = rho * wt;
+      }
+      coef[r] = cf;
+      // A-operand position of token r: (iteration, k-step, lane group, m, half)
+      const int it = r / C::TIT, rr = r % C::TIT;
+      const int gg = rr / C::TPW, hf = j / (C::TPW / 2), jj = j % (C::TPW / 2);
+      const int ks = jj / 4, m = jj % 4;
+      const int pos = ((it * C::NK + ks) * 4 + gg) * 8 + 2 * m + hf;
+      _Float16 hi = (_Float16)rw;
+      _Float16 lo = (_Float16)(rw - (float)hi);
+      rh[pos] = hi;
+      rl[pos] = lo;
+    }
+    if (tid < 8) ((_Float16*)(lds + M::VR + 2 * kMaxSplitTokens * 2))[tid] = (_Float16)0.f;
+  } else {
+    float2* vg = (float2*)(lds + M::VA);
+    for (int e = tid; e < ng * kHeadDim; e += kThreads) {
+      const uint16_t* pz = vsz_chan(tb + (e / kHeadDim) * kGroup, e % kHeadDim);
+      float sv = f16val(pz[0]), zv = f16val(pz[1]);
+      vg[e] = make_float2(sv != 0.f ? sv : 1.f, sv != 0.f ? zv / sv : zv);
+    }
+  }
+  __syncthreads();
+
+  // ---- main loop --------------------------------------------------------
+  f4 O[8];
+  #pragma unroll
+  for (int c = 0; c < 8; ++c) O[c] = f4{0.f, 0.f, 0.f, 0.f};
+  f4 X = f4{0.f, 0.f, 0.f, 0.f};  // extra tile accumulator
+  float m_run = -INFINITY;
+  float lsum = 0.f;
+  const float Qh = red[20 + hh];
+  const float sc_k = ldexpf(1.f, E + 24);
+
+  for (int it = wv;; it += kWaves) {
+    const int t0 = tb + it * C::TIT;
+    if (t0 >= te) break;
+    Codes nxt;
+    const int t1 = t0 + kWaves * C::TIT;
+    if (t1 < te) load_codes(t1, nxt);
+
+    const int rel = t0 - tb;
+    const int gi = rel / kGroup;
+
+    // QK^T: NT tiles of 16 tokens, 4 k-steps of 32 channels
+    f4 acc[C::NT];
+    {
+      const u4* qb = qB + ((KAX == KVQ_CHANNEL_WISE ? gi : 0) * 4 + hh) * 16;
+      u4 bq[4];
+      #pragma unroll
+      for (int s = 0; s < 4; ++s) bq[s] = qb[s * 4 + g];
+      #pragma unroll
+      for (int T = 0; T < C::NT; ++T) {
+        f4 c4 = f4{0.f, 0.f, 0.f, 0.f};
+        #pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          u4 av = BITS == 4 ? unpack4(cur.k[T][s]) : unpack2(cur.k[T][s >> 1], s & 1);
+          c4 = mfma(av, bq[s], c4);
+        }
+        acc[T] = c4;
+      }
+    }
+
+    // scores (log2 units)
+    float S[C::NT][4];
+    if (KAX == KVQ_CHANNEL_WISE) {
+      const float bias = ((const float*)(lds + M::KB))[gi * 4 + hh];
+      #pragma unroll
+      for (int T = 0; T < C::NT; ++T)
+        #pragma unroll
+        for (int j = 0; j < 4; ++j) S[T][j] = fmaf(acc[T][j], sc_k, bias);
+    } else {
+      const float4* kt = (const float4*)(lds + M::KB);
+      #pragma unroll
+      for (int T = 0; T < C::NT; ++T) {
+        const int r0 = rel + C::TPW * g + 4 * T;  // 4 consecutive tokens
+        float4 p0 = kt[r0 / 2], p1 = kt[r0 / 2 + 1];
+        S[T][0] = fmaf(acc[T][0], p0.x, p0.y * Qh);
+        S[T][1] = fmaf(acc[T][1], p0.z, p0.w * Qh);
+        S[T][2] = fmaf(acc[T][2], p1.x, p1.y * Qh);
+        S[T][3] = fmaf(acc[T][3], p1.z, p1.w * Qh);
+      }
+    }
+    if (t0 + C::TIT > te) {
+      #pragma unroll
+      for (int T = 0; T < C::NT; ++T)
+        #pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (t0 + C::TPW * g + 4 * T + j >= te) S[T][j] = -INFINITY;
+    }
+    float mx = S[0][0];
+    #pragma unroll
+    for (int T = 0; T < C::NT; ++T)
+      #pragma unroll
+      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, S[T][j]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (__any(mx > m_run + (float)kThr)) {
+      const float mn = fmaxf(m_run, mx);
+      const float sc = exp2_fast(m_run - mn);
+      #pragma unroll
+      for (int c = 0; c < 8; ++c) O[c] *= sc;
+      X *= sc;
+      lsum *= sc;
+      m_run = mn;
+    }
+    float P[C::NT][4];
+    #pragma unroll
+    for (int T = 0; T < C::NT; ++T)
+      #pragma unroll
+      for (int j = 0; j < 4; ++j) P[T][j] = exp2_fast(S[T][j] - m_run);
+
+    // B operands for PV
+    u4 bp[C::NK];
+    if (VAX == KVQ_TOKEN_WISE) {
+      const float4* cf = (const float4*)(lds + M::VA);
+      float Pc[C::NT][4];
+      #pragma unroll
+      for (int T = 0; T < C::NT; ++T) {
+        float4 c4 = cf[(rel + C::TPW * g + 4 * T) / 4];
+        Pc[T][0] = P[T][0] * c4.x; Pc[T][1] = P[T][1] * c4.y;
+        Pc[T][2] = P[T][2] * c4.z; Pc[T][3] = P[T][3] * c4.w;
+        lsum += (P[T][0] + P[T][1]) + (P[T][2] + P[T][3]);
+      }
+      #pragma unroll
+      for (int k = 0; k < C::NK; ++k)
+        #pragma unroll
+        for (int m = 0; m < 4; ++m) bp[k][m] = pack_f16x2(Pc[k][m], Pc[C::NT / 2 + k][m]);
+    } else {
+      #pragma unroll
+      for (int k = 0; k < C::NK; ++k)
+        #pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float cm = two_mF * C::inv_w(m);
+          bp[k][m] = pack_f16x2(P[k][m] * cm, P[C::NT / 2 + k][m] * cm);
+        }
+    }
+
+    // PV: 8 channel tiles + the extra tile
+    if (VAX == KVQ_TOKEN_WISE) {
+      const _Float16* rbase = (const _Float16*)(lds + M::VR);
+      #pragma unroll
+      for (int k = 0; k < C::NK; ++k) {
+        #pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint32_t w = cur.v[c >> 2][c & 3];
+          u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
+          O[c] = mfma(av, bp[k], O[c]);
+        }
+        const int pos = (((rel / C::TIT) * C::NK + k) * 4 + g) * 8;
+        const _Float16* src = ri == 0 ? rbase + pos
+                             : ri == 1 ? rbase + kMaxSplitTokens + pos
+                                       : rbase + 2 * kMaxSplitTokens;
+        X = mfma(*(const u4*)src, bp[k], X);
+      }
+    } else {
+      f4 G8[8];
+      f4 Xg = f4{0.f, 0.f, 0.f, 0.f};
+      #pragma unroll
+      for (int c = 0; c < 8; ++c) G8[c] = f4{0.f, 0.f, 0.f, 0.f};
+      #pragma unroll
+      for (int k = 0; k < C::NK; ++k) {
+        #pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint32_t w = cur.v[c >> 2][c & 3];
+          u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
+          G8[c] = mfma(av, bp[k], G8[c]);
+        }
+        u4 ones = u4{0u, 0u, 0u, 0u};
+        if (ri == 0) {
+          #pragma unroll
+          for (int m = 0; m < 4; ++m) ones[m] = 0x00010001u << (BITS * (m % C::SLOTS));
+        }
+        Xg = mfma(ones, bp[k], Xg);
+      }
+      // fold this group's partial: O_d += sigma_d (G_d + rho_d * sum P)
+      const float psum = __shfl(Xg[0], n);  // row 0 lives in lane group 0
+      const float4* vg = (const float4*)(lds + M::VA) + (gi * kHeadDim + 32 * g) / 2;
+      #pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        #pragma unroll
+        for (int c = 0; c < 8; c += 2) {
+          // channels 32g + 8j + c and +1: (sigma, rho, sigma, rho)
+          float4 sr = vg[(8 * j + c) / 2];
+          O[c][j] = fmaf(sr.x, fmaf(sr.y, psum, G8[c][j]), O[c][j]);
+          O[c + 1][j] = fmaf(sr.z, fmaf(sr.w, psum, G8[c + 1][j]), O[c + 1][j]);
+        }
+      }
+      lsum += psum;
+    }
+    cur = nxt;
+  }
+
+  // ---- per-wave result: numerator N and normaliser l (same scale) --------
+  float lw;
+  if (VAX == KVQ_TOKEN_WISE) {
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    const float off = __shfl(X[0] + X[1], n);
+    const float s24 = ldexpf(1.f, F + 24), sF = ldexpf(1.f, F);
+    #pragma unroll
+    for (int c = 0; c < 8; ++c)
+      #pragma unroll
+      for (int j = 0; j < 4; ++j) O[c][j] = fmaf(O[c][j], s24, off * sF);
+    lw = lsum;
+  } else {
+    const float s24 = ldexpf(1.f, F + 24);
+    #pragma unroll
+    for (int c = 0; c < 8; ++c) O[c] *= s24;
+    lw = lsum * s24;
+  }
+
+  // ---- merge the four waves --------------------------------------------
+  __syncthreads();  // main-loop LDS no longer needed
+  float* mo = (float*)(lds + M::MO);
+  float* ml = (float*)(lds + M::ML);
+  if (n < 4 && g == 0) {
+    ml[(wv * 4 + n) * 2] = m_run;
+  }
+  __syncthreads();
+  float mall = -INFINITY;
+  #pragma unroll
+  for (int w = 0; w < kWaves; ++w) mall = fmaxf(mall, ml[(w * 4 + hh) * 2]);
+  const float f = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - mall);
+  __syncthreads();
+  if (n < 4) {
+    float* dst = mo + (wv * 4 + n) * kHeadDim + 32 * g;
+    #pragma unroll
+    for (int j = 0; j < 4; ++j)
+      #pragma unroll
+      for (int c = 0; c < 8; ++c) dst[8 * j + c] = O[c][j] * f;
+    if (g == 0) ml[(wv * 4 + n) * 2 + 1] = lw * f;
+  }
+  if (n < 4 && g == 0) ml[(wv * 4 + n) * 2] = mall;
+  __syncthreads();
+  {
+    const int qh = tid >> 6, d = (tid & 63) * 2;
+    float n0 = 0.f, n1 = 0.f, lt = 0.f;
+    #pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      n0 += mo[(w * 4 + qh) * kHeadDim + d];
+      n1 += mo[(w * 4 + qh) * kHeadDim + d + 1];
+      lt += ml[(w * 4 + qh) * 2 + 1];
+    }
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float o0 = n0 * inv, o1 = n1 * inv;
+    const long row = row0 + qh;
+    if (a.num_splits == 1) {
+      if (a.out_bf16) {
+        __bf16 b0 = (__bf16)o0, b1 = (__bf16)o1;
+        uint32_t pk = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        *(uint32_t*)((uint16_t*)a.out + row * kHeadDim + d) = pk;
+      } else {
+        *(float2*)((float*)a.out + row * kHeadDim + d) = make_float2(o0, o1);
+      }
+    } else {
+      const long pr = row * a.num_splits + sp;
+      *(float2*)(a.part_o + pr * kHeadDim + d) = make_float2(o0, o1);
+      if (d == 0) {
+        // m in log2 units, l in units of 2^(S - m)
+        a.part_ml[pr * 2] = ml[(0 * 4 + qh) * 2];
+        a.part_ml[pr * 2 + 1] = lt;
+      }
+    }
+  }
+}
+
+// LSE combine of the split partials: O = sum_i 2^(m_i - M) l_i O_i / sum_i 2^(m_i - M) l_i.
+__global__ void __launch_bounds__(128) combine_kernel(const float* part_o, const float* part_ml,
+                                                      int num_splits, void* out, int out_bf16) {
+  const long row = blockIdx.x;
+  const int d = threadIdx.x;
+  const float* ml = part_ml + row * num_splits * 2;
+  float M = -INFINITY;
+  for (int i = 0; i < num_splits; ++i) M = fmaxf(M, ml[2 * i]);
+  float num = 0.f, den = 0.f;
+  if (M != -INFINITY) {
+    for (int i = 0; i < num_splits; ++i) {
+      const float m = ml[2 * i];
+      if (m == -INFINITY) continue;
+      const float w = exp2f(m - M) * ml[2 * i + 1];
+      num = fmaf(w, part_o[(row * num_splits + i) * kHeadDim + d], num);
+      den += w;
+    }
+  }
+  const float o = den > 0.f ? num / den : 0.f;
+  if (out_bf16) ((__bf16*)out)[row * kHeadDim + d] = (__bf16)o;
+  else ((float*)out)[row * kHeadDim + d] = o;
+}
+
+template <int BITS, int KAX, int VAX, bool PAGED>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
+  dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
+  decode_kernel<BITS, KAX, VAX, PAGED><<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int BITS, int KAX, int VAX>
+hipError_t launch_p(const DecodeArgs& a, bool paged, hipStream_t s) {
+  return paged ? launch_t<BITS, KAX, VAX, true>(a, s) : launch_t<BITS, KAX, VAX, false>(a, s);
+}
+
+template <int BITS>
+hipError_t launch_b(const kvq_format& f, const DecodeArgs& a, hipStream_t s) {
+  const bool paged = f.page_size != 0;
+  if (f.k_axis == KVQ_CHANNEL_WISE) {
+    if (f.v_axis == KVQ_TOKEN_WISE) return launch_p<BITS, KVQ_CHANNEL_WISE, KVQ_TOKEN_WISE>(a, paged, s);
+    return launch_p<BITS, KVQ_CHANNEL_WISE, KVQ_CHANNEL_WISE>(a, paged, s);
+  }
+  if (f.v_axis == KVQ_TOKEN_WISE) return launch_p<BITS, KVQ_TOKEN_WISE, KVQ_TOKEN_WISE>(a, paged, s);
+  return launch_p<BITS, KVQ_TOKEN_WISE, KVQ_CHANNEL_WISE>(a, paged, s);
+}
+
+}  // namespace
+
+hipError_t launch_decode_quant(const kvq_format& f, const DecodeArgs& a, hipStream_t s) {
+  return f.bits == 4 ? launch_b<4>(f, a, s) : launch_b<2>(f, a, s);
+}
+
+hipError_t launch_combine(const float* part_o, const float* part_ml, int rows, int num_splits,
+                          void* out, int out_bf16, hipStream_t s) {
+  combine_kernel<<<rows, kHeadDim, 0, s>>>(part_o, part_ml, num_splits, out, out_bf16);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

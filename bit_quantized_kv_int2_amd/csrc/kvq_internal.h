@@ -1,0 +1,89 @@
+// Internal declarations shared by the library's HIP sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+constexpr int kHeadDim = 128;
+constexpr int kGroup = 128;
+constexpr int kGqa = 4;            // query heads per KV head
+constexpr int kPage = 64;          // tokens per page
+constexpr int kSplitQuantum = 256; // split lengths are multiples of this
+constexpr int kMaxSplitTokens = 2048;
+
+// Launch arguments of the quantised decode (one layer).
+struct DecodeArgs {
+  const uint16_t* q;       // bf16 [B][Hq][D]
+  const uint8_t* k_codes;
+  const uint32_t* v_words;
+  const uint16_t* k_sz;
+  const uint16_t* v_sz;
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  int max_pages;
+  int batch;
+  int num_kv_heads;
+  int max_len;             // sequence lengths are clamped to [0, max_len]
+  int padded_len;          // contiguous Lp
+  int split_tokens;        // multiple of kSplitQuantum, <= kMaxSplitTokens
+  int num_splits;
+  float scale_log2;        // softmax_scale * log2(e)
+  float* part_o;           // [B][Hq][num_splits][D]   (num_splits > 1)
+  float* part_ml;          // [B][Hq][num_splits][2]
+  void* out;               // final output when num_splits == 1
+  int out_bf16;
+};
+
+struct Bf16Args {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  int max_pages;
+  int batch;
+  int num_kv_heads;
+  int max_len;
+  int page_size;
+  int split_tokens;
+  int num_splits;
+  float scale_log2;
+  float* part_o;
+  float* part_ml;
+  void* out;
+  int out_bf16;
+};
+
+struct PackArgs {
+  const float* k;
+  const float* v;
+  const int32_t* seq_lens;
+  const int32_t* page_table;
+  int max_pages;
+  int batch;
+  int max_len;
+  int num_kv_heads;
+  int bits;
+  int k_axis;
+  int v_axis;
+  int paged;
+  int padded_len;
+  uint8_t* k_codes;
+  uint32_t* v_words;
+  uint16_t* k_sz;
+  uint16_t* v_sz;
+};
+
+// Kernel launchers (return the hipError_t of the launch).
+hipError_t launch_pack(const PackArgs& a, hipStream_t s);
+hipError_t launch_decode_quant(const kvq_format& f, const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const Bf16Args& a, hipStream_t s);
+hipError_t launch_combine(const float* part_o, const float* part_ml, int rows, int num_splits,
+                          void* out, int out_bf16, hipStream_t s);
+
+}  // namespace kvq

@@ -1,0 +1,224 @@
+// Quantise + pack one layer's K and V into the documented cache layout.
+//
+// Each group shares one scale s and offset z (x ~ s*c + z); groups run along
+// tokens or along channels, chosen separately for K and V (FOSCAR pages:
+// grafy.ai "What is FOSCAR and how does it work?", rag-lover.com
+// "conditions of use"). The rule is fixed bit for bit: min/max in fp32,
+// s = fp16((max - min) / (2^b - 1)) with an IEEE fp32 division, z =
+// fp16(min), code = clamp(rint((x - z) / s), 0, 2^b - 1) in fp32 from the
+// stored fp16 s and z, code 0 when s == 0.
+//
+// Two passes: one thread per group computes (s, z); then one thread per
+// packed 32-bit word recomputes its codes from the stored pairs. K words
+// hold 32/b consecutive channels of a token; V words hold 32/b consecutive
+// tokens of a channel.
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+struct Geo {
+  int H, Lp, max_pages, paged;
+  const int32_t* table;
+  // index of the 64-token chunk holding token t of (b, h)
+  __device__ long chunk(int b, int h, int t) const {
+    if (!paged) return ((long)b * H + h) * (Lp / kPage) + t / kPage;
+    return (long)table[(long)b * max_pages + t / kPage] * H + h;
+  }
+  // written extent of a sequence: whole padded length, or whole pages
+  __device__ int extent(int L) const { return paged ? ((L + kPage - 1) / kPage) * kPage : Lp; }
+};
+
+__device__ inline uint16_t f16_bits(float x) {
+  _Float16 h = (_Float16)x;  // v_cvt_f16_f32, round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ inline float f16_val(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
+
+__device__ inline long pair_token(const Geo& g, int b, int h, int t) {
+  return (g.chunk(b, h, t) * kPage + t % kPage) * 2;
+}
+__device__ inline long pair_channel(const Geo& g, int b, int h, int t, int d) {
+  if (!g.paged) return (((long)b * g.H + h) * (g.Lp / kGroup) + t / kGroup) * (long)kHeadDim * 2 + d * 2;
+  int t0 = (t / kGroup) * kGroup;
+  return (g.chunk(b, h, t0) * kHeadDim + d) * 2;
+}
+
+__device__ inline int encode(float x, float S, float Z, int qmax) {
+  if (S == 0.0f) return 0;
+  float diff = x - Z;
+  float t = __fdiv_rn(diff, S);
+  float r = rintf(t);
+  r = fminf(fmaxf(r, 0.0f), (float)qmax);
+  return (int)r;
+}
+
+// ---- pass 1: scale/offset per group -----------------------------------
+
+__global__ void __launch_bounds__(256) sz_token_kernel(PackArgs a, Geo g, int is_k) {
+  const float* x = is_k ? a.k : a.v;
+  uint16_t* sz = is_k ? a.k_sz : a.v_sz;
+  const int qmax = (1 << a.bits) - 1;
+  const long total = (long)a.batch * a.num_kv_heads * a.padded_len;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total;
+       i += (long)gridDim.x * blockDim.x) {
+    int t = (int)(i % a.padded_len);
+    long bh = i / a.padded_len;
+    int h = (int)(bh % a.num_kv_heads), b = (int)(bh / a.num_kv_heads);
+    int L = min(max(a.seq_lens[b], 0), a.max_len);
+    if (t >= g.extent(L)) continue;
+    uint16_t s16 = 0, z16 = 0;
+    if (t < L) {
+      const float4* row = (const float4*)(x + ((bh * a.max_len) + t) * (long)kHeadDim);
+      float4 v0 = row[0];
+      float mn = fminf(fminf(v0.x, v0.y), fminf(v0.z, v0.w));
+      float mx = fmaxf(fmaxf(v0.x, v0.y), fmaxf(v0.z, v0.w));
+      for (int j = 1; j < kHeadDim / 4; ++j) {
+        float4 v = row[j];
+        mn = fminf(mn, fminf(fminf(v.x, v.y), fminf(v.z, v.w)));
+        mx = fmaxf(mx, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+      }
+      s16 = f16_bits(__fdiv_rn(mx - mn, (float)qmax));
+      z16 = f16_bits(mn);
+    }
+    long p = pair_token(g, b, h, t);
+    sz[p] = s16;
+    sz[p + 1] = z16;
+  }
+}
+
+__global__ void __launch_bounds__(256) sz_channel_kernel(PackArgs a, Geo g, int is_k) {
+  const float* x = is_k ? a.k : a.v;
+  uint16_t* sz = is_k ? a.k_sz : a.v_sz;
+  const int qmax = (1 << a.bits) - 1;
+  const int ngroups = a.padded_len / kGroup;
+  const long total = (long)a.batch * a.num_kv_heads * ngroups * kHeadDim;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total;
+       i += (long)gridDim.x * blockDim.x) {
+    int d = (int)(i % kHeadDim);
+    long r = i / kHeadDim;
+    int gi = (int)(r % ngroups);
+    long bh = r / ngroups;
+    int h = (int)(bh % a.num_kv_heads), b = (int)(bh / a.num_kv_heads);
+    int L = min(max(a.seq_lens[b], 0), a.max_len);
+    int t0 = gi * kGroup;
+    if (t0 >= g.extent(L)) continue;
+    uint16_t s16 = 0, z16 = 0;
+    if (t0 < L) {
+      int n = min(kGroup, L - t0);
+      const float* col = x + (bh * a.max_len + t0) * (long)kHeadDim + d;
+      float mn = col[0], mx = col[0];
+      for (int t = 1; t < n; ++t) {
+        float v = col[(long)t * kHeadDim];
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+      }
+      s16 = f16_bits(__fdiv_rn(mx - mn, (float)qmax));
+      z16 = f16_bits(mn);
+    }
+    long p = pair_channel(g, b, h, t0, d);
+    sz[p] = s16;
+    sz[p + 1] = z16;
+  }
+}
+
+// ---- pass 2: codes -------------------------------------------------------
+
+// K: one thread per 32-bit word of a token row (32/b consecutive channels).
+__global__ void __launch_bounds__(256) k_codes_kernel(PackArgs a, Geo g) {
+  const int bits = a.bits, qmax = (1 << bits) - 1, per = 32 / bits;
+  const int words = kHeadDim / per;
+  const long total = (long)a.batch * a.num_kv_heads * a.padded_len * words;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total;
+       i += (long)gridDim.x * blockDim.x) {
+    int j = (int)(i % words);
+    long r = i / words;
+    int t = (int)(r % a.padded_len);
+    long bh = r / a.padded_len;
+    int h = (int)(bh % a.num_kv_heads), b = (int)(bh / a.num_kv_heads);
+    int L = min(max(a.seq_lens[b], 0), a.max_len);
+    if (t >= g.extent(L)) continue;
+    uint32_t w = 0;
+    if (t < L) {
+      const float* xr = a.k + (bh * a.max_len + t) * (long)kHeadDim + j * per;
+      float S = 0.f, Z = 0.f;
+      if (a.k_axis == KVQ_TOKEN_WISE) {
+        long p = pair_token(g, b, h, t);
+        S = f16_val(a.k_sz[p]);
+        Z = f16_val(a.k_sz[p + 1]);
+      }
+      for (int e = 0; e < per; ++e) {
+        int d = j * per + e;
+        if (a.k_axis == KVQ_CHANNEL_WISE) {
+          long p = pair_channel(g, b, h, t, d);
+          S = f16_val(a.k_sz[p]);
+          Z = f16_val(a.k_sz[p + 1]);
+        }
+        w |= (uint32_t)encode(xr[e], S, Z, qmax) << (bits * e);
+      }
+    }
+    long row = g.chunk(b, h, t) * kPage + t % kPage;
+    ((uint32_t*)a.k_codes)[row * words + j] = w;
+  }
+}
+
+// V: one thread per word = 32/b consecutive tokens of one channel.
+__global__ void __launch_bounds__(256) v_codes_kernel(PackArgs a, Geo g) {
+  const int bits = a.bits, qmax = (1 << bits) - 1, per = 32 / bits;
+  const int nw = a.padded_len / per;
+  const long total = (long)a.batch * a.num_kv_heads * nw * kHeadDim;
+  for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total;
+       i += (long)gridDim.x * blockDim.x) {
+    int d = (int)(i % kHeadDim);
+    long r = i / kHeadDim;
+    int wi = (int)(r % nw);
+    long bh = r / nw;
+    int h = (int)(bh % a.num_kv_heads), b = (int)(bh / a.num_kv_heads);
+    int L = min(max(a.seq_lens[b], 0), a.max_len);
+    int t0 = wi * per;
+    if (t0 >= g.extent(L)) continue;
+    uint32_t w = 0;
+    for (int e = 0; e < per; ++e) {
+      int t = t0 + e;
+      if (t >= L) break;
+      long p = (a.v_axis == KVQ_TOKEN_WISE) ? pair_token(g, b, h, t) : pair_channel(g, b, h, t, d);
+      float S = f16_val(a.v_sz[p]), Z = f16_val(a.v_sz[p + 1]);
+      float xv = a.v[(bh * a.max_len + t) * (long)kHeadDim + d];
+      w |= (uint32_t)encode(xv, S, Z, qmax) << (bits * e);
+    }
+    long word = (g.chunk(b, h, t0) * (kPage / per) + (t0 % kPage) / per) * kHeadDim + d;
+    a.v_words[word] = w;
+  }
+}
+
+int grid_for(long total) {
+  long blocks = (total + 255) / 256;
+  if (blocks > 256 * 64) blocks = 256 * 64;
+  if (blocks < 1) blocks = 1;
+  return (int)blocks;
+}
+
+}  // namespace
+
+hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
+  Geo g{a.num_kv_heads, a.padded_len, a.max_pages, a.paged, a.page_table};
+  const long tok = (long)a.batch * a.num_kv_heads * a.padded_len;
+  const long grp = (long)a.batch * a.num_kv_heads * (a.padded_len / kGroup) * kHeadDim;
+  for (int is_k = 1; is_k >= 0; --is_k) {
+    int axis = is_k ? a.k_axis : a.v_axis;
+    if (axis == KVQ_TOKEN_WISE)
+      sz_token_kernel<<<grid_for(tok), 256, 0, s>>>(a, g, is_k);
+    else
+      sz_channel_kernel<<<grid_for(grp), 256, 0, s>>>(a, g, is_k);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int per = 32 / a.bits;
+  k_codes_kernel<<<grid_for(tok * (kHeadDim / per)), 256, 0, s>>>(a, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  v_codes_kernel<<<grid_for(tok / per * kHeadDim), 256, 0, s>>>(a, g);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

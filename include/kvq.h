@@ -1,0 +1,171 @@
+/*
+ * kvq.h -- C ABI of the MI355X (gfx950) INT2/INT4 decode-attention library.
+ *
+ * Single-token decode attention, softmax(scale * q.K^T) . V with grouped
+ * query heads, read directly from KV caches quantised to 2 or 4 bits with a
+ * per-group scale s and offset z (x ~ s*c + z), groups token-wise or
+ * channel-wise independently for K and V. The scale and offset are folded
+ * into the other operand or the partial products instead of dequantising
+ * each element (FOSCAR, arXiv:2611.09722: abstract; grafy.ai "What is FOSCAR
+ * and how does it work?"; rag-lover.com explainer on acc-fold/operand-fold).
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers are plain device addresses (hipMalloc or a framework's
+ *     allocator), 16-byte aligned. The caller owns every buffer; the library
+ *     never allocates or frees device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls are asynchronous on that stream and never synchronise it.
+ *   - All argument checks are synchronous, run on the host before any HIP
+ *     call, and launch nothing on failure. A failed launch returns
+ *     KVQ_ERR_HIP (kvq_last_hip_error() gives the hipError_t of the calling
+ *     thread). A device fault shows up at the caller's next synchronisation.
+ *   - seq_lens lives in device memory; max_len (host) is an upper bound,
+ *     0 <= seq_lens[b] <= max_len. A length of 0 gives a zero output row.
+ *   - No state is kept between calls except the thread-local last HIP error.
+ *
+ * Cache layout (layout_version 1; little-endian; D = head_dim, b = bits,
+ * G = group = 128, tpw = 32/b tokens per V word, Lp = max_len rounded up to
+ * a multiple of 128; paged caches use 64-token pages):
+ *   K codes   contiguous [B][Hkv][Lp][D*b/8] bytes; paged [P][Hkv][64][D*b/8].
+ *             Channel d of a token sits at bit b*d of the token's row.
+ *   V codes   contiguous [B][Hkv][Lp/tpw][D] uint32; paged [P][Hkv][64/tpw][D].
+ *             Token j of a word sits at bit b*j (V is packed along tokens).
+ *   (s, z)    binary16 pairs, s first.
+ *             token-wise:   contiguous [B][Hkv][Lp][2];  paged [P][Hkv][64][2]
+ *             channel-wise: contiguous [B][Hkv][Lp/G][D][2]; paged [P][Hkv][D][2],
+ *                           a 128-token group's pairs in the page that holds
+ *                           its first token (the other page's slot is unused).
+ *   Quantisation of a group: s = fp16((max - min) / (2^b - 1)) with an fp32
+ *   division, z = fp16(min), c = clamp(rint((x - z) / s), 0, 2^b - 1) in fp32
+ *   with the stored s and z (c = 0 when s == 0). Codes of tokens at or past a
+ *   sequence's length, within the written extent, are 0.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_LAYOUT_VERSION 1u
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+  KVQ_ERR_BAD_FORMAT = 2,   /* unsupported bits/axes/group/head_dim/heads/page size/version */
+  KVQ_ERR_BAD_SHAPE = 3,    /* batch, max_len, pages or splits out of range */
+  KVQ_ERR_MISALIGNED = 4,   /* a device pointer is not 16-byte aligned */
+  KVQ_ERR_WORKSPACE = 5,    /* workspace missing or smaller than kvq_workspace_size() */
+  KVQ_ERR_HIP = 6           /* a HIP launch failed; see kvq_last_hip_error() */
+} kvq_status;
+
+typedef enum { KVQ_TOKEN_WISE = 0, KVQ_CHANNEL_WISE = 1 } kvq_axis;
+typedef enum { KVQ_OUT_F32 = 0, KVQ_OUT_BF16 = 1 } kvq_out_dtype;
+
+typedef struct {
+  int32_t bits;         /* 2 or 4 */
+  int32_t k_axis;       /* kvq_axis of K's groups */
+  int32_t v_axis;       /* kvq_axis of V's groups */
+  int32_t group;        /* 128 */
+  int32_t head_dim;     /* 128 */
+  int32_t num_kv_heads; /* >= 1 */
+  int32_t num_q_heads;  /* 4 * num_kv_heads (query head hq reads KV head hq / 4) */
+  int32_t page_size;    /* 0 = contiguous cache, 64 = paged cache */
+  uint32_t layout_version; /* must be KVQ_LAYOUT_VERSION */
+} kvq_format;
+
+/* Device pointers to one layer's packed cache (layout above). */
+typedef struct {
+  void* k_codes;
+  void* v_codes;
+  void* k_scale_offset;
+  void* v_scale_offset;
+} kvq_cache;
+
+/* Host-only helpers (no GPU needed). */
+const char* kvq_status_string(kvq_status s);
+int32_t kvq_last_hip_error(void);
+uint32_t kvq_layout_version(void);
+
+/* Checks a format; KVQ_OK if the library supports it. */
+kvq_status kvq_check_format(const kvq_format* fmt);
+
+/* Byte sizes of the four cache arrays (k_codes, v_codes, k_scale_offset,
+ * v_scale_offset). Contiguous caches use batch and max_len; paged caches use
+ * num_pages (pool slots of 64 tokens each). */
+kvq_status kvq_cache_sizes(const kvq_format* fmt, int32_t batch, int32_t max_len,
+                           int32_t num_pages, size_t bytes[4]);
+
+/* Split-KV plan: the number of token splits per (sequence, KV head) the
+ * decode uses for num_splits = 0 (auto), given batch and max_len. */
+kvq_status kvq_plan_splits(const kvq_format* fmt, int32_t batch, int32_t max_len,
+                           int32_t* num_splits);
+
+/* Workspace bytes decode_attention_quant / decode_attention_bf16 need for a
+ * given split count (0 = the auto plan). */
+kvq_status kvq_workspace_size(const kvq_format* fmt, int32_t batch, int32_t max_len,
+                              int32_t num_splits, size_t* bytes);
+
+/*
+ * kv_quantize_pack -- quantise and pack one layer's K and V into the cache.
+ * Producer side of the format the decode reads (grafy.ai "How can developers
+ * integrate": the cache must be quantised with the required group-wise
+ * scale/offset layout; the grouping choices follow rag-lover.com
+ * "conditions of use").
+ *   k, v        device fp32 [batch][Hkv][max_len][D], row-major.
+ *   seq_lens    device int32 [batch].
+ *   page_table  device int32 [batch][max_pages_per_seq] (physical page of each
+ *               64-token logical page) for paged formats, NULL for contiguous.
+ *   out         cache to write: every token row / word / pair of every page a
+ *               sequence references (contiguous: its whole padded extent),
+ *               zeros past the sequence length.
+ * Bit-exact with the documented quantisation rule.
+ */
+kvq_status kv_quantize_pack(const kvq_format* fmt, const float* k, const float* v,
+                            const int32_t* seq_lens, const int32_t* page_table,
+                            int32_t max_pages_per_seq, int32_t batch, int32_t max_len,
+                            const kvq_cache* out, void* stream);
+
+/*
+ * decode_attention_quant -- one query token per sequence against the packed
+ * cache, with the affine folds (token-wise K: scale the partial q.K^T and add
+ * z times the query sum; channel-wise K: fold s into q and add the offset
+ * after the product; token-wise V: fold s into P with a per-head offset;
+ * channel-wise V: scale each 128-token group's partial P.V, never across
+ * groups -- rag-lover.com explainer and limits section).
+ *   q           device bf16 [batch][Hq][D].
+ *   cache       packed cache in fmt's layout.
+ *   softmax_scale  multiplies q.K^T (e.g. 1/sqrt(D)).
+ *   out         device [batch][Hq][D], fp32 or bf16 per out_dtype.
+ *   num_splits  token splits per (sequence, KV head); 0 = automatic plan.
+ *   workspace   device scratch of at least kvq_workspace_size() bytes.
+ */
+kvq_status decode_attention_quant(const kvq_format* fmt, const void* q, const kvq_cache* cache,
+                                  const int32_t* seq_lens, const int32_t* page_table,
+                                  int32_t max_pages_per_seq, int32_t batch, int32_t max_len,
+                                  float softmax_scale, void* out, int32_t out_dtype,
+                                  int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
+ * decode_attention_bf16 -- the same decode over an unquantised bf16 cache
+ * (the comparison baseline; bits and axes of fmt are ignored).
+ *   k, v        device bf16: contiguous [batch][Hkv][max_len][D], paged
+ *               [P][Hkv][64][D].
+ *   other arguments as decode_attention_quant.
+ */
+kvq_status decode_attention_bf16(const kvq_format* fmt, const void* q, const void* k,
+                                 const void* v, const int32_t* seq_lens,
+                                 const int32_t* page_table, int32_t max_pages_per_seq,
+                                 int32_t batch, int32_t max_len, float softmax_scale, void* out,
+                                 int32_t out_dtype, int32_t num_splits, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,106 @@
+"""Shared helpers for the tests: run a synthetic workload through the GPU
+library and through the CPU oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import math
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+
+REL_L2_TOL = 4e-3
+MAX_ABS_TOL = 2e-2
+SCALE = 1.0 / math.sqrt(128.0)
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a - b))
+
+
+def max_abs(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)))) if np.size(a) else 0.0
+
+
+def gpu_format(w):
+    import bit_quantized_kv_int2_amd as kvq
+    return kvq.make_format(w.bits, w.k_axis, w.v_axis, w.num_kv_heads, page_size=w.page_size)
+
+
+class Inputs:
+    """Host copies of one workload's inputs (small workloads only)."""
+
+    def __init__(self, w, page_seed=9):
+        self.w = w
+        self.k = w.kv_all("k")
+        self.v = w.kv_all("v")
+        self.q = w.q_bf16()
+        self.lens = np.asarray(w.seq_lens, np.int32)
+        self.table, self.num_pages = (None, 0)
+        if w.page_size:
+            self.table, self.num_pages = synth.build_page_table(w.seq_lens, w.page_size, page_seed)
+
+
+def oracle_pack(inp: Inputs):
+    w = inp.w
+    return oracle.quantize_pack(oracle.fmt_of(w), inp.k, inp.v, inp.lens, page_table=inp.table,
+                                num_pages=inp.num_pages)
+
+
+def oracle_attention(inp: Inputs, cache, units=None):
+    w = inp.w
+    return oracle.decode_attention(oracle.fmt_of(w), inp.q, cache, inp.lens, w.max_len, SCALE,
+                                   page_table=inp.table, units=units)
+
+
+class GpuRun:
+    """Device tensors for one workload, packed by the library."""
+
+    def __init__(self, inp: Inputs, device="cuda"):
+        import torch
+        import bit_quantized_kv_int2_amd as kvq
+        self.kvq = kvq
+        w = inp.w
+        self.inp = inp
+        self.fmt = gpu_format(w)
+        self.k = torch.from_numpy(inp.k).to(device)
+        self.v = torch.from_numpy(inp.v).to(device)
+        self.q = torch.from_numpy(inp.q.view(np.int16)).to(device).view(torch.bfloat16)
+        self.lens = torch.from_numpy(inp.lens).to(device)
+        self.table = None if inp.table is None else torch.from_numpy(inp.table).to(device)
+        self.cache = kvq.cache_tensors(self.fmt, w.batch, w.max_len, inp.num_pages, device=device)
+        kvq.kv_quantize_pack(self.fmt, self.k, self.v, self.lens, self.cache, self.table,
+                             max_len=w.max_len)
+
+    def cache_host(self):
+        return [c.cpu().numpy() for c in self.cache]
+
+    def decode(self, num_splits=0, out_dtype=None):
+        import torch
+        w = self.inp.w
+        out = torch.empty((w.batch, w.num_q_heads, w.head_dim), device=self.q.device,
+                          dtype=out_dtype or torch.float32)
+        self.kvq.decode_attention_quant(self.fmt, self.q, self.cache, self.lens, w.max_len, SCALE,
+                                        out, page_table=self.table, num_splits=num_splits)
+        torch.cuda.synchronize()
+        return out.float().cpu().numpy().astype(np.float64)
+
+
+def cache_bytes_equal(gpu_cache, orc_cache):
+    """Compare the library's packed buffers with the oracle's arrays byte for byte."""
+    for i, (g, o) in enumerate(zip(gpu_cache, orc_cache)):
+        ob = np.ascontiguousarray(o).view(np.uint8).ravel()
+        gb = np.asarray(g).ravel()[:ob.size]
+        if not np.array_equal(gb, ob):
+            bad = np.nonzero(gb != ob)[0]
+            return False, f"array {i}: {bad.size} bytes differ, first at {bad[:8]}"
+    return True, ""

@@ -1,0 +1,143 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/kvq.h declares, and rejects bad arguments synchronously, before any
+HIP call (so these checks run on a host with no device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_kv_int2_amd as kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULLP, BADFMT, BADSHAPE, MISALIGNED, WORKSPACE = 0, 1, 2, 3, 4, 5
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(kvq.LIB_PATH):
+        from bit_quantized_kv_int2_amd import build
+        build.build()
+    return kvq.lib()
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_function(L):
+    names = _declared_functions()
+    assert {"kv_quantize_pack", "decode_attention_quant", "decode_attention_bf16"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_layout_version_and_status_strings(L):
+    assert L.kvq_layout_version() == kvq.LAYOUT_VERSION
+    for s in range(7):
+        assert L.kvq_status_string(s)
+
+
+def test_format_checks(L):
+    good = kvq.make_format(2, "channel", "token", 8)
+    assert kvq.kvq_check_format(good) == OK
+    for field, bad in [("bits", 3), ("bits", 8), ("group", 64), ("head_dim", 64),
+                       ("num_q_heads", 16), ("page_size", 32), ("layout_version", 2),
+                       ("k_axis", 2), ("num_kv_heads", 0)]:
+        f = kvq.make_format(2, "channel", "token", 8)
+        setattr(f, field, bad)
+        assert kvq.kvq_check_format(f) == BADFMT, field
+    assert L.kvq_check_format(None) == NULLP
+
+
+def test_cache_sizes(L):
+    f = kvq.make_format(4, "channel", "token", 8)
+    kc, vc, ks, vs = kvq.kvq_cache_sizes(f, 128, 32768)
+    assert kc == vc == 128 * 8 * 32768 * 64
+    assert ks == 128 * 8 * 256 * 128 * 4 and vs == 128 * 8 * 32768 * 4
+    f2 = kvq.make_format(2, "token", "channel", 8)
+    kc, vc, ks, vs = kvq.kvq_cache_sizes(f2, 3, 1000)   # padded to 1024 tokens
+    assert kc == 3 * 8 * 1024 * 32 and ks == 3 * 8 * 1024 * 4 and vs == 3 * 8 * 8 * 128 * 4
+    fp = kvq.make_format(4, "channel", "token", 8, page_size=64)
+    kc, vc, ks, vs = kvq.kvq_cache_sizes(fp, 0, 0, 100)
+    assert kc == 100 * 8 * 64 * 64 and ks == 100 * 8 * 128 * 4 and vs == 100 * 8 * 64 * 4
+
+
+def test_split_plan_and_workspace(L):
+    f = kvq.make_format(2, "channel", "token", 8)
+    ns = kvq.kvq_plan_splits(f, 128, 32768)
+    assert ns * 2048 >= 32768 and ns >= 16
+    assert kvq.kvq_workspace_size(f, 128, 32768) == 128 * 32 * ns * 130 * 4
+    assert kvq.kvq_plan_splits(kvq.make_format(4, num_kv_heads=1), 1, 1024) >= 1
+    # explicit splits: at least ceil(L / 2048), at most ceil(L / 256)
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_workspace_size(f, 2, 32768, 3)
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_workspace_size(f, 2, 1024, 5)
+    assert kvq.kvq_workspace_size(f, 2, 2048, 1) == 0
+
+
+def _call_decode(L, fmt, q=16, cache=(16, 16, 16, 16), lens=16, table=None, maxp=0, B=1,
+                 max_len=128, out=16, od=0, ns=0, ws=None, wsb=0):
+    c = kvq.Cache(*cache) if cache is not None else None
+    return L.decode_attention_quant(ctypes.byref(fmt) if fmt is not None else None, q,
+                                    ctypes.byref(c) if c is not None else None, lens, table, maxp,
+                                    B, max_len, ctypes.c_float(0.088), out, od, ns, ws, wsb, None)
+
+
+def test_decode_validation_without_gpu(L):
+    f = kvq.make_format(4, "channel", "token", 1)
+    A = 4096  # fake, 16-byte aligned addresses: never dereferenced on failure paths
+    assert _call_decode(L, None) == NULLP
+    assert _call_decode(L, f, q=None) == NULLP
+    assert _call_decode(L, f, cache=(A, A, None, A)) == NULLP
+    assert _call_decode(L, f, cache=(A, A + 4, A, A)) == MISALIGNED
+    assert _call_decode(L, f, q=A + 2, cache=(A, A, A, A), lens=A, out=A) == MISALIGNED
+    assert _call_decode(L, f, cache=(A, A, A, A), lens=None, out=A, q=A) == NULLP
+    assert _call_decode(L, f, cache=(A, A, A, A), lens=A, out=A, q=A, od=7) == BADFMT
+    assert _call_decode(L, f, cache=(A, A, A, A), lens=A, out=A, q=A, B=-1) == BADSHAPE
+    # needs a workspace: 2 splits requested, none given
+    assert _call_decode(L, f, cache=(A, A, A, A), lens=A, out=A, q=A, max_len=4096,
+                        ns=2) == WORKSPACE
+    assert _call_decode(L, f, cache=(A, A, A, A), lens=A, out=A, q=A, max_len=4096, ns=2,
+                        ws=A, wsb=10) == WORKSPACE
+    # paged formats need a page table that covers max_len
+    fp = kvq.make_format(4, "channel", "token", 1, page_size=64)
+    assert _call_decode(L, fp, cache=(A, A, A, A), lens=A, out=A, q=A) == NULLP
+    assert _call_decode(L, fp, cache=(A, A, A, A), lens=A, out=A, q=A, table=A, maxp=1,
+                        max_len=4096) == BADSHAPE
+    bad = kvq.make_format(3, "channel", "token", 1)
+    assert _call_decode(L, bad, cache=(A, A, A, A), lens=A, out=A, q=A) == BADFMT
+
+
+def test_pack_and_bf16_validation_without_gpu(L):
+    f = kvq.make_format(2, "token", "channel", 2)
+    A = 4096
+    c = kvq.Cache(A, A, A, A)
+    assert L.kv_quantize_pack(ctypes.byref(f), None, A, A, None, 0, 1, 128, ctypes.byref(c),
+                              None) == NULLP
+    assert L.kv_quantize_pack(ctypes.byref(f), A + 8, A, A, None, 0, 1, 128, ctypes.byref(c),
+                              None) == MISALIGNED
+    assert L.kv_quantize_pack(ctypes.byref(f), A, A, A, None, 0, 1, 128, None, None) == NULLP
+    assert L.kv_quantize_pack(ctypes.byref(f), A, A, A, None, 0, 1, -5, ctypes.byref(c),
+                              None) == BADSHAPE
+    # nothing to do: no launch, OK
+    assert L.kv_quantize_pack(ctypes.byref(f), A, A, A, None, 0, 0, 128, ctypes.byref(c),
+                              None) == OK
+    assert L.decode_attention_bf16(ctypes.byref(f), A, None, A, A, None, 0, 1, 128,
+                                   ctypes.c_float(0.1), A, 0, 0, None, 0, None) == NULLP
+    assert L.decode_attention_bf16(ctypes.byref(f), A, A, A, A, None, 0, 1, 128,
+                                   ctypes.c_float(float("nan")), A, 0, 0, None, 0, None) == BADSHAPE
+
+
+def test_calls_without_library_fail_loudly(monkeypatch, tmp_path):
+    """The binding has no fallback: with the library missing, calls raise."""
+    import importlib
+    monkeypatch.setattr(kvq, "_lib", None)
+    monkeypatch.setattr(kvq, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        kvq.lib()
