@@ -1,0 +1,276 @@
+"""Benchmark: single-token GQA decode attention over INT2/INT4 quantised KV
+caches on one MI355X, B=128 sequences x 32768 tokens, 8 KV heads x 32 query
+heads, head_dim 128, K channel-wise / V token-wise groups of 128, fp16 (s, z).
+
+One step = one decode_attention_quant call (split-KV decode kernel + LSE
+combine) over the whole INT2 headline cache, inputs resident in HBM. The
+same line also carries the INT4 headline and the library's own bf16 decode
+over the same (unquantised) values, and the CPU oracle timed on a bounded
+sample of units.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak, GB/s (AMD spec)
+METRIC = "effective KV-read GB/s (% of HBM peak) + µs/call, B=128 KV=32K INT2/INT4"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--batch", type=int, default=128)
+    p.add_argument("--seq-len", type=int, default=32768)
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle baseline sample")
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    p.add_argument("--no-bf16", action="store_true")
+    p.add_argument("--only", choices=["int2", "int4"], default=None,
+                   help="time one bit width only (profiling runs)")
+    return p.parse_args()
+
+
+def time_calls(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t_all0 = torch.cuda.Event(enable_timing=True)
+    t_all1 = torch.cuda.Event(enable_timing=True)
+    t_all0.record(stream)
+    for e0, e1 in evs:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    t_all1.record(stream)
+    torch.cuda.synchronize()
+    per = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3  # us
+    total_ms = t_all0.elapsed_time(t_all1)
+    return per, total_ms
+
+
+def make_inputs(B, L, widths, need_bf16, dev, log=log):
+    """Headline inputs: fp32 K/V drawn per batch row on the host, packed on the
+    GPU into one cache per bit width (and copied to bf16 for the baseline)."""
+    import torch
+    import synth
+    import bit_quantized_kv_int2_amd as kvq
+    H, Hq, D = 8, 32, 128
+    w = synth.headline(2)
+    w.batch, w.seq_lens = B, [L] * B
+    fmts = {bits: kvq.make_format(bits, "channel", "token", H) for bits in (2, 4)}
+    caches = {bits: kvq.cache_tensors(fmts[bits], B, L, device=dev) for bits in widths}
+    row_bytes = {bits: kvq.kvq_cache_sizes(fmts[bits], 1, L) for bits in widths}
+    if need_bf16:
+        kb = torch.empty((B, H, L, D), dtype=torch.bfloat16, device=dev)
+        vb = torch.empty((B, H, L, D), dtype=torch.bfloat16, device=dev)
+
+    # ---- inputs: generated per batch row on the host, packed on the GPU ----
+    t0 = time.time()
+    offs = w.outlier_offsets()
+    kh = np.empty((H, L, D), np.float32)
+    vh = np.empty((H, L, D), np.float32)
+    kst = torch.empty((1, H, L, D), dtype=torch.float32, device=dev)
+    vst = torch.empty((1, H, L, D), dtype=torch.float32, device=dev)
+    len1 = torch.tensor([L], dtype=torch.int32, device=dev)
+    for b in range(B):
+        w.kv_row("k", b, offsets=offs, out=kh)
+        w.kv_row("v", b, out=vh)
+        kst.copy_(torch.from_numpy(kh)[None])
+        vst.copy_(torch.from_numpy(vh)[None])
+        for bits in widths:
+            rc = [c[b * n:(b + 1) * n] for c, n in zip(caches[bits], row_bytes[bits])]
+            kvq.kv_quantize_pack(fmts[bits], kst, vst, len1, rc, max_len=L)
+        if need_bf16:
+            kb[b].copy_(kst[0])
+            vb[b].copy_(vst[0])
+        if b % 16 == 15:
+            torch.cuda.synchronize()
+            log(f"inputs: {b + 1}/{B} rows generated and packed ({time.time() - t0:.0f} s)")
+    torch.cuda.synchronize()
+    del kst, vst
+    q = torch.from_numpy(w.q_bf16().view(np.int16)).to(dev).view(torch.bfloat16)
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+
+    kb_vb = (kb, vb) if need_bf16 else None
+    return dict(w=w, fmts=fmts, caches=caches, row_bytes=row_bytes, q=q, lens=lens, out=out,
+                bf16=kb_vb)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import bit_quantized_kv_int2_amd as kvq
+
+    kvq.lib()  # fails loudly when the library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    B, L = args.batch, args.seq_len
+    H, Hq, D = 8, 32, 128
+    scale = 1.0 / math.sqrt(D)
+    widths = [int(args.only[-1])] if args.only else [2, 4]
+    need_bf16 = not args.no_bf16 and args.only is None
+    inp = make_inputs(B, L, widths, need_bf16, dev)
+    w, fmts, caches, row_bytes = inp["w"], inp["fmts"], inp["caches"], inp["row_bytes"]
+    q, lens, out = inp["q"], inp["lens"], inp["out"]
+    if need_bf16:
+        kb, vb = inp["bf16"]
+    results = {}
+    for bits in widths:
+        fmt = fmts[bits]
+        ns = kvq.kvq_plan_splits(fmt, B, L)
+        ws = torch.empty(max(kvq.kvq_workspace_size(fmt, B, L), 16), dtype=torch.uint8, device=dev)
+        eff = sum(kvq.kvq_cache_sizes(fmt, B, L))
+        codes = sum(kvq.kvq_cache_sizes(fmt, B, L)[:2])
+        cache = caches[bits]
+
+        def call():
+            kvq.decode_attention_quant(fmt, q, cache, lens, L, scale, out, workspace=ws)
+
+        per, total_ms = time_calls(call, args.steps, args.warmup, stream)
+        us = total_ms * 1e3 / args.steps
+        gbs = eff / (us * 1e-6) / 1e9
+        results[bits] = dict(us_per_call=us, us_median=float(np.median(per)),
+                             us_p10=float(np.percentile(per, 10)),
+                             us_p90=float(np.percentile(per, 90)),
+                             effective_bytes=eff, codes_bytes=codes, gbs=gbs,
+                             pct_peak=100.0 * gbs / PEAK_HBM_GBS, num_splits=ns,
+                             workspace_bytes=int(ws.numel()))
+        log(f"INT{bits}: {us:.1f} us/call, {gbs:.0f} GB/s effective "
+            f"({100 * gbs / PEAK_HBM_GBS:.1f}% of {PEAK_HBM_GBS:.0f}), splits {ns}")
+        if bits == 2:
+            out2 = out.clone()
+        else:
+            out4 = out.clone()
+
+    bf16 = None
+    if need_bf16:
+        fmt = fmts[2]
+        ws = torch.empty(max(kvq.kvq_workspace_size(fmt, B, L), 16), dtype=torch.uint8, device=dev)
+        outb = torch.empty_like(out)
+
+        def callb():
+            kvq.decode_attention_bf16(fmt, q, kb, vb, lens, L, scale, outb, workspace=ws)
+
+        steps_b = max(5, args.steps // 4)
+        per, total_ms = time_calls(callb, steps_b, min(args.warmup, 3), stream)
+        us = total_ms * 1e3 / steps_b
+        eff = 2 * B * H * L * D * 2
+        gbs = eff / (us * 1e-6) / 1e9
+        bf16 = dict(us_per_call=us, us_median=float(np.median(per)), effective_bytes=eff, gbs=gbs,
+                    pct_peak=100.0 * gbs / PEAK_HBM_GBS, steps=steps_b)
+        log(f"bf16: {us:.1f} us/call, {gbs:.0f} GB/s")
+
+    # ---- CPU oracle on a bounded sample (rank 0, one GPU) --------------------
+    cpu = None
+    parity = {}
+    if not args.no_cpu:
+        import oracle
+        threads = min(16, os.cpu_count() or 1)
+        bits = widths[0]
+        fmt_o = oracle.make_format(bits, "channel", "token", 128, D, H, Hq)
+        per_row = row_bytes[bits]
+        qall = w.q_bf16()
+
+        def host_rows(b0, n):
+            hc = [c[b0 * m:(b0 + n) * m].cpu().numpy() for c, m in zip(caches[bits], per_row)]
+            shapes = oracle.cache_shapes(fmt_o, n, L)
+            return [x[:int(np.prod(sh)) * np.dtype(dt).itemsize].view(dt).reshape(sh)
+                    for x, (dt, sh) in zip(hc, shapes)]
+
+        # one unit, one thread, to size the sample
+        hc = host_rows(0, 1)
+        t1 = time.time()
+        oracle.decode_attention(fmt_o, qall[:1], hc, [L], L, scale, units=[(0, 0)], threads=1)
+        one = time.time() - t1
+        n_rows = int(min(B, max(1, math.ceil(args.cpu_seconds * threads / (one * H)))))
+        b0 = (B - n_rows) // 2
+        hc = host_rows(b0, n_rows)
+        t1 = time.time()
+        ref = oracle.decode_attention(fmt_o, qall[b0:b0 + n_rows], hc, [L] * n_rows, L, scale,
+                                      threads=threads)
+        dt_cpu = time.time() - t1
+        unit_bytes = results[bits]["effective_bytes"] / (B * H)
+        cpu_gbs = n_rows * H * unit_bytes / dt_cpu / 1e9
+        used = min(threads, n_rows * H)
+        cpu = {"value": cpu_gbs, "unit": "GB/s", "cores": used, "kind": "oracle",
+               "sample": f"INT{bits} headline rows {b0}..{b0 + n_rows - 1} ({n_rows * H} KV-head "
+                         f"units x {L} tokens, fp64 dequantise + attention), {dt_cpu:.1f} s on "
+                         f"{used} threads; value scaled to GB/s of effective cache bytes"}
+        got = (out2 if bits == 2 else out4)[b0:b0 + n_rows].double().cpu().numpy()
+        parity = {"rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref)),
+                  "max_abs": float(np.abs(got - ref).max()),
+                  "rows": [b0, b0 + n_rows], "bits": bits}
+        log(f"oracle: {cpu_gbs:.4f} GB/s on {used} threads ({dt_cpu:.1f} s); sampled parity {parity}")
+
+    main_bits = 2 if 2 in results else widths[0]
+    r = results[main_bits]
+    line = {
+        "metric": METRIC,
+        "value": round(r["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["us_per_call"] / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"INT{main_bits} decode attention, B={B} sequences x {L} tokens, "
+                               f"8 KV x 32 query heads, head_dim 128, K channel-wise / V token-wise "
+                               f"groups of 128, fp16 scale/offset; N(0,1) with 2% K outlier channels",
+                   "batch": B, "seq_len": L, "bits": main_bits, "num_kv_heads": H,
+                   "num_q_heads": Hq, "head_dim": D, "group": 128, "k_axis": "channel",
+                   "v_axis": "token", "num_splits": r["num_splits"]},
+        "us_per_call": round(r["us_per_call"], 2),
+        "pct_peak_hbm": round(r["pct_peak"], 2),
+        "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(r["gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel + combine_kernel (one decode_attention_quant call)",
+                     "algorithmic_bytes_per_launch": r["effective_bytes"]},
+        "cpu_baseline": cpu,
+        "parity_sample": parity or None,
+        "int2": results.get(2),
+        "int4": results.get(4),
+        "bf16": bf16,
+    }
+    if bf16 is not None:
+        for bits in results:
+            line[f"speedup_int{bits}_vs_bf16"] = round(bf16["us_per_call"] / results[bits]["us_per_call"], 3)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

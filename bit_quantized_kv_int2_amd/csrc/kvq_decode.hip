@@ -61,9 +61,11 @@ __device__ inline f4 mfma(u4 a, u4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a), as_h8(b), c, 0, 0, 0);
 }
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 __device__ inline uint32_t pack_f16x2(float lo, float hi) {
-  _Float16 a = (_Float16)lo, b = (_Float16)hi;  // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  // v_cvt_pk_f16_f32: both halves rounded to nearest even in one instruction
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), h2));
 }
 __device__ inline float f16lo(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFF)); }
 __device__ inline float f16hi(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16)); }
@@ -120,11 +122,11 @@ struct Lds {
   static constexpr int QB = QS + 4 * 128 * 4;                    // u4 [groups][4][4 s][4 g]
   static constexpr int QB_BYTES = (KAX == KVQ_CHANNEL_WISE ? kMaxGroups : 1) * 4 * 16 * 16;
   static constexpr int KB = QB + QB_BYTES;                       // chan-K bias [groups][4] / tok-K (s',z'') [tokens][2]
-  static constexpr int KB_BYTES = KAX == KVQ_CHANNEL_WISE ? kMaxGroups * 4 * 4 : kMaxSplitTokens * 8;
+  static constexpr int KB_BYTES = KAX == KVQ_CHANNEL_WISE ? kMaxGroups * 4 * 8 : kMaxSplitTokens * 8;
   static constexpr int VA = KB + KB_BYTES;                       // tok-V coef [tokens] / chan-V (sigma,rho) [groups][128]
   static constexpr int VA_BYTES = VAX == KVQ_TOKEN_WISE ? kMaxSplitTokens * 4 : kMaxGroups * 128 * 8;
   static constexpr int VR = VA + VA_BYTES;                       // tok-V rho hi/lo, A-operand order, fp16 [2][tokens] + 16 B zero
-  static constexpr int VR_BYTES = VAX == KVQ_TOKEN_WISE ? 2 * kMaxSplitTokens * 2 + 16 : 0;
+  static constexpr int VR_BYTES = VAX == KVQ_TOKEN_WISE ? 3 * kMaxSplitTokens * 2 : 0;
   static constexpr int RED = VR + VR_BYTES;                      // float [16] reductions + [4] Q sums
   static constexpr int TOTAL = RED + 32 * 4;
   // merge area reuses the front of LDS after the main loop
@@ -142,7 +144,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   float* red = (float*)(lds + M::RED);
 
   const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps addressing scalar
   const int H = a.num_kv_heads, Hq = H * kGqa;
   const int L = min(max(a.seq_lens[b], 0), a.max_len);  // contract: 0 <= len <= max_len
   const int tb = sp * a.split_tokens;
@@ -191,28 +194,34 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   const int ri = lane & 15;  // A-operand row
 
   // ---- code loads for one iteration -----------------------------------
+  // Per-lane byte/word offsets are the same every iteration; the chunk base
+  // is wave-uniform, so the address arithmetic stays on the scalar unit.
   struct Codes {
     uint32_t k[C::NT][BITS == 4 ? 4 : 2];
     u4 v[2];
   };
+  uint32_t koff[C::NT];
+#pragma unroll
+  for (int T = 0; T < C::NT; ++T)
+    koff[T] = (uint32_t)((C::TPW * (ri >> 2) + 4 * T + (ri & 3)) * C::KROW + (BITS == 4 ? 16 : 8) * g);
+  const uint32_t voff = (uint32_t)(g * kHeadDim + 8 * ri);
   auto load_codes = [&](int t0, Codes& cd) {
     const long ch = chunk_of(t0);
     const int tt0 = t0 % kPage;
-    #pragma unroll
+    const unsigned char* kb = a.k_codes + (ch * kPage + tt0) * C::KROW;
+#pragma unroll
     for (int T = 0; T < C::NT; ++T) {
-      const int tok = tt0 + C::TPW * (ri >> 2) + 4 * T + (ri & 3);
-      const unsigned char* p = a.k_codes + (ch * kPage + tok) * C::KROW;
       if (BITS == 4) {
-        u4 x = *(const u4*)(p + 16 * g);
+        u4 x = *(const u4*)(kb + koff[T]);
         cd.k[T][0] = x[0]; cd.k[T][1] = x[1]; cd.k[T][2] = x[2]; cd.k[T][3] = x[3];
       } else {
-        u2 x = *(const u2*)(p + 8 * g);
+        u2 x = *(const u2*)(kb + koff[T]);
         cd.k[T][0] = x[0]; cd.k[T][1] = x[1];
       }
     }
-    const uint32_t* vp = a.v_words + ((ch * (kPage / C::TPW) + tt0 / C::TPW + g) * kHeadDim + 8 * ri);
-    cd.v[0] = *(const u4*)vp;
-    cd.v[1] = *(const u4*)(vp + 4);
+    const uint32_t* vb = a.v_words + (ch * (kPage / C::TPW) + tt0 / C::TPW) * kHeadDim;
+    cd.v[0] = *(const u4*)(vb + voff);
+    cd.v[1] = *(const u4*)(vb + voff + 4);
   };
 
   // first iteration's codes go out before the prologue
@@ -222,7 +231,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     if (t0 < te) load_codes(t0, cur);
   }
 
-  // ---- prologue pass 1: q, maxima -----------------------------------------
+  // ---- prologue phase A: loads, per-wave maxima ----------------------------
+  // Thread t owns 8 consecutive tokens (token-wise (s, z)) or 8 consecutive
+  // (group, channel) pairs (channel-wise V): one 32-byte load each, kept in
+  // registers for phase B.
   {
     const int d = lane * 2;  // wave wv loads query head wv
     uint32_t qq = *(const uint32_t*)(a.q + (row0 + wv) * kHeadDim + d);
@@ -233,74 +245,99 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     float sum = wave_sum(q0 + q1);
     if (lane == 0) { red[wv] = m; red[20 + wv] = sum; }
   }
-  if (KAX == KVQ_CHANNEL_WISE) {
-    float m = 0.f;  // largest K scale of the split
-    for (int e = tid; e < ng * kHeadDim; e += kThreads) {
-      const uint16_t* p = ksz_chan(tb + (e / kHeadDim) * kGroup, e % kHeadDim);
-      m = fmaxf(m, f16val(p[0]));
-    }
-    m = wave_max(m);
-    if (lane == 0) red[4 + wv] = m;
-  }
+  const int r8 = 8 * tid;  // first token / pair of this thread
+  u4 vz0 = u4{0u, 0u, 0u, 0u}, vz1 = u4{0u, 0u, 0u, 0u};  // V (s, z) of 8 tokens or pairs
+  u4 kz0 = u4{0u, 0u, 0u, 0u}, kz1 = u4{0u, 0u, 0u, 0u};  // token-wise K (s, z) of 8 tokens
   if (VAX == KVQ_TOKEN_WISE) {
     float m = 0.f;
-    for (int r = tid; r < ntok; r += kThreads) {
-      float s = f16val(vsz_tok(tb + r)[0]);
-      m = fmaxf(m, s != 0.f ? s : 1.f);
+    if (r8 < ntok) {
+      const u4* p = (const u4*)vsz_tok(tb + r8);
+      vz0 = p[0];
+      vz1 = p[1];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t pr = (e < 4 ? vz0 : vz1)[e & 3];
+        const float sv = f16lo(pr);
+        if (r8 + e < ntok) m = fmaxf(m, sv != 0.f ? sv : 1.f);
+      }
     }
     m = wave_max(m);
     if (lane == 0) red[8 + wv] = m;
+  } else if (r8 < ng * kHeadDim) {
+    const u4* p = (const u4*)vsz_chan(tb + (r8 / kHeadDim) * kGroup, r8 % kHeadDim);
+    vz0 = p[0];
+    vz1 = p[1];
+  }
+  if (KAX == KVQ_TOKEN_WISE && r8 < ntok) {
+    const u4* p = (const u4*)ksz_tok(tb + r8);
+    kz0 = p[0];
+    kz1 = p[1];
   }
   __syncthreads();
   const float qmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  int E = 0;  // q'' = (alpha q s | q) * 2^-E, max |q''| < 2^14
-  if (KAX == KVQ_CHANNEL_WISE) {
-    const float smax = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
-    E = exp_above(alpha * qmax * smax) - 14;
-  } else {
-    E = exp_above(qmax) - 14;
-  }
   int F = kThr - 14;  // P'' = P * coef * 2^-F, max P'' < 2^14
   if (VAX == KVQ_TOKEN_WISE) {
     const float smax = fmaxf(fmaxf(red[8], red[9]), fmaxf(red[10], red[11]));
     F = exp_above(smax) + kThr - 14;
   }
-  const float two_mE = ldexpf(1.f, -E), two_E = ldexpf(1.f, E);
   const float two_mF = ldexpf(1.f, -F);
+  const int npad = ((ntok + C::TIT - 1) / C::TIT) * C::TIT;
 
-  // ---- prologue pass 2: fold operands into LDS ------------------------------
+  // ---- prologue phase B: fold operands into LDS ------------------------------
   u4* qB = (u4*)(lds + M::QB);
+  int E = 0;  // token-wise K: q'' = q * 2^-E, max |q''| < 2^14
   if (KAX == KVQ_CHANNEL_WISE) {
-    // combo = (group, head, s, g); 16 consecutive threads share (group, head)
-    float* kbias = (float*)(lds + M::KB);
+    // combo = (group, head, s, g); the 16 lanes of a (group, head) share one
+    // exponent E so that max |q''| < 2^14, and sum the bias.
+    float2* kb = (float2*)(lds + M::KB);
     for (int c0 = 0; c0 < ng * 64; c0 += kThreads) {
       const int c = c0 + tid;
       const int p = c & 15, s = p >> 2, gg = p & 3;
       const int gh = c >> 4, gi = gh >> 2, qh = gh & 3;
-      float bias = 0.f;
-      uint32_t wds[4] = {0, 0, 0, 0};
-      if (gi < ng) {
-        #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          float part[2];
-          float qq[2];
-          float raw[2];
+      const bool live = gi < ng;
+      float aqs[8], rho[8], raw[8];
+      float amax = 0.f;
+      if (live) {
+        u4 pz[2];
+        float qv[8];
 #pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int d = C::k_channel(s, gg, m, hf);
-            const uint16_t* pz = ksz_chan(tb + gi * kGroup, d);
-            const float sv = f16val(pz[0]), zv = f16val(pz[1]);
-            const float aq = alpha * qs[qh * 128 + d];
-            // s == 0: every code is 0, the group is the constant z
-            qq[hf] = sv != 0.f ? aq * sv * two_mE * C::inv_w(m) : 0.f;
-            part[hf] = sv != 0.f ? zv / sv : 0.f;
-            raw[hf] = sv != 0.f ? 0.f : aq * zv;
-          }
-          uint32_t pk = pack_f16x2(qq[0], qq[1]);
+        for (int hf = 0; hf < 2; ++hf) {
+          const int cb = C::k_channel(s, gg, 0, hf);  // 4 consecutive channels
+          pz[hf] = *(const u4*)ksz_chan(tb + gi * kGroup, cb);
+          const uint2 qb2 = *(const uint2*)(a.q + (row0 + qh) * kHeadDim + cb);
+          qv[4 * hf + 0] = bf16val((uint16_t)(qb2.x & 0xFFFF));
+          qv[4 * hf + 1] = bf16val((uint16_t)(qb2.x >> 16));
+          qv[4 * hf + 2] = bf16val((uint16_t)(qb2.y & 0xFFFF));
+          qv[4 * hf + 3] = bf16val((uint16_t)(qb2.y >> 16));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {  // e = 4 hf + m
+          const uint32_t pr = pz[e >> 2][e & 3];
+          const float sv = f16lo(pr), zv = f16hi(pr);
+          const float aq = alpha * qv[e];
+          // s == 0: every code is 0 and the group is the constant z
+          aqs[e] = sv != 0.f ? aq * sv * C::inv_w(e & 3) : 0.f;
+          rho[e] = sv != 0.f ? zv * __builtin_amdgcn_rcpf(sv) : 0.f;
+          raw[e] = sv != 0.f ? 0.f : aq * zv;
+          amax = fmaxf(amax, fabsf(aqs[e]));
+        }
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 1));
+      amax = fmaxf(amax, __shfl_xor(amax, 2));
+      amax = fmaxf(amax, __shfl_xor(amax, 4));
+      amax = fmaxf(amax, __shfl_xor(amax, 8));
+      const int Eg = exp_above(amax) - 14;
+      const float tm = ldexpf(1.f, -Eg), tp = ldexpf(1.f, Eg);
+      float bias = 0.f;
+      if (live) {
+        uint32_t wds[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t pk = pack_f16x2(aqs[m] * tm, aqs[4 + m] * tm);
           wds[m] = pk;
           // consistent offset: the rounded operand (times its slot weight and
           // 2^E) times z/s, so rounding q*s moves only the weight of x^
-          bias += (f16lo(pk) * part[0] + f16hi(pk) * part[1]) * (C::w(m) * two_E) + raw[0] + raw[1];
+          bias += (f16lo(pk) * rho[m] + f16hi(pk) * rho[4 + m]) * (C::w(m) * tp) + raw[m] + raw[4 + m];
         }
         qB[((gi * 4 + qh) * 4 + s) * 4 + gg] = u4{wds[0], wds[1], wds[2], wds[3]};
       }
@@ -308,13 +345,15 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
       bias += __shfl_xor(bias, 2);
       bias += __shfl_xor(bias, 4);
       bias += __shfl_xor(bias, 8);
-      if (gi < ng && p == 0) kbias[gi * 4 + qh] = bias;
+      if (live && p == 0) kb[gi * 4 + qh] = make_float2(ldexpf(1.f, Eg + 24), bias);
     }
   } else {
+    E = exp_above(qmax) - 14;
+    const float two_mE = ldexpf(1.f, -E);
     if (tid < 64) {
       const int s = (tid & 15) >> 2, gg = tid & 3, qh = tid >> 4;
       uint32_t wds[4];
-      #pragma unroll
+#pragma unroll
       for (int m = 0; m < 4; ++m) {
         float v0 = qs[qh * 128 + C::k_channel(s, gg, m, 0)] * two_mE * C::inv_w(m);
         float v1 = qs[qh * 128 + C::k_channel(s, gg, m, 1)] * two_mE * C::inv_w(m);
@@ -322,66 +361,72 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
       }
       qB[(qh * 4 + s) * 4 + gg] = u4{wds[0], wds[1], wds[2], wds[3]};
     }
-    float2* ktok = (float2*)(lds + M::KB);
-    const int npad = ((ntok + C::TIT - 1) / C::TIT) * C::TIT;
+    float4* ktok = (float4*)(lds + M::KB);  // (s', z'') of two tokens per float4
     const float sc = alpha * ldexpf(1.f, E + 24);
-    for (int r = tid; r < npad; r += kThreads) {
-      float2 v = make_float2(0.f, 0.f);
-      if (r < ntok) {
-        const uint16_t* pz = ksz_tok(tb + r);
-        v = make_float2(f16val(pz[0]) * sc, f16val(pz[1]) * alpha);
+    if (r8 < npad) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t p0 = (e < 4 ? kz0 : kz1)[e & 3], p1 = (e < 4 ? kz0 : kz1)[(e + 1) & 3];
+        const bool v0 = r8 + e < ntok, v1 = r8 + e + 1 < ntok;
+        ktok[(r8 + e) / 2] = make_float4(v0 ? f16lo(p0) * sc : 0.f, v0 ? f16hi(p0) * alpha : 0.f,
+                                         v1 ? f16lo(p1) * sc : 0.f, v1 ? f16hi(p1) * alpha : 0.f);
       }
-      ktok[r] = v;
     }
   }
   if (VAX == KVQ_TOKEN_WISE) {
     float* coef = (float*)(lds + M::VA);
     _Float16* rh = (_Float16*)(lds + M::VR);
     _Float16* rl = rh + kMaxSplitTokens;
-    const int npad = ((ntok + C::TIT - 1) / C::TIT) * C::TIT;
-    for (int r = tid; r < npad; r += kThreads) {
-      float cf = 0.f, rw = 0.f;
-      const int j = r % C::TPW;
-      const float wt = (float)(1 << (BITS * (j % C::SLOTS)));
-      if (r < ntok) {
-        const uint16_t* pz = vsz_tok(tb + r);
-        float sv = f16val(pz[0]), zv = f16val(pz[1]);
-        float sig = sv != 0.f ? sv : 1.f;
-        float rho = sv != 0.f ? zv / sv : zv;
-        cf = sig * two_mF / wt;
-        rw = rho * wt;
+    if (r8 < npad) {
+      float cf[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = r8 + e;
+        const int j = r % C::TPW;
+        const float wt = (float)(1 << (BITS * (j % C::SLOTS)));
+        float c1 = 0.f, rw = 0.f;
+        if (r < ntok) {
+          const uint32_t pr = (e < 4 ? vz0 : vz1)[e & 3];
+          const float sv = f16lo(pr), zv = f16hi(pr);
+          c1 = (sv != 0.f ? sv : 1.f) * two_mF / wt;
+          rw = (sv != 0.f ? zv * __builtin_amdgcn_rcpf(sv) : zv) * wt;
+        }
+        cf[e] = c1;
+        // A-operand position of token r: (iteration, k-step, lane group, m, half)
+        const int it = r / C::TIT, rr = r % C::TIT;
+        const int gg = rr / C::TPW, hf = j / (C::TPW / 2), jj = j % (C::TPW / 2);
+        const int ks = jj / 4, m = jj % 4;
+        const int pos = ((it * C::NK + ks) * 4 + gg) * 8 + 2 * m + hf;
+        const _Float16 hi = (_Float16)rw;
+        rh[pos] = hi;
+        rl[pos] = (_Float16)(rw - (float)hi);
       }
-      coef[r] = cf;
-      // A-operand position of token r: (iteration, k-step, lane group, m, half)
-      const int it = r / C::TIT, rr = r % C::TIT;
-      const int gg = rr / C::TPW, hf = j / (C::TPW / 2), jj = j % (C::TPW / 2);
-      const int ks = jj / 4, m = jj % 4;
-      const int pos = ((it * C::NK + ks) * 4 + gg) * 8 + 2 * m + hf;
-      _Float16 hi = (_Float16)rw;
-      _Float16 lo = (_Float16)(rw - (float)hi);
-      rh[pos] = hi;
-      rl[pos] = lo;
+      ((float4*)coef)[r8 / 4] = make_float4(cf[0], cf[1], cf[2], cf[3]);
+      ((float4*)coef)[r8 / 4 + 1] = make_float4(cf[4], cf[5], cf[6], cf[7]);
     }
-    if (tid < 8) ((_Float16*)(lds + M::VR + 2 * kMaxSplitTokens * 2))[tid] = (_Float16)0.f;
-  } else {
-    float2* vg = (float2*)(lds + M::VA);
-    for (int e = tid; e < ng * kHeadDim; e += kThreads) {
-      const uint16_t* pz = vsz_chan(tb + (e / kHeadDim) * kGroup, e % kHeadDim);
-      float sv = f16val(pz[0]), zv = f16val(pz[1]);
-      vg[e] = make_float2(sv != 0.f ? sv : 1.f, sv != 0.f ? zv / sv : zv);
+    // third row: zeros, read by the A-operand rows 2..15 of the extra tile
+    u4* zr = (u4*)(lds + M::VR + 2 * kMaxSplitTokens * 2);
+    for (int e = tid; e < kMaxSplitTokens * 2 / 16; e += kThreads) zr[e] = u4{0u, 0u, 0u, 0u};
+  } else if (r8 < ng * kHeadDim) {
+    float4* vg = (float4*)(lds + M::VA);  // (sigma, rho) of two pairs per float4
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const uint32_t p0 = (e < 4 ? vz0 : vz1)[e & 3], p1 = (e < 4 ? vz0 : vz1)[(e + 1) & 3];
+      const float s0 = f16lo(p0), z0 = f16hi(p0), s1 = f16lo(p1), z1 = f16hi(p1);
+      vg[(r8 + e) / 2] = make_float4(s0 != 0.f ? s0 : 1.f, s0 != 0.f ? z0 * __builtin_amdgcn_rcpf(s0) : z0,
+                                     s1 != 0.f ? s1 : 1.f, s1 != 0.f ? z1 * __builtin_amdgcn_rcpf(s1) : z1);
     }
   }
   __syncthreads();
 
   // ---- main loop --------------------------------------------------------
   f4 O[8];
-  #pragma unroll
+#pragma unroll
   for (int c = 0; c < 8; ++c) O[c] = f4{0.f, 0.f, 0.f, 0.f};
   f4 X = f4{0.f, 0.f, 0.f, 0.f};  // extra tile accumulator
   float m_run = -INFINITY;
   float lsum = 0.f;
   const float Qh = red[20 + hh];
-  const float sc_k = ldexpf(1.f, E + 24);
 
   for (int it = wv;; it += kWaves) {
     const int t0 = tb + it * C::TIT;
@@ -398,31 +443,32 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     {
       const u4* qb = qB + ((KAX == KVQ_CHANNEL_WISE ? gi : 0) * 4 + hh) * 16;
       u4 bq[4];
-      #pragma unroll
+#pragma unroll
       for (int s = 0; s < 4; ++s) bq[s] = qb[s * 4 + g];
-      #pragma unroll
-      for (int T = 0; T < C::NT; ++T) {
-        f4 c4 = f4{0.f, 0.f, 0.f, 0.f};
-        #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int T = 0; T < C::NT; ++T) acc[T] = f4{0.f, 0.f, 0.f, 0.f};
+      // k-step outer, tiles inner: consecutive MFMAs are independent
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+#pragma unroll
+        for (int T = 0; T < C::NT; ++T) {
           u4 av = BITS == 4 ? unpack4(cur.k[T][s]) : unpack2(cur.k[T][s >> 1], s & 1);
-          c4 = mfma(av, bq[s], c4);
+          acc[T] = mfma(av, bq[s], acc[T]);
         }
-        acc[T] = c4;
       }
     }
 
     // scores (log2 units)
     float S[C::NT][4];
     if (KAX == KVQ_CHANNEL_WISE) {
-      const float bias = ((const float*)(lds + M::KB))[gi * 4 + hh];
-      #pragma unroll
+      const float2 sb = ((const float2*)(lds + M::KB))[gi * 4 + hh];  // (2^(E+24), bias)
+#pragma unroll
       for (int T = 0; T < C::NT; ++T)
-        #pragma unroll
-        for (int j = 0; j < 4; ++j) S[T][j] = fmaf(acc[T][j], sc_k, bias);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[T][j] = fmaf(acc[T][j], sb.x, sb.y);
     } else {
       const float4* kt = (const float4*)(lds + M::KB);
-      #pragma unroll
+#pragma unroll
       for (int T = 0; T < C::NT; ++T) {
         const int r0 = rel + C::TPW * g + 4 * T;  // 4 consecutive tokens
         float4 p0 = kt[r0 / 2], p1 = kt[r0 / 2 + 1];
@@ -433,32 +479,32 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
       }
     }
     if (t0 + C::TIT > te) {
-      #pragma unroll
+#pragma unroll
       for (int T = 0; T < C::NT; ++T)
-        #pragma unroll
+#pragma unroll
         for (int j = 0; j < 4; ++j)
           if (t0 + C::TPW * g + 4 * T + j >= te) S[T][j] = -INFINITY;
     }
     float mx = S[0][0];
-    #pragma unroll
+#pragma unroll
     for (int T = 0; T < C::NT; ++T)
-      #pragma unroll
+#pragma unroll
       for (int j = 0; j < 4; ++j) mx = fmaxf(mx, S[T][j]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     if (__any(mx > m_run + (float)kThr)) {
       const float mn = fmaxf(m_run, mx);
       const float sc = exp2_fast(m_run - mn);
-      #pragma unroll
+#pragma unroll
       for (int c = 0; c < 8; ++c) O[c] *= sc;
       X *= sc;
       lsum *= sc;
       m_run = mn;
     }
     float P[C::NT][4];
-    #pragma unroll
+#pragma unroll
     for (int T = 0; T < C::NT; ++T)
-      #pragma unroll
+#pragma unroll
       for (int j = 0; j < 4; ++j) P[T][j] = exp2_fast(S[T][j] - m_run);
 
     // B operands for PV
@@ -466,21 +512,21 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     if (VAX == KVQ_TOKEN_WISE) {
       const float4* cf = (const float4*)(lds + M::VA);
       float Pc[C::NT][4];
-      #pragma unroll
+#pragma unroll
       for (int T = 0; T < C::NT; ++T) {
         float4 c4 = cf[(rel + C::TPW * g + 4 * T) / 4];
         Pc[T][0] = P[T][0] * c4.x; Pc[T][1] = P[T][1] * c4.y;
         Pc[T][2] = P[T][2] * c4.z; Pc[T][3] = P[T][3] * c4.w;
         lsum += (P[T][0] + P[T][1]) + (P[T][2] + P[T][3]);
       }
-      #pragma unroll
+#pragma unroll
       for (int k = 0; k < C::NK; ++k)
-        #pragma unroll
+#pragma unroll
         for (int m = 0; m < 4; ++m) bp[k][m] = pack_f16x2(Pc[k][m], Pc[C::NT / 2 + k][m]);
     } else {
-      #pragma unroll
+#pragma unroll
       for (int k = 0; k < C::NK; ++k)
-        #pragma unroll
+#pragma unroll
         for (int m = 0; m < 4; ++m) {
           const float cm = two_mF * C::inv_w(m);
           bp[k][m] = pack_f16x2(P[k][m] * cm, P[C::NT / 2 + k][m] * cm);
@@ -490,28 +536,27 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     // PV: 8 channel tiles + the extra tile
     if (VAX == KVQ_TOKEN_WISE) {
       const _Float16* rbase = (const _Float16*)(lds + M::VR);
-      #pragma unroll
+      // row 0: hi part, row 1: lo part, rows 2..15: the zero row
+      const int rrow = (ri < 2 ? ri : 2) * kMaxSplitTokens + 8 * g;
+#pragma unroll
       for (int k = 0; k < C::NK; ++k) {
-        #pragma unroll
+#pragma unroll
         for (int c = 0; c < 8; ++c) {
           const uint32_t w = cur.v[c >> 2][c & 3];
           u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
           O[c] = mfma(av, bp[k], O[c]);
         }
-        const int pos = (((rel / C::TIT) * C::NK + k) * 4 + g) * 8;
-        const _Float16* src = ri == 0 ? rbase + pos
-                             : ri == 1 ? rbase + kMaxSplitTokens + pos
-                                       : rbase + 2 * kMaxSplitTokens;
-        X = mfma(*(const u4*)src, bp[k], X);
+        const int pos = ((rel / C::TIT) * C::NK + k) * 32;  // wave-uniform part
+        X = mfma(*(const u4*)(rbase + rrow + pos), bp[k], X);
       }
     } else {
       f4 G8[8];
       f4 Xg = f4{0.f, 0.f, 0.f, 0.f};
-      #pragma unroll
+#pragma unroll
       for (int c = 0; c < 8; ++c) G8[c] = f4{0.f, 0.f, 0.f, 0.f};
-      #pragma unroll
+#pragma unroll
       for (int k = 0; k < C::NK; ++k) {
-        #pragma unroll
+#pragma unroll
         for (int c = 0; c < 8; ++c) {
           const uint32_t w = cur.v[c >> 2][c & 3];
           u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
@@ -519,7 +564,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
         }
         u4 ones = u4{0u, 0u, 0u, 0u};
         if (ri == 0) {
-          #pragma unroll
+#pragma unroll
           for (int m = 0; m < 4; ++m) ones[m] = 0x00010001u << (BITS * (m % C::SLOTS));
         }
         Xg = mfma(ones, bp[k], Xg);
@@ -527,9 +572,9 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
       // fold this group's partial: O_d += sigma_d (G_d + rho_d * sum P)
       const float psum = __shfl(Xg[0], n);  // row 0 lives in lane group 0
       const float4* vg = (const float4*)(lds + M::VA) + (gi * kHeadDim + 32 * g) / 2;
-      #pragma unroll
+#pragma unroll
       for (int j = 0; j < 4; ++j) {
-        #pragma unroll
+#pragma unroll
         for (int c = 0; c < 8; c += 2) {
           // channels 32g + 8j + c and +1: (sigma, rho, sigma, rho)
           float4 sr = vg[(8 * j + c) / 2];
@@ -549,14 +594,14 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     lsum += __shfl_xor(lsum, 32);
     const float off = __shfl(X[0] + X[1], n);
     const float s24 = ldexpf(1.f, F + 24), sF = ldexpf(1.f, F);
-    #pragma unroll
+#pragma unroll
     for (int c = 0; c < 8; ++c)
-      #pragma unroll
+#pragma unroll
       for (int j = 0; j < 4; ++j) O[c][j] = fmaf(O[c][j], s24, off * sF);
     lw = lsum;
   } else {
     const float s24 = ldexpf(1.f, F + 24);
-    #pragma unroll
+#pragma unroll
     for (int c = 0; c < 8; ++c) O[c] *= s24;
     lw = lsum * s24;
   }
@@ -570,15 +615,15 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
   float mall = -INFINITY;
-  #pragma unroll
+#pragma unroll
   for (int w = 0; w < kWaves; ++w) mall = fmaxf(mall, ml[(w * 4 + hh) * 2]);
   const float f = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - mall);
   __syncthreads();
   if (n < 4) {
     float* dst = mo + (wv * 4 + n) * kHeadDim + 32 * g;
-    #pragma unroll
+#pragma unroll
     for (int j = 0; j < 4; ++j)
-      #pragma unroll
+#pragma unroll
       for (int c = 0; c < 8; ++c) dst[8 * j + c] = O[c][j] * f;
     if (g == 0) ml[(wv * 4 + n) * 2 + 1] = lw * f;
   }
@@ -587,7 +632,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   {
     const int qh = tid >> 6, d = (tid & 63) * 2;
     float n0 = 0.f, n1 = 0.f, lt = 0.f;
-    #pragma unroll
+#pragma unroll
     for (int w = 0; w < kWaves; ++w) {
       n0 += mo[(w * 4 + qh) * kHeadDim + d];
       n1 += mo[(w * 4 + qh) * kHeadDim + d + 1];
