@@ -99,19 +99,28 @@ __device__ inline u4 unpack2(uint32_t w, int sel) {
 
 template <int BITS>
 struct Cfg {
-  static constexpr int TPW = 32 / BITS;        // tokens per V word
-  static constexpr int NT = TPW / 4;           // QK tiles per iteration
-  static constexpr int TIT = 4 * TPW;          // tokens per wave iteration
-  static constexpr int NK = TPW / 8;           // PV k-steps per iteration
+  static constexpr int TPW = 32 / BITS;             // tokens per V word
+  static constexpr int TIT = 64;                    // tokens per wave iteration
+  static constexpr int NK = 2;                      // PV k-steps per iteration
   static constexpr int KROW = kHeadDim * BITS / 8;  // bytes per K token row
-  static constexpr int SLOTS = 8 / BITS;       // codes per byte
-  // bit offset inside its byte of element (m, *) of a k-step: weight 2^(BITS*(m % SLOTS))
+  static constexpr int KDW = KROW / 4;              // dwords per K token row
+  static constexpr int NVW = BITS == 4 ? 4 : 2;     // 16-byte V loads per lane
+  static constexpr int SLOTS = 8 / BITS;            // codes per byte
+  static constexpr int D2 = TPW / 2;                // token distance of a packed pair
+  // weight 2^(BITS*(m % SLOTS)) of VGPR m of an unpacked word (its codes' bit
+  // offset within their bytes); the other operand is divided by it
   __device__ static inline float inv_w(int m) { return 1.0f / (float)(1 << (BITS * (m % SLOTS))); }
   __device__ static inline float w(int m) { return (float)(1 << (BITS * (m % SLOTS))); }
-  // channel fed by element (m, hf) of k-step s in lane group g
-  __device__ static inline int k_channel(int s, int g, int m, int hf) {
-    if (BITS == 4) return 32 * g + 8 * s + m + 4 * hf;
-    return 32 * g + 16 * (s >> 1) + 4 * (s & 1) + m + 8 * hf;
+  // first of the 4 consecutive channels fed by half hf of QK k-step s
+  __device__ static inline int k_run(int s, int hf) {
+    return BITS == 4 ? 8 * s + 4 * hf : 16 * (s >> 1) + 4 * (s & 1) + 8 * hf;
+  }
+  // token (within an iteration) of QK row i = 4 gi + j in k-group q; chosen so
+  // that a lane's pairs (j = 2a, 2a + 1) are the two tokens of one packed V
+  // VGPR, which makes the P -> B-operand move one permute per VGPR
+  __device__ static inline int tok(int q, int gi, int j) {
+    const int base = BITS == 4 ? 8 * (gi >> 1) + 2 * (gi & 1) : 2 * gi;
+    return 16 * q + base + (j >> 1) + D2 * (j & 1);
   }
 };
 
@@ -119,15 +128,16 @@ struct Cfg {
 template <int KAX, int VAX>
 struct Lds {
   static constexpr int QS = 0;                                   // float [4][128]
-  static constexpr int QB = QS + 4 * 128 * 4;                    // u4 [groups][4][4 s][4 g]
+  static constexpr int QB = QS + 4 * 128 * 4;                    // u4 [groups][4 heads][16 k-steps]
   static constexpr int QB_BYTES = (KAX == KVQ_CHANNEL_WISE ? kMaxGroups : 1) * 4 * 16 * 16;
-  static constexpr int KB = QB + QB_BYTES;                       // chan-K bias [groups][4] / tok-K (s',z'') [tokens][2]
+  static constexpr int QZ = QB + QB_BYTES;                       // 256 B of zeros (off-diagonal B)
+  static constexpr int KB = QZ + 256;                            // chan-K (scale, bias) [groups][4] / tok-K (s',z'') [tokens]
   static constexpr int KB_BYTES = KAX == KVQ_CHANNEL_WISE ? kMaxGroups * 4 * 8 : kMaxSplitTokens * 8;
   static constexpr int VA = KB + KB_BYTES;                       // tok-V coef [tokens] / chan-V (sigma,rho) [groups][128]
   static constexpr int VA_BYTES = VAX == KVQ_TOKEN_WISE ? kMaxSplitTokens * 4 : kMaxGroups * 128 * 8;
-  static constexpr int VR = VA + VA_BYTES;                       // tok-V rho hi/lo, A-operand order, fp16 [2][tokens] + 16 B zero
+  static constexpr int VR = VA + VA_BYTES;                       // tok-V rho hi / lo / zero rows, fp16, A-operand order
   static constexpr int VR_BYTES = VAX == KVQ_TOKEN_WISE ? 3 * kMaxSplitTokens * 2 : 0;
-  static constexpr int RED = VR + VR_BYTES;                      // float [16] reductions + [4] Q sums
+  static constexpr int RED = VR + VR_BYTES;                      // float [32] reductions
   static constexpr int TOTAL = RED + 32 * 4;
   // merge area reuses the front of LDS after the main loop
   static constexpr int MO = 0;                                   // float [4 waves][4 heads][128]
@@ -189,39 +199,29 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   auto ksz_tok = [&](int t) -> const uint16_t* { return a.k_sz + (chunk_of(t) * kPage + t % kPage) * 2; };
   auto vsz_tok = [&](int t) -> const uint16_t* { return a.v_sz + (chunk_of(t) * kPage + t % kPage) * 2; };
 
-  // lane roles
-  const int n = lane & 15, g = lane >> 4, hh = n & 3;
-  const int ri = lane & 15;  // A-operand row
+  // lane roles: C/B layout column n = head (n & 3) + 4 q, lane group g;
+  // A layout row ri
+  const int n = lane & 15, g = lane >> 4, hh = n & 3, nq = n >> 2;
+  const int ri = lane & 15;
 
-  // ---- code loads for one iteration -----------------------------------
-  // Per-lane byte/word offsets are the same every iteration; the chunk base
-  // is wave-uniform, so the address arithmetic stays on the scalar unit.
+  // ---- code loads for one 64-token iteration ---------------------------
+  // K: lane (ri, g) loads the whole row of token tok(g, ri>>2, ri&3);
+  // V: lane (ri, g) loads words of channels 8 ri .. 8 ri + 7.
   struct Codes {
-    uint32_t k[C::NT][BITS == 4 ? 4 : 2];
-    u4 v[2];
+    u4 k[C::KDW / 4];
+    u4 v[C::NVW];
   };
-  uint32_t koff[C::NT];
-#pragma unroll
-  for (int T = 0; T < C::NT; ++T)
-    koff[T] = (uint32_t)((C::TPW * (ri >> 2) + 4 * T + (ri & 3)) * C::KROW + (BITS == 4 ? 16 : 8) * g);
-  const uint32_t voff = (uint32_t)(g * kHeadDim + 8 * ri);
+  const uint32_t koff = (uint32_t)(C::tok(g, ri >> 2, ri & 3) * C::KROW);
+  const uint32_t voff = (uint32_t)(g * kHeadDim + 8 * ri);  // words
   auto load_codes = [&](int t0, Codes& cd) {
     const long ch = chunk_of(t0);
-    const int tt0 = t0 % kPage;
-    const unsigned char* kb = a.k_codes + (ch * kPage + tt0) * C::KROW;
+    const unsigned char* kb = a.k_codes + (ch * kPage + t0 % kPage) * C::KROW + koff;
 #pragma unroll
-    for (int T = 0; T < C::NT; ++T) {
-      if (BITS == 4) {
-        u4 x = *(const u4*)(kb + koff[T]);
-        cd.k[T][0] = x[0]; cd.k[T][1] = x[1]; cd.k[T][2] = x[2]; cd.k[T][3] = x[3];
-      } else {
-        u2 x = *(const u2*)(kb + koff[T]);
-        cd.k[T][0] = x[0]; cd.k[T][1] = x[1];
-      }
-    }
-    const uint32_t* vb = a.v_words + (ch * (kPage / C::TPW) + tt0 / C::TPW) * kHeadDim;
-    cd.v[0] = *(const u4*)(vb + voff);
-    cd.v[1] = *(const u4*)(vb + voff + 4);
+    for (int e = 0; e < C::KDW / 4; ++e) cd.k[e] = *(const u4*)(kb + 16 * e);
+    const uint32_t* vb = a.v_words + (ch * (kPage / C::TPW) + (t0 % kPage) / C::TPW) * kHeadDim + voff;
+#pragma unroll
+    for (int e = 0; e < C::NVW; ++e)  // INT4: words g and 4 + g
+      cd.v[e] = *(const u4*)(vb + (e >> 1) * 4 * kHeadDim + 4 * (e & 1));
   };
 
   // first iteration's codes go out before the prologue
@@ -273,6 +273,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     kz0 = p[0];
     kz1 = p[1];
   }
+  if (tid < 16) ((u4*)(lds + M::QZ))[tid] = u4{0u, 0u, 0u, 0u};
   __syncthreads();
   const float qmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   int F = kThr - 14;  // P'' = P * coef * 2^-F, max P'' < 2^14
@@ -287,12 +288,12 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   u4* qB = (u4*)(lds + M::QB);
   int E = 0;  // token-wise K: q'' = q * 2^-E, max |q''| < 2^14
   if (KAX == KVQ_CHANNEL_WISE) {
-    // combo = (group, head, s, g); the 16 lanes of a (group, head) share one
-    // exponent E so that max |q''| < 2^14, and sum the bias.
+    // combo = (group, head, k-step s); the 16 lanes of a (group, head) share
+    // one exponent E so that max |q''| < 2^14, and sum the bias.
     float2* kb = (float2*)(lds + M::KB);
     for (int c0 = 0; c0 < ng * 64; c0 += kThreads) {
       const int c = c0 + tid;
-      const int p = c & 15, s = p >> 2, gg = p & 3;
+      const int s = c & 15;
       const int gh = c >> 4, gi = gh >> 2, qh = gh & 3;
       const bool live = gi < ng;
       float aqs[8], rho[8], raw[8];
@@ -302,7 +303,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
         float qv[8];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const int cb = C::k_channel(s, gg, 0, hf);  // 4 consecutive channels
+          const int cb = C::k_run(s, hf);  // 4 consecutive channels
           pz[hf] = *(const u4*)ksz_chan(tb + gi * kGroup, cb);
           const uint2 qb2 = *(const uint2*)(a.q + (row0 + qh) * kHeadDim + cb);
           qv[4 * hf + 0] = bf16val((uint16_t)(qb2.x & 0xFFFF));
@@ -339,27 +340,27 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
           // 2^E) times z/s, so rounding q*s moves only the weight of x^
           bias += (f16lo(pk) * rho[m] + f16hi(pk) * rho[4 + m]) * (C::w(m) * tp) + raw[m] + raw[4 + m];
         }
-        qB[((gi * 4 + qh) * 4 + s) * 4 + gg] = u4{wds[0], wds[1], wds[2], wds[3]};
+        qB[(gi * 4 + qh) * 16 + s] = u4{wds[0], wds[1], wds[2], wds[3]};
       }
       bias += __shfl_xor(bias, 1);
       bias += __shfl_xor(bias, 2);
       bias += __shfl_xor(bias, 4);
       bias += __shfl_xor(bias, 8);
-      if (live && p == 0) kb[gi * 4 + qh] = make_float2(ldexpf(1.f, Eg + 24), bias);
+      if (live && s == 0) kb[gi * 4 + qh] = make_float2(ldexpf(1.f, Eg + 24), bias);
     }
   } else {
     E = exp_above(qmax) - 14;
     const float two_mE = ldexpf(1.f, -E);
     if (tid < 64) {
-      const int s = (tid & 15) >> 2, gg = tid & 3, qh = tid >> 4;
+      const int s = tid & 15, qh = tid >> 4;
       uint32_t wds[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        float v0 = qs[qh * 128 + C::k_channel(s, gg, m, 0)] * two_mE * C::inv_w(m);
-        float v1 = qs[qh * 128 + C::k_channel(s, gg, m, 1)] * two_mE * C::inv_w(m);
+        float v0 = qs[qh * 128 + C::k_run(s, 0) + m] * two_mE * C::inv_w(m);
+        float v1 = qs[qh * 128 + C::k_run(s, 1) + m] * two_mE * C::inv_w(m);
         wds[m] = pack_f16x2(v0, v1);
       }
-      qB[(qh * 4 + s) * 4 + gg] = u4{wds[0], wds[1], wds[2], wds[3]};
+      qB[qh * 16 + s] = u4{wds[0], wds[1], wds[2], wds[3]};
     }
     float4* ktok = (float4*)(lds + M::KB);  // (s', z'') of two tokens per float4
     const float sc = alpha * ldexpf(1.f, E + 24);
@@ -382,7 +383,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = r8 + e;
-        const int j = r % C::TPW;
+        const int j = r % C::TPW;  // slot of token r in its V word
         const float wt = (float)(1 << (BITS * (j % C::SLOTS)));
         float c1 = 0.f, rw = 0.f;
         if (r < ntok) {
@@ -394,8 +395,18 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
         cf[e] = c1;
         // A-operand position of token r: (iteration, k-step, lane group, m, half)
         const int it = r / C::TIT, rr = r % C::TIT;
-        const int gg = rr / C::TPW, hf = j / (C::TPW / 2), jj = j % (C::TPW / 2);
-        const int ks = jj / 4, m = jj % 4;
+        int gg, ks, m, hf;
+        if (BITS == 2) {
+          gg = rr / 16;
+          hf = (rr % 16) / 8;
+          ks = (rr % 8) / 4;
+          m = rr % 4;
+        } else {
+          ks = rr / 32;
+          gg = (rr % 32) / 8;
+          hf = (rr % 8) / 4;
+          m = rr % 4;
+        }
         const int pos = ((it * C::NK + ks) * 4 + gg) * 8 + 2 * m + hf;
         const _Float16 hi = (_Float16)rw;
         rh[pos] = hi;
@@ -419,7 +430,30 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   }
   __syncthreads();
 
-  // ---- main loop --------------------------------------------------------
+  // ---- per-lane constants of the main loop ---------------------------------
+  // compact scores: lane (n, g) holds tokens tk0 + {0, D2, 1, D2 + 1} (j = 0..3)
+  const int tk0 = C::tok(nq, g, 0);
+  // B operand of QK^T is block diagonal: column (head, q) is nonzero only in
+  // k-group q, so only lanes with g == q read q''; the others read zeros
+  const bool qlive = g == nq;
+  // PV B operand VGPR m of k-step k comes from lane src[k][m >> 1], register pk[m & 1]
+  int src[2][2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int m2 = 0; m2 < 2; ++m2) {
+      const int sq = BITS == 2 ? g : 2 * k + (g >> 1);
+      const int sg = BITS == 2 ? 2 * k + m2 : 2 * (g & 1) + m2;
+      src[k][m2] = 4 * (hh + 4 * sq + 16 * sg);  // byte address for ds_bpermute
+    }
+  // channel-wise V: 2^-F / weight of the compact values' tokens (pairs a = 0, 1)
+  float cw[2];
+#pragma unroll
+  for (int aa = 0; aa < 2; ++aa) {
+    const int slot = (tk0 + aa) % C::TPW;
+    cw[aa] = two_mF / (float)(1 << (BITS * (slot % C::SLOTS)));
+  }
+
   f4 O[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) O[c] = f4{0.f, 0.f, 0.f, 0.f};
@@ -427,6 +461,9 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   float m_run = -INFINITY;
   float lsum = 0.f;
   const float Qh = red[20 + hh];
+  const _Float16* rbase = (const _Float16*)(lds + M::VR);
+  // extra-tile rows: 0 = hi part, 1 = lo part, 2..15 = the zero row
+  const int rrow = (ri < 2 ? ri : 2) * kMaxSplitTokens + 8 * g;
 
   for (int it = wv;; it += kWaves) {
     const int t0 = tb + it * C::TIT;
@@ -438,58 +475,41 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     const int rel = t0 - tb;
     const int gi = rel / kGroup;
 
-    // QK^T: NT tiles of 16 tokens, 4 k-steps of 32 channels
-    f4 acc[C::NT];
+    // QK^T over 16 k-steps of 8 channels per k-group: 64 tokens x 4 heads
+    float S[4];
     {
-      const u4* qb = qB + ((KAX == KVQ_CHANNEL_WISE ? gi : 0) * 4 + hh) * 16;
-      u4 bq[4];
+      const u4* qb = (const u4*)(lds + (qlive ? M::QB + ((KAX == KVQ_CHANNEL_WISE ? gi : 0) * 4 + hh) * 256
+                                              : M::QZ));
+      f4 c0 = f4{0.f, 0.f, 0.f, 0.f}, c1 = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) bq[s] = qb[s * 4 + g];
-#pragma unroll
-      for (int T = 0; T < C::NT; ++T) acc[T] = f4{0.f, 0.f, 0.f, 0.f};
-      // k-step outer, tiles inner: consecutive MFMAs are independent
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int T = 0; T < C::NT; ++T) {
-          u4 av = BITS == 4 ? unpack4(cur.k[T][s]) : unpack2(cur.k[T][s >> 1], s & 1);
-          acc[T] = mfma(av, bq[s], acc[T]);
-        }
+      for (int s = 0; s < 16; ++s) {
+        const uint32_t w = BITS == 4 ? cur.k[s >> 2][s & 3] : cur.k[s >> 3][(s >> 1) & 3];
+        const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, s & 1);
+        if (s & 1) c1 = mfma(av, qb[s], c1);
+        else c0 = mfma(av, qb[s], c0);
       }
-    }
-
-    // scores (log2 units)
-    float S[C::NT][4];
-    if (KAX == KVQ_CHANNEL_WISE) {
-      const float2 sb = ((const float2*)(lds + M::KB))[gi * 4 + hh];  // (2^(E+24), bias)
+      const f4 acc = c0 + c1;
+      if (KAX == KVQ_CHANNEL_WISE) {
+        const float2 sb = ((const float2*)(lds + M::KB))[gi * 4 + hh];  // (2^(E+24), bias)
 #pragma unroll
-      for (int T = 0; T < C::NT; ++T)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) S[T][j] = fmaf(acc[T][j], sb.x, sb.y);
-    } else {
-      const float4* kt = (const float4*)(lds + M::KB);
-#pragma unroll
-      for (int T = 0; T < C::NT; ++T) {
-        const int r0 = rel + C::TPW * g + 4 * T;  // 4 consecutive tokens
-        float4 p0 = kt[r0 / 2], p1 = kt[r0 / 2 + 1];
-        S[T][0] = fmaf(acc[T][0], p0.x, p0.y * Qh);
-        S[T][1] = fmaf(acc[T][1], p0.z, p0.w * Qh);
-        S[T][2] = fmaf(acc[T][2], p1.x, p1.y * Qh);
-        S[T][3] = fmaf(acc[T][3], p1.z, p1.w * Qh);
+        for (int j = 0; j < 4; ++j) S[j] = fmaf(acc[j], sb.x, sb.y);
+      } else {
+        const float4* kt = (const float4*)(lds + M::KB);  // (s', z'') per token, two per float4
+        const float4 p0 = kt[(rel + tk0) / 2], p1 = kt[(rel + tk0 + C::D2) / 2];
+        S[0] = fmaf(acc[0], p0.x, p0.y * Qh);  // token tk0
+        S[1] = fmaf(acc[1], p1.x, p1.y * Qh);  // tk0 + D2
+        S[2] = fmaf(acc[2], p0.z, p0.w * Qh);  // tk0 + 1
+        S[3] = fmaf(acc[3], p1.z, p1.w * Qh);  // tk0 + D2 + 1
       }
     }
     if (t0 + C::TIT > te) {
 #pragma unroll
-      for (int T = 0; T < C::NT; ++T)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (t0 + C::TPW * g + 4 * T + j >= te) S[T][j] = -INFINITY;
+      for (int j = 0; j < 4; ++j)
+        if (t0 + tk0 + (j >> 1) + C::D2 * (j & 1) >= te) S[j] = -INFINITY;
     }
-    float mx = S[0][0];
-#pragma unroll
-    for (int T = 0; T < C::NT; ++T)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mx = fmaxf(mx, S[T][j]);
+    float mx = fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 4));
+    mx = fmaxf(mx, __shfl_xor(mx, 8));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     if (__any(mx > m_run + (float)kThr)) {
@@ -501,49 +521,36 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
       lsum *= sc;
       m_run = mn;
     }
-    float P[C::NT][4];
+    float P[4];
 #pragma unroll
-    for (int T = 0; T < C::NT; ++T)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) P[T][j] = exp2_fast(S[T][j] - m_run);
+    for (int j = 0; j < 4; ++j) P[j] = exp2_fast(S[j] - m_run);
 
-    // B operands for PV
-    u4 bp[C::NK];
+    // P'' into packed pairs: pk[a] = (token tk0 + a, token tk0 + a + D2)
+    uint32_t pk[2];
     if (VAX == KVQ_TOKEN_WISE) {
-      const float4* cf = (const float4*)(lds + M::VA);
-      float Pc[C::NT][4];
-#pragma unroll
-      for (int T = 0; T < C::NT; ++T) {
-        float4 c4 = cf[(rel + C::TPW * g + 4 * T) / 4];
-        Pc[T][0] = P[T][0] * c4.x; Pc[T][1] = P[T][1] * c4.y;
-        Pc[T][2] = P[T][2] * c4.z; Pc[T][3] = P[T][3] * c4.w;
-        lsum += (P[T][0] + P[T][1]) + (P[T][2] + P[T][3]);
-      }
-#pragma unroll
-      for (int k = 0; k < C::NK; ++k)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) bp[k][m] = pack_f16x2(Pc[k][m], Pc[C::NT / 2 + k][m]);
+      const float2* cf = (const float2*)(lds + M::VA);
+      const float2 c0 = cf[(rel + tk0) / 2], c1 = cf[(rel + tk0 + C::D2) / 2];
+      pk[0] = pack_f16x2(P[0] * c0.x, P[1] * c1.x);
+      pk[1] = pack_f16x2(P[2] * c0.y, P[3] * c1.y);
+      lsum += (P[0] + P[1]) + (P[2] + P[3]);
     } else {
-#pragma unroll
-      for (int k = 0; k < C::NK; ++k)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float cm = two_mF * C::inv_w(m);
-          bp[k][m] = pack_f16x2(P[k][m] * cm, P[C::NT / 2 + k][m] * cm);
-        }
+      pk[0] = pack_f16x2(P[0] * cw[0], P[1] * cw[0]);
+      pk[1] = pack_f16x2(P[2] * cw[1], P[3] * cw[1]);
     }
-
-    // PV: 8 channel tiles + the extra tile
-    if (VAX == KVQ_TOKEN_WISE) {
-      const _Float16* rbase = (const _Float16*)(lds + M::VR);
-      // row 0: hi part, row 1: lo part, rows 2..15: the zero row
-      const int rrow = (ri < 2 ? ri : 2) * kMaxSplitTokens + 8 * g;
+    u4 bp[2];
 #pragma unroll
-      for (int k = 0; k < C::NK; ++k) {
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) bp[k][m] = (uint32_t)__builtin_amdgcn_ds_bpermute(src[k][m >> 1], (int)pk[m & 1]);
+
+    // PV: 8 channel tiles + the extra tile, 2 k-steps of 32 tokens
+    if (VAX == KVQ_TOKEN_WISE) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          const uint32_t w = cur.v[c >> 2][c & 3];
-          u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
+          const uint32_t w = BITS == 4 ? cur.v[2 * k + (c >> 2)][c & 3] : cur.v[c >> 2][c & 3];
+          const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
           O[c] = mfma(av, bp[k], O[c]);
         }
         const int pos = ((rel / C::TIT) * C::NK + k) * 32;  // wave-uniform part
@@ -555,11 +562,11 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) G8[c] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < C::NK; ++k) {
+      for (int k = 0; k < 2; ++k) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          const uint32_t w = cur.v[c >> 2][c & 3];
-          u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
+          const uint32_t w = BITS == 4 ? cur.v[2 * k + (c >> 2)][c & 3] : cur.v[c >> 2][c & 3];
+          const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
           G8[c] = mfma(av, bp[k], G8[c]);
         }
         u4 ones = u4{0u, 0u, 0u, 0u};
@@ -590,6 +597,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   // ---- per-wave result: numerator N and normaliser l (same scale) --------
   float lw;
   if (VAX == KVQ_TOKEN_WISE) {
+    lsum += __shfl_xor(lsum, 4);
+    lsum += __shfl_xor(lsum, 8);
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
     const float off = __shfl(X[0] + X[1], n);
