@@ -81,6 +81,53 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
+// Cross-lane reductions without LDS: DPP row rotations inside 16-lane rows,
+// v_permlane16/32_swap across rows.
+template <int R>
+__device__ inline float ror(float x) {  // lane l of a 16-lane row reads lane (l - R) mod 16
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + R, 0xF, 0xF, false));
+}
+__device__ inline float swap32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ inline float swap16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ inline float swap32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ inline float swap16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+// max / sum over the 16 lanes that share (lane & 3): lanes n, n+4, n+8, n+12 of all 4 rows
+__device__ inline float head_max(float x) {
+  x = fmaxf(x, ror<4>(x));
+  x = fmaxf(x, ror<8>(x));
+  return swap16_max(swap32_max(x));
+}
+__device__ inline float head_sum(float x) {
+  x += ror<4>(x);
+  x += ror<8>(x);
+  return swap16_sum(swap32_sum(x));
+}
+// max / sum over one 16-lane row
+__device__ inline float row_max(float x) {
+  x = fmaxf(x, ror<1>(x));
+  x = fmaxf(x, ror<2>(x));
+  x = fmaxf(x, ror<4>(x));
+  return fmaxf(x, ror<8>(x));
+}
+__device__ inline float row_sum(float x) {
+  x += ror<1>(x);
+  x += ror<2>(x);
+  x += ror<4>(x);
+  return x + ror<8>(x);
+}
+
 // exponent e with x < 2^e (x > 0), 0 for x == 0
 __device__ inline int exp_above(float x) { return x > 0.f ? ilogbf(x) + 1 : 0; }
 
@@ -232,9 +279,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   }
 
   // ---- prologue phase A: loads, per-wave maxima ----------------------------
-  // Thread t owns 8 consecutive tokens (token-wise (s, z)) or 8 consecutive
-  // (group, channel) pairs (channel-wise V): one 32-byte load each, kept in
-  // registers for phase B.
+  // Token-wise (s, z): thread t owns the 8 tokens of one A-operand block of
+  // the extra PV tile (iteration t/8, k-step (t/4)%2, lane group t%4), loaded
+  // as two 16-byte runs of 4 tokens. Channel-wise V: thread t owns pairs
+  // 8t..8t+7 (one 32-byte load). Values stay in registers for phase B.
   {
     const int d = lane * 2;  // wave wv loads query head wv
     uint32_t qq = *(const uint32_t*)(a.q + (row0 + wv) * kHeadDim + d);
@@ -245,33 +293,45 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     float sum = wave_sum(q0 + q1);
     if (lane == 0) { red[wv] = m; red[20 + wv] = sum; }
   }
-  const int r8 = 8 * tid;  // first token / pair of this thread
-  u4 vz0 = u4{0u, 0u, 0u, 0u}, vz1 = u4{0u, 0u, 0u, 0u};  // V (s, z) of 8 tokens or pairs
-  u4 kz0 = u4{0u, 0u, 0u, 0u}, kz1 = u4{0u, 0u, 0u, 0u};  // token-wise K (s, z) of 8 tokens
+  // tokens of this thread's block: run r (0, 1) covers tb_run[r] .. +3
+  int tb_run[2];
+  {
+    const int it = tid >> 3, ks = (tid >> 2) & 1, gg = tid & 3;
+    if (BITS == 2) {
+      tb_run[0] = it * C::TIT + 16 * gg + 4 * ks;
+      tb_run[1] = tb_run[0] + 8;
+    } else {
+      tb_run[0] = it * C::TIT + 32 * ks + 8 * gg;
+      tb_run[1] = tb_run[0] + 4;
+    }
+  }
+  const int r8 = 8 * tid;  // first pair (channel-wise V)
+  u4 vz[2] = {u4{0u, 0u, 0u, 0u}, u4{0u, 0u, 0u, 0u}};  // V (s, z): 2 runs of 4 tokens, or 8 pairs
+  u4 kz[2] = {u4{0u, 0u, 0u, 0u}, u4{0u, 0u, 0u, 0u}};  // token-wise K (s, z): 2 runs of 4 tokens
   if (VAX == KVQ_TOKEN_WISE) {
     float m = 0.f;
-    if (r8 < ntok) {
-      const u4* p = (const u4*)vsz_tok(tb + r8);
-      vz0 = p[0];
-      vz1 = p[1];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t pr = (e < 4 ? vz0 : vz1)[e & 3];
-        const float sv = f16lo(pr);
-        if (r8 + e < ntok) m = fmaxf(m, sv != 0.f ? sv : 1.f);
+    for (int rr = 0; rr < 2; ++rr) {
+      if (tb_run[rr] < ntok) {
+        vz[rr] = *(const u4*)vsz_tok(tb + tb_run[rr]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sv = f16lo(vz[rr][e]);
+          if (tb_run[rr] + e < ntok) m = fmaxf(m, sv != 0.f ? sv : 1.f);
+        }
       }
     }
     m = wave_max(m);
     if (lane == 0) red[8 + wv] = m;
   } else if (r8 < ng * kHeadDim) {
     const u4* p = (const u4*)vsz_chan(tb + (r8 / kHeadDim) * kGroup, r8 % kHeadDim);
-    vz0 = p[0];
-    vz1 = p[1];
+    vz[0] = p[0];
+    vz[1] = p[1];
   }
-  if (KAX == KVQ_TOKEN_WISE && r8 < ntok) {
-    const u4* p = (const u4*)ksz_tok(tb + r8);
-    kz0 = p[0];
-    kz1 = p[1];
+  if (KAX == KVQ_TOKEN_WISE) {
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+      if (tb_run[rr] < ntok) kz[rr] = *(const u4*)ksz_tok(tb + tb_run[rr]);
   }
   if (tid < 16) ((u4*)(lds + M::QZ))[tid] = u4{0u, 0u, 0u, 0u};
   __syncthreads();
@@ -282,51 +342,49 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     F = exp_above(smax) + kThr - 14;
   }
   const float two_mF = ldexpf(1.f, -F);
-  const int npad = ((ntok + C::TIT - 1) / C::TIT) * C::TIT;
 
   // ---- prologue phase B: fold operands into LDS ------------------------------
   u4* qB = (u4*)(lds + M::QB);
   int E = 0;  // token-wise K: q'' = q * 2^-E, max |q''| < 2^14
   if (KAX == KVQ_CHANNEL_WISE) {
-    // combo = (group, head, k-step s); the 16 lanes of a (group, head) share
-    // one exponent E so that max |q''| < 2^14, and sum the bias.
+    // thread = (group gi, k-step s): the 8 channels of k-step s for all 4
+    // heads. The 16 lanes of a group share, per head, one exponent E (so
+    // that max |q''| < 2^14) and the bias sum.
     float2* kb = (float2*)(lds + M::KB);
-    for (int c0 = 0; c0 < ng * 64; c0 += kThreads) {
-      const int c = c0 + tid;
-      const int s = c & 15;
-      const int gh = c >> 4, gi = gh >> 2, qh = gh & 3;
-      const bool live = gi < ng;
-      float aqs[8], rho[8], raw[8];
+    const int s = tid & 15, gi = tid >> 4;
+    const bool live = gi < ng;
+    float sig[8], rho[8], zr[8];
+    if (live) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const u4 pz = *(const u4*)ksz_chan(tb + gi * kGroup, C::k_run(s, hf));
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float sv = f16lo(pz[m]), zv = f16hi(pz[m]);
+          // s == 0: every code is 0 and the group is the constant z
+          sig[4 * hf + m] = alpha * sv * C::inv_w(m);
+          rho[4 * hf + m] = sv != 0.f ? zv * __builtin_amdgcn_rcpf(sv) : 0.f;
+          zr[4 * hf + m] = sv != 0.f ? 0.f : alpha * zv;
+        }
+      }
+    }
+#pragma unroll
+    for (int qh = 0; qh < 4; ++qh) {
+      float aqs[8], qv[8];
       float amax = 0.f;
       if (live) {
-        u4 pz[2];
-        float qv[8];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const int cb = C::k_run(s, hf);  // 4 consecutive channels
-          pz[hf] = *(const u4*)ksz_chan(tb + gi * kGroup, cb);
-          const uint2 qb2 = *(const uint2*)(a.q + (row0 + qh) * kHeadDim + cb);
-          qv[4 * hf + 0] = bf16val((uint16_t)(qb2.x & 0xFFFF));
-          qv[4 * hf + 1] = bf16val((uint16_t)(qb2.x >> 16));
-          qv[4 * hf + 2] = bf16val((uint16_t)(qb2.y & 0xFFFF));
-          qv[4 * hf + 3] = bf16val((uint16_t)(qb2.y >> 16));
+          const float4 q4 = *(const float4*)(qs + qh * 128 + C::k_run(s, hf));
+          qv[4 * hf + 0] = q4.x; qv[4 * hf + 1] = q4.y; qv[4 * hf + 2] = q4.z; qv[4 * hf + 3] = q4.w;
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {  // e = 4 hf + m
-          const uint32_t pr = pz[e >> 2][e & 3];
-          const float sv = f16lo(pr), zv = f16hi(pr);
-          const float aq = alpha * qv[e];
-          // s == 0: every code is 0 and the group is the constant z
-          aqs[e] = sv != 0.f ? aq * sv * C::inv_w(e & 3) : 0.f;
-          rho[e] = sv != 0.f ? zv * __builtin_amdgcn_rcpf(sv) : 0.f;
-          raw[e] = sv != 0.f ? 0.f : aq * zv;
+        for (int e = 0; e < 8; ++e) {
+          aqs[e] = qv[e] * sig[e];
           amax = fmaxf(amax, fabsf(aqs[e]));
         }
       }
-      amax = fmaxf(amax, __shfl_xor(amax, 1));
-      amax = fmaxf(amax, __shfl_xor(amax, 2));
-      amax = fmaxf(amax, __shfl_xor(amax, 4));
-      amax = fmaxf(amax, __shfl_xor(amax, 8));
+      amax = row_max(amax);
       const int Eg = exp_above(amax) - 14;
       const float tm = ldexpf(1.f, -Eg), tp = ldexpf(1.f, Eg);
       float bias = 0.f;
@@ -338,14 +396,12 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
           wds[m] = pk;
           // consistent offset: the rounded operand (times its slot weight and
           // 2^E) times z/s, so rounding q*s moves only the weight of x^
-          bias += (f16lo(pk) * rho[m] + f16hi(pk) * rho[4 + m]) * (C::w(m) * tp) + raw[m] + raw[4 + m];
+          bias = fmaf(f16lo(pk) * rho[m] + f16hi(pk) * rho[4 + m], C::w(m) * tp, bias);
+          bias = fmaf(qv[m], zr[m], fmaf(qv[4 + m], zr[4 + m], bias));
         }
         qB[(gi * 4 + qh) * 16 + s] = u4{wds[0], wds[1], wds[2], wds[3]};
       }
-      bias += __shfl_xor(bias, 1);
-      bias += __shfl_xor(bias, 2);
-      bias += __shfl_xor(bias, 4);
-      bias += __shfl_xor(bias, 8);
+      bias = row_sum(bias);
       if (live && s == 0) kb[gi * 4 + qh] = make_float2(ldexpf(1.f, Eg + 24), bias);
     }
   } else {
@@ -364,65 +420,59 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     }
     float4* ktok = (float4*)(lds + M::KB);  // (s', z'') of two tokens per float4
     const float sc = alpha * ldexpf(1.f, E + 24);
-    if (r8 < npad) {
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const uint32_t p0 = (e < 4 ? kz0 : kz1)[e & 3], p1 = (e < 4 ? kz0 : kz1)[(e + 1) & 3];
-        const bool v0 = r8 + e < ntok, v1 = r8 + e + 1 < ntok;
-        ktok[(r8 + e) / 2] = make_float4(v0 ? f16lo(p0) * sc : 0.f, v0 ? f16hi(p0) * alpha : 0.f,
-                                         v1 ? f16lo(p1) * sc : 0.f, v1 ? f16hi(p1) * alpha : 0.f);
+    for (int rr = 0; rr < 2; ++rr) {
+      const int t4 = tb_run[rr];  // 4 tokens
+      if (t4 < kMaxSplitTokens) {
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const bool v0 = t4 + e < ntok, v1 = t4 + e + 1 < ntok;
+          const uint32_t p0 = kz[rr][e], p1 = kz[rr][e + 1];
+          ktok[(t4 + e) / 2] = make_float4(v0 ? f16lo(p0) * sc : 0.f, v0 ? f16hi(p0) * alpha : 0.f,
+                                           v1 ? f16lo(p1) * sc : 0.f, v1 ? f16hi(p1) * alpha : 0.f);
+        }
       }
     }
   }
   if (VAX == KVQ_TOKEN_WISE) {
-    float* coef = (float*)(lds + M::VA);
+    // coef[t] = sigma * 2^-F / w(t); extra-tile rows hold w(t) * rho as hi + lo fp16
+    float4* coef = (float4*)(lds + M::VA);
     _Float16* rh = (_Float16*)(lds + M::VR);
-    _Float16* rl = rh + kMaxSplitTokens;
-    if (r8 < npad) {
-      float cf[8];
+    float rw[2][4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = r8 + e;
-        const int j = r % C::TPW;  // slot of token r in its V word
-        const float wt = (float)(1 << (BITS * (j % C::SLOTS)));
-        float c1 = 0.f, rw = 0.f;
+    for (int rr = 0; rr < 2; ++rr) {
+      float cf[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = tb_run[rr] + e;
+        const float wt = (float)(1 << (BITS * ((r % C::TPW) % C::SLOTS)));
+        float c1 = 0.f, w1 = 0.f;
         if (r < ntok) {
-          const uint32_t pr = (e < 4 ? vz0 : vz1)[e & 3];
-          const float sv = f16lo(pr), zv = f16hi(pr);
+          const float sv = f16lo(vz[rr][e]), zv = f16hi(vz[rr][e]);
           c1 = (sv != 0.f ? sv : 1.f) * two_mF / wt;
-          rw = (sv != 0.f ? zv * __builtin_amdgcn_rcpf(sv) : zv) * wt;
+          w1 = (sv != 0.f ? zv * __builtin_amdgcn_rcpf(sv) : zv) * wt;
         }
         cf[e] = c1;
-        // A-operand position of token r: (iteration, k-step, lane group, m, half)
-        const int it = r / C::TIT, rr = r % C::TIT;
-        int gg, ks, m, hf;
-        if (BITS == 2) {
-          gg = rr / 16;
-          hf = (rr % 16) / 8;
-          ks = (rr % 8) / 4;
-          m = rr % 4;
-        } else {
-          ks = rr / 32;
-          gg = (rr % 32) / 8;
-          hf = (rr % 8) / 4;
-          m = rr % 4;
-        }
-        const int pos = ((it * C::NK + ks) * 4 + gg) * 8 + 2 * m + hf;
-        const _Float16 hi = (_Float16)rw;
-        rh[pos] = hi;
-        rl[pos] = (_Float16)(rw - (float)hi);
+        rw[rr][e] = w1;
       }
-      ((float4*)coef)[r8 / 4] = make_float4(cf[0], cf[1], cf[2], cf[3]);
-      ((float4*)coef)[r8 / 4 + 1] = make_float4(cf[4], cf[5], cf[6], cf[7]);
+      coef[tb_run[rr] / 4] = make_float4(cf[0], cf[1], cf[2], cf[3]);
     }
-    // third row: zeros, read by the A-operand rows 2..15 of the extra tile
-    u4* zr = (u4*)(lds + M::VR + 2 * kMaxSplitTokens * 2);
-    for (int e = tid; e < kMaxSplitTokens * 2 / 16; e += kThreads) zr[e] = u4{0u, 0u, 0u, 0u};
+    // A-operand element 2 m + hf of this block is token run hf, slot m
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float a0 = rw[0][m], a1 = rw[1][m];
+      hi[m] = pack_f16x2(a0, a1);
+      lo[m] = pack_f16x2(a0 - f16lo(hi[m]), a1 - f16hi(hi[m]));
+    }
+    ((u4*)rh)[tid] = u4{hi[0], hi[1], hi[2], hi[3]};
+    ((u4*)(rh + kMaxSplitTokens))[tid] = u4{lo[0], lo[1], lo[2], lo[3]};
+    ((u4*)(rh + 2 * kMaxSplitTokens))[tid] = u4{0u, 0u, 0u, 0u};  // the zero row
   } else if (r8 < ng * kHeadDim) {
     float4* vg = (float4*)(lds + M::VA);  // (sigma, rho) of two pairs per float4
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const uint32_t p0 = (e < 4 ? vz0 : vz1)[e & 3], p1 = (e < 4 ? vz0 : vz1)[(e + 1) & 3];
+      const uint32_t p0 = vz[e >> 2][e & 3], p1 = vz[e >> 2][(e + 1) & 3];
       const float s0 = f16lo(p0), z0 = f16hi(p0), s1 = f16lo(p1), z1 = f16hi(p1);
       vg[(r8 + e) / 2] = make_float4(s0 != 0.f ? s0 : 1.f, s0 != 0.f ? z0 * __builtin_amdgcn_rcpf(s0) : z0,
                                      s1 != 0.f ? s1 : 1.f, s1 != 0.f ? z1 * __builtin_amdgcn_rcpf(s1) : z1);
@@ -465,13 +515,13 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   // extra-tile rows: 0 = hi part, 1 = lo part, 2..15 = the zero row
   const int rrow = (ri < 2 ? ri : 2) * kMaxSplitTokens + 8 * g;
 
+  // the next iteration's codes are in flight while this one is computed
   for (int it = wv;; it += kWaves) {
     const int t0 = tb + it * C::TIT;
     if (t0 >= te) break;
     Codes nxt;
     const int t1 = t0 + kWaves * C::TIT;
     if (t1 < te) load_codes(t1, nxt);
-
     const int rel = t0 - tb;
     const int gi = rel / kGroup;
 
@@ -507,11 +557,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
       for (int j = 0; j < 4; ++j)
         if (t0 + tk0 + (j >> 1) + C::D2 * (j & 1) >= te) S[j] = -INFINITY;
     }
-    float mx = fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 4));
-    mx = fmaxf(mx, __shfl_xor(mx, 8));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mx = head_max(fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3])));
     if (__any(mx > m_run + (float)kThr)) {
       const float mn = fmaxf(m_run, mx);
       const float sc = exp2_fast(m_run - mn);
@@ -597,10 +643,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   // ---- per-wave result: numerator N and normaliser l (same scale) --------
   float lw;
   if (VAX == KVQ_TOKEN_WISE) {
-    lsum += __shfl_xor(lsum, 4);
-    lsum += __shfl_xor(lsum, 8);
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
+    lsum = head_sum(lsum);
     const float off = __shfl(X[0] + X[1], n);
     const float s24 = ldexpf(1.f, F + 24), sF = ldexpf(1.f, F);
 #pragma unroll
