@@ -153,6 +153,14 @@ def cache_tensors(fmt: Format, batch: int, max_len: int, num_pages: int = 0, dev
     return [torch.zeros(max(s, 16), dtype=torch.uint8, device=device) for s in sizes]
 
 
+def workspace_tensor(fmt: Format, batch: int, max_len: int, num_splits: int = 0, device="cuda"):
+    """Zero-filled workspace for decode calls (its arrival counters must start
+    at zero; each call leaves them zero again)."""
+    import torch
+    ws = kvq_workspace_size(fmt, batch, max_len, num_splits)
+    return torch.zeros(max(ws, 16), dtype=torch.uint8, device=device)
+
+
 def _cache_struct(cache):
     return Cache(*[c.data_ptr() for c in cache])
 
@@ -177,8 +185,7 @@ def decode_attention_quant(fmt: Format, q, cache, seq_lens, max_len, softmax_sca
     _require_gpu(q, seq_lens, out, page_table)
     B = q.shape[0]
     if workspace is None:
-        ws = kvq_workspace_size(fmt, B, max_len, num_splits)
-        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=q.device)
+        workspace = workspace_tensor(fmt, B, max_len, num_splits, q.device)
     maxp = 0 if page_table is None else page_table.shape[1]
     od = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
     cs = _cache_struct(cache)
@@ -197,8 +204,7 @@ def decode_attention_bf16(fmt: Format, q, k, v, seq_lens, max_len, softmax_scale
     _require_gpu(q, k, v, seq_lens, out, page_table)
     B = q.shape[0]
     if workspace is None:
-        ws = kvq_workspace_size(fmt, B, max_len, num_splits)
-        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=q.device)
+        workspace = workspace_tensor(fmt, B, max_len, num_splits, q.device)
     maxp = 0 if page_table is None else page_table.shape[1]
     od = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
     _check(lib().decode_attention_bf16(ctypes.byref(fmt), _ptr(q), _ptr(k), _ptr(v),

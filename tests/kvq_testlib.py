@@ -104,3 +104,54 @@ def cache_bytes_equal(gpu_cache, orc_cache):
             bad = np.nonzero(gb != ob)[0]
             return False, f"array {i}: {bad.size} bytes differ, first at {bad[:8]}"
     return True, ""
+
+
+def pack_rowwise(w, fmt, table=None, num_pages=0, device="cuda", log=None):
+    """Pack a large workload one sequence at a time (host draw -> GPU pack),
+    without holding the whole fp32 K/V anywhere. Returns the cache tensors."""
+    import torch
+    import bit_quantized_kv_int2_amd as kvq
+    H, D = w.num_kv_heads, w.head_dim
+    L = w.max_len
+    cache = kvq.cache_tensors(fmt, w.batch, L, num_pages, device=device)
+    offs = w.outlier_offsets()
+    kh = np.empty((H, L, D), np.float32)
+    vh = np.empty((H, L, D), np.float32)
+    for b in range(w.batch):
+        Lb = int(w.seq_lens[b])
+        if Lb == 0:
+            continue
+        w.kv_row("k", b, length=Lb, offsets=offs, out=kh[:, :Lb])
+        w.kv_row("v", b, length=Lb, out=vh[:, :Lb])
+        kd = torch.from_numpy(np.ascontiguousarray(kh[:, :Lb])).to(device)[None]
+        vd = torch.from_numpy(np.ascontiguousarray(vh[:, :Lb])).to(device)[None]
+        lens = torch.tensor([Lb], dtype=torch.int32, device=device)
+        if table is None:
+            # contiguous rows are laid out for max_len tokens: every sequence full length
+            assert Lb == L, "row-wise contiguous packing needs equal lengths"
+            sizes = kvq.kvq_cache_sizes(fmt, 1, L)
+            rc = [c[b * n:(b + 1) * n] for c, n in zip(cache, sizes)]
+            kvq.kv_quantize_pack(fmt, kd, vd, lens, rc, max_len=Lb)
+        else:
+            pt = torch.from_numpy(np.ascontiguousarray(table[b:b + 1])).to(device)
+            kvq.kv_quantize_pack(fmt, kd, vd, lens, cache, page_table=pt, max_len=Lb)
+        if log and b % 16 == 15:
+            torch.cuda.synchronize()
+            log(f"packed {b + 1}/{w.batch}")
+    torch.cuda.synchronize()
+    return cache
+
+
+def unit_host_cache(w, fmt_o, gpu_cache, b, table=None, num_pages=0):
+    """Host copy of the packed cache restricted to what the oracle needs for
+    sequence b: the contiguous row, or the whole paged pool."""
+    import bit_quantized_kv_int2_amd as kvq
+    if table is None:
+        sizes = kvq.kvq_cache_sizes(gpu_format(w), 1, w.max_len)
+        host = [c[b * n:(b + 1) * n].cpu().numpy() for c, n in zip(gpu_cache, sizes)]
+        shapes = oracle.cache_shapes(fmt_o, 1, w.max_len)
+    else:
+        host = [c.cpu().numpy() for c in gpu_cache]
+        shapes = oracle.cache_shapes(fmt_o, 0, 0, num_pages)
+    return [x[:int(np.prod(sh)) * np.dtype(dt).itemsize].view(dt).reshape(sh)
+            for x, (dt, sh) in zip(host, shapes)]
