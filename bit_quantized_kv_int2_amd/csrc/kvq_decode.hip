@@ -67,25 +67,28 @@ __device__ inline uint32_t pack_f16x2(float lo, float hi) {
   // v_cvt_pk_f16_f32: both halves rounded to nearest even in one instruction
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), h2));
 }
+// two binary16 products, each rounded once (v_pk_mul_f16); operands are
+// taken by value: bit-casting an ext-vector element in place reads element 0
+__device__ inline uint32_t mul_f16x2(uint32_t x, uint32_t y) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, x) * __builtin_bit_cast(h2, y));
+}
 __device__ inline float f16lo(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFF)); }
 __device__ inline float f16hi(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16)); }
 __device__ inline float f16val(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
 __device__ inline float bf16val(uint16_t u) { return __builtin_bit_cast(float, (uint32_t)u << 16); }
 
-__device__ inline float wave_max(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ inline float wave_sum(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
 // Cross-lane reductions without LDS: DPP row rotations inside 16-lane rows,
 // v_permlane16/32_swap across rows.
+// Every lane of every row is a valid source for these rotations, so the
+// bound-control form is exact and lets the compiler fold the move into the
+// consuming max / add (one DPP instruction per step).
 template <int R>
 __device__ inline float ror(float x) {  // lane l of a 16-lane row reads lane (l - R) mod 16
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + R, 0xF, 0xF, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + R, 0xF, 0xF, true));
+}
+template <int R>
+__device__ inline uint32_t ror_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x120 + R, 0xF, 0xF, true);
 }
 __device__ inline float swap32_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
@@ -127,9 +130,35 @@ __device__ inline float row_sum(float x) {
   x += ror<4>(x);
   return x + ror<8>(x);
 }
+__device__ inline uint32_t row_max_u(uint32_t x) {
+  x = max(x, ror_u<1>(x));
+  x = max(x, ror_u<2>(x));
+  x = max(x, ror_u<4>(x));
+  return max(x, ror_u<8>(x));
+}
+__device__ inline uint32_t swap32_max_u(uint32_t x) {
+  auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max((uint32_t)r[0], (uint32_t)r[1]);
+}
+__device__ inline uint32_t swap16_max_u(uint32_t x) {
+  auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return max((uint32_t)r[0], (uint32_t)r[1]);
+}
+// whole-wave reductions
+__device__ inline float wave_max_dpp(float x) { return swap16_max(swap32_max(row_max(x))); }
+__device__ inline float wave_sum_dpp(float x) { return swap16_sum(swap32_sum(row_sum(x))); }
+__device__ inline uint32_t wave_max_u(uint32_t x) { return swap16_max_u(swap32_max_u(row_max_u(x))); }
+// largest binary16 bit pattern (sign cleared) among the low halves of 8 words
+__device__ inline uint32_t max_lo16(const u4& a, const u4& b) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) m = max(m, max(a[e] & 0x7FFFu, b[e] & 0x7FFFu));
+  return m;
+}
 
-// exponent e with x < 2^e (x > 0), 0 for x == 0
-__device__ inline int exp_above(float x) { return x > 0.f ? ilogbf(x) + 1 : 0; }
+// exponent e with x < 2^e (x > 0), 0 for x == 0: the frexp exponent
+// (x = f * 2^e with 0.5 <= f < 1), one v_frexp_exp_i32_f32
+__device__ inline int exp_above(float x) { return __builtin_amdgcn_frexp_expf(x); }
 
 // Unpack one 32-bit word of INT4 codes into one k-step of fp16 subnormals:
 // VGPR m holds codes (m, m+4), weight 16^(m&1).
@@ -169,6 +198,16 @@ struct Cfg {
     const int base = BITS == 4 ? 8 * (gi >> 1) + 2 * (gi & 1) : 2 * gi;
     return 16 * q + base + (j >> 1) + D2 * (j & 1);
   }
+  // QK^T B-operand position of channel d: half hf of VGPR m of k-step s, as
+  // a binary16 index ((s * 4 + m) * 2 + hf); inverse of k_run
+  __device__ static inline int qpos(int d) {
+    const int m = d & 3;
+    const int s = BITS == 4 ? d >> 3 : 2 * (d >> 4) + ((d >> 2) & 1);
+    const int hf = BITS == 4 ? (d >> 2) & 1 : (d >> 3) & 1;
+    return (s * 4 + m) * 2 + hf;
+  }
+  // 1 / weight of channel d's code slot (its bit offset within its byte)
+  __device__ static inline float inv_wd(int d) { return 1.0f / (float)(1 << (BITS * (d % SLOTS))); }
 };
 
 // LDS layout (bytes), sized for the largest split.
@@ -200,8 +239,12 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   float* qs = (float*)(lds + M::QS);
   float* red = (float*)(lds + M::RED);
 
-  const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63;
+  // work-item and work-group ids straight from the builtins: this file is
+  // built with the IEEE mode bit cleared, which keeps the device library's
+  // id helpers from being inlined
+  const int sp = __builtin_amdgcn_workgroup_id_x(), h = __builtin_amdgcn_workgroup_id_y(),
+            b = __builtin_amdgcn_workgroup_id_z();
+  const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps addressing scalar
   const int H = a.num_kv_heads, Hq = H * kGqa;
   const int L = min(max(a.seq_lens[b], 0), a.max_len);  // contract: 0 <= len <= max_len
@@ -282,16 +325,30 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   // Token-wise (s, z): thread t owns the 8 tokens of one A-operand block of
   // the extra PV tile (iteration t/8, k-step (t/4)%2, lane group t%4), loaded
   // as two 16-byte runs of 4 tokens. Channel-wise V: thread t owns pairs
-  // 8t..8t+7 (one 32-byte load). Values stay in registers for phase B.
+  // 8t..8t+7 (one 32-byte load). Channel-wise K: thread (group t/16, k-step
+  // t%16) owns the 8 channels that k-step feeds. Values stay in registers
+  // for phase B.
+  unsigned* redu = (unsigned*)red;
   {
     const int d = lane * 2;  // wave wv loads query head wv
-    uint32_t qq = *(const uint32_t*)(a.q + (row0 + wv) * kHeadDim + d);
-    float q0 = bf16val((uint16_t)(qq & 0xFFFF)), q1 = bf16val((uint16_t)(qq >> 16));
-    qs[wv * 128 + d] = q0;
-    qs[wv * 128 + d + 1] = q1;
-    float m = wave_max(fmaxf(fabsf(q0), fabsf(q1)));
-    float sum = wave_sum(q0 + q1);
-    if (lane == 0) { red[wv] = m; red[20 + wv] = sum; }
+    const uint32_t qq = *(const uint32_t*)(a.q + (row0 + wv) * kHeadDim + d);
+    const float q0 = bf16val((uint16_t)(qq & 0xFFFF)), q1 = bf16val((uint16_t)(qq >> 16));
+    const float m = wave_max_dpp(fmaxf(fabsf(q0), fabsf(q1)));
+    if (KAX == KVQ_CHANNEL_WISE) {
+      // q * 2^-Eq / w(d) in binary16 (|.| < 1; exact: a bf16 value scaled by
+      // powers of two), stored in B-operand order for the per-group products
+      const int Eq = exp_above(m);
+      const float t = ldexpf(1.f, -Eq);
+      _Float16* qh = (_Float16*)(lds + M::QS) + wv * 128;
+      qh[C::qpos(d)] = (_Float16)(q0 * t * C::inv_wd(d));
+      qh[C::qpos(d + 1)] = (_Float16)(q1 * t * C::inv_wd(d + 1));
+      if (lane == 0) redu[wv] = (unsigned)Eq;
+    } else {
+      qs[wv * 128 + d] = q0;
+      qs[wv * 128 + d + 1] = q1;
+      const float sum = wave_sum_dpp(q0 + q1);
+      if (lane == 0) { red[wv] = m; red[20 + wv] = sum; }
+    }
   }
   // tokens of this thread's block: run r (0, 1) covers tb_run[r] .. +3
   int tb_run[2];
@@ -307,39 +364,68 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   }
   const int r8 = 8 * tid;  // first pair (channel-wise V)
   u4 vz[2] = {u4{0u, 0u, 0u, 0u}, u4{0u, 0u, 0u, 0u}};  // V (s, z): 2 runs of 4 tokens, or 8 pairs
-  u4 kz[2] = {u4{0u, 0u, 0u, 0u}, u4{0u, 0u, 0u, 0u}};  // token-wise K (s, z): 2 runs of 4 tokens
+  u4 kz[2] = {u4{0u, 0u, 0u, 0u}, u4{0u, 0u, 0u, 0u}};  // K (s, z): 2 runs of 4 tokens, or 8 channels
   if (VAX == KVQ_TOKEN_WISE) {
-    float m = 0.f;
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
       if (tb_run[rr] < ntok) {
         vz[rr] = *(const u4*)vsz_tok(tb + tb_run[rr]);
+        if (tb_run[rr] + 4 > ntok) {  // tokens past the end contribute (s, z) = (0, 0)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float sv = f16lo(vz[rr][e]);
-          if (tb_run[rr] + e < ntok) m = fmaxf(m, sv != 0.f ? sv : 1.f);
+          for (int e = 1; e < 4; ++e)
+            if (tb_run[rr] + e >= ntok) vz[rr][e] = 0u;
         }
       }
     }
-    m = wave_max(m);
-    if (lane == 0) red[8 + wv] = m;
+    // largest scale of the split (scales are >= 0, so bit patterns order as values)
+    const uint32_t mb = wave_max_u(max_lo16(vz[0], vz[1]));
+    if (lane == 0) redu[8 + wv] = mb;
   } else if (r8 < ng * kHeadDim) {
     const u4* p = (const u4*)vsz_chan(tb + (r8 / kHeadDim) * kGroup, r8 % kHeadDim);
     vz[0] = p[0];
     vz[1] = p[1];
   }
+  const int ck_s = tid & 15, ck_g = tid >> 4;  // channel-wise K: k-step, group
+  const bool ck_live = KAX == KVQ_CHANNEL_WISE && ck_g < ng;
   if (KAX == KVQ_TOKEN_WISE) {
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr)
       if (tb_run[rr] < ntok) kz[rr] = *(const u4*)ksz_tok(tb + tb_run[rr]);
+  } else if (ck_live) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) kz[hf] = *(const u4*)ksz_chan(tb + ck_g * kGroup, C::k_run(ck_s, hf));
+  }
+  // Channel-wise K, per channel of the thread's group: s' = s * 2^(14 - es)
+  // with every s of the group < 2^es (s' < 2^14), and the offset weight
+  // rho' = w * (z / s) * 2^(es - 14); a channel with s == 0 (all codes 0)
+  // takes s' = 2^13 and rho' = w * z * 2^-13, which gives the same offset.
+  uint32_t spk[4];
+  float rho[8];
+  int es = 0;
+  if (KAX == KVQ_CHANNEL_WISE) {
+    const uint32_t mb = row_max_u(max_lo16(kz[0], kz[1]));  // the 16 lanes of a row share the group
+    es = (int)(mb >> 10) - 14;
+    const float up = ldexpf(1.f, 14 - es), dn = ldexpf(1.f, es - 14);
+    float sp[8];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float sv = f16lo(kz[hf][m]), zv = f16hi(kz[hf][m]);
+        const bool nz = sv != 0.f;
+        sp[4 * hf + m] = nz ? sv * up : 8192.f;
+        rho[4 * hf + m] = zv * (nz ? __builtin_amdgcn_rcpf(sv) * (C::w(m) * dn) : C::w(m) * (1.f / 8192.f));
+      }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) spk[m] = pack_f16x2(sp[m], sp[4 + m]);
   }
   if (tid < 16) ((u4*)(lds + M::QZ))[tid] = u4{0u, 0u, 0u, 0u};
   __syncthreads();
-  const float qmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   int F = kThr - 14;  // P'' = P * coef * 2^-F, max P'' < 2^14
   if (VAX == KVQ_TOKEN_WISE) {
-    const float smax = fmaxf(fmaxf(red[8], red[9]), fmaxf(red[10], red[11]));
-    F = exp_above(smax) + kThr - 14;
+    // every scale < 2^Fs (scales of 0 are replaced by 1, hence Fs >= 1)
+    const uint32_t mb = max(max(redu[8], redu[9]), max(redu[10], redu[11]));
+    F = max((int)(mb >> 10) - 14, 1) + kThr - 14;
   }
   const float two_mF = ldexpf(1.f, -F);
 
@@ -347,64 +433,30 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
   u4* qB = (u4*)(lds + M::QB);
   int E = 0;  // token-wise K: q'' = q * 2^-E, max |q''| < 2^14
   if (KAX == KVQ_CHANNEL_WISE) {
-    // thread = (group gi, k-step s): the 8 channels of k-step s for all 4
-    // heads. The 16 lanes of a group share, per head, one exponent E (so
-    // that max |q''| < 2^14) and the bias sum.
+    // q'' = (q 2^-Eq / w) * s' rounded once to binary16 (one packed multiply
+    // per two channels); S = alpha 2^(10 + es + Eq) acc + alpha 2^Eq sum q'' rho'
+    // uses the rounded q'' in both terms, so rounding moves only the weight of x^
     float2* kb = (float2*)(lds + M::KB);
-    const int s = tid & 15, gi = tid >> 4;
-    const bool live = gi < ng;
-    float sig[8], rho[8], zr[8];
-    if (live) {
+    const u4* qh = (const u4*)(lds + M::QS);
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const u4 pz = *(const u4*)ksz_chan(tb + gi * kGroup, C::k_run(s, hf));
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float sv = f16lo(pz[m]), zv = f16hi(pz[m]);
-          // s == 0: every code is 0 and the group is the constant z
-          sig[4 * hf + m] = alpha * sv * C::inv_w(m);
-          rho[4 * hf + m] = sv != 0.f ? zv * __builtin_amdgcn_rcpf(sv) : 0.f;
-          zr[4 * hf + m] = sv != 0.f ? 0.f : alpha * zv;
-        }
-      }
-    }
-#pragma unroll
-    for (int qh = 0; qh < 4; ++qh) {
-      float aqs[8], qv[8];
-      float amax = 0.f;
-      if (live) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const float4 q4 = *(const float4*)(qs + qh * 128 + C::k_run(s, hf));
-          qv[4 * hf + 0] = q4.x; qv[4 * hf + 1] = q4.y; qv[4 * hf + 2] = q4.z; qv[4 * hf + 3] = q4.w;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          aqs[e] = qv[e] * sig[e];
-          amax = fmaxf(amax, fabsf(aqs[e]));
-        }
-      }
-      amax = row_max(amax);
-      const int Eg = exp_above(amax) - 14;
-      const float tm = ldexpf(1.f, -Eg), tp = ldexpf(1.f, Eg);
+    for (int qh_i = 0; qh_i < 4; ++qh_i) {
+      const u4 qv = qh[qh_i * 16 + ck_s];
+      u4 wds;
       float bias = 0.f;
-      if (live) {
-        uint32_t wds[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t pk = pack_f16x2(aqs[m] * tm, aqs[4 + m] * tm);
-          wds[m] = pk;
-          // consistent offset: the rounded operand (times its slot weight and
-          // 2^E) times z/s, so rounding q*s moves only the weight of x^
-          bias = fmaf(f16lo(pk) * rho[m] + f16hi(pk) * rho[4 + m], C::w(m) * tp, bias);
-          bias = fmaf(qv[m], zr[m], fmaf(qv[4 + m], zr[4 + m], bias));
-        }
-        qB[(gi * 4 + qh) * 16 + s] = u4{wds[0], wds[1], wds[2], wds[3]};
+      for (int m = 0; m < 4; ++m) {
+        wds[m] = mul_f16x2(qv[m], spk[m]);
+        bias = fmaf(f16lo(wds[m]), rho[m], fmaf(f16hi(wds[m]), rho[4 + m], bias));
       }
+      if (ck_live) qB[(ck_g * 4 + qh_i) * 16 + ck_s] = wds;
       bias = row_sum(bias);
-      if (live && s == 0) kb[gi * 4 + qh] = make_float2(ldexpf(1.f, Eg + 24), bias);
+      if (ck_live && ck_s == 0) {
+        const int Eq = (int)redu[qh_i];
+        kb[ck_g * 4 + qh_i] = make_float2(alpha * ldexpf(1.f, 10 + es + Eq), alpha * ldexpf(bias, Eq));
+      }
     }
   } else {
+    const float qmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     E = exp_above(qmax) - 14;
     const float two_mE = ldexpf(1.f, -E);
     if (tid < 64) {
@@ -435,7 +487,9 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     }
   }
   if (VAX == KVQ_TOKEN_WISE) {
-    // coef[t] = sigma * 2^-F / w(t); extra-tile rows hold w(t) * rho as hi + lo fp16
+    // coef[t] = sigma * 2^-F / w(t); extra-tile rows hold w(t) * rho as hi + lo
+    // fp16 (sigma = s, or 1 where s == 0; rho = z / sigma). Runs start at a
+    // multiple of 4 tokens, so token e of a run has slot e % SLOTS.
     float4* coef = (float4*)(lds + M::VA);
     _Float16* rh = (_Float16*)(lds + M::VR);
     float rw[2][4];
@@ -444,16 +498,11 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
       float cf[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = tb_run[rr] + e;
-        const float wt = (float)(1 << (BITS * ((r % C::TPW) % C::SLOTS)));
-        float c1 = 0.f, w1 = 0.f;
-        if (r < ntok) {
-          const float sv = f16lo(vz[rr][e]), zv = f16hi(vz[rr][e]);
-          c1 = (sv != 0.f ? sv : 1.f) * two_mF / wt;
-          w1 = (sv != 0.f ? zv * __builtin_amdgcn_rcpf(sv) : zv) * wt;
-        }
-        cf[e] = c1;
-        rw[rr][e] = w1;
+        const float wt = (float)(1 << (BITS * (e % C::SLOTS)));
+        const float sv = f16lo(vz[rr][e]), zv = f16hi(vz[rr][e]);
+        const float sg = sv != 0.f ? sv : 1.f;
+        cf[e] = sg * (two_mF / wt);
+        rw[rr][e] = zv * (__builtin_amdgcn_rcpf(sg) * wt);
       }
       coef[tb_run[rr] / 4] = make_float4(cf[0], cf[1], cf[2], cf[3]);
     }
@@ -717,8 +766,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
 // LSE combine of the split partials: O = sum_i 2^(m_i - M) l_i O_i / sum_i 2^(m_i - M) l_i.
 __global__ void __launch_bounds__(128) combine_kernel(const float* part_o, const float* part_ml,
                                                       int num_splits, void* out, int out_bf16) {
-  const long row = blockIdx.x;
-  const int d = threadIdx.x;
+  const long row = __builtin_amdgcn_workgroup_id_x();
+  const int d = __builtin_amdgcn_workitem_id_x();
   const float* ml = part_ml + row * num_splits * 2;
   float M = -INFINITY;
   for (int i = 0; i < num_splits; ++i) M = fmaxf(M, ml[2 * i]);
@@ -727,7 +776,7 @@ __global__ void __launch_bounds__(128) combine_kernel(const float* part_o, const
     for (int i = 0; i < num_splits; ++i) {
       const float m = ml[2 * i];
       if (m == -INFINITY) continue;
-      const float w = exp2f(m - M) * ml[2 * i + 1];
+      const float w = exp2_fast(m - M) * ml[2 * i + 1];
       num = fmaf(w, part_o[(row * num_splits + i) * kHeadDim + d], num);
       den += w;
     }
