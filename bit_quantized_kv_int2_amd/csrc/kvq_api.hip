@@ -75,25 +75,24 @@ kvq_status kvq_cache_sizes(const kvq_format* f, int32_t batch, int32_t max_len,
   return KVQ_OK;
 }
 
-// Token split per (sequence, KV head): a multiple of kSplitQuantum tokens,
-// at most kMaxSplitTokens (the per-split fold operands sit in LDS), and
-// enough workgroups to fill 256 CUs several times over.
+// Token split per (sequence, KV head): a multiple of kSplitQuantum tokens.
+// A decode work-group walks its split in chunks of kChunkTokens (the fold
+// operands of one chunk sit in LDS), so a split may span the whole sequence;
+// the automatic plan splits only as far as needed for kTargetGroups
+// work-groups over the chip.
+static constexpr long kTargetGroups = 2048;
+
 static int plan_split_tokens(int batch, int num_kv_heads, int max_len, int num_splits) {
   if (max_len <= 0) return kSplitQuantum;
   const int quanta = (max_len + kSplitQuantum - 1) / kSplitQuantum;
   if (num_splits <= 0) {
     const long units = (long)batch * num_kv_heads;
-    const long want_groups = 1536;
-    long ns = (want_groups + units - 1) / units;
-    long ns_min = (max_len + kMaxSplitTokens - 1) / kMaxSplitTokens;
-    if (ns < ns_min) ns = ns_min;
+    long ns = units > 0 ? (kTargetGroups + units - 1) / units : 1;
     if (ns > quanta) ns = quanta;
     num_splits = (int)ns;
   }
-  int q_per = (quanta + num_splits - 1) / num_splits;
-  int st = q_per * kSplitQuantum;
-  if (st > kMaxSplitTokens) st = kMaxSplitTokens;
-  return st;
+  const int q_per = (quanta + num_splits - 1) / num_splits;
+  return q_per * kSplitQuantum;
 }
 
 static int splits_for(int max_len, int split_tokens) {
@@ -115,8 +114,7 @@ static kvq_status resolve_splits(const kvq_format* f, int batch, int max_len, in
                                  int* split_tokens, int* nsplit) {
   if (req < 0) return KVQ_ERR_BAD_SHAPE;
   int quanta = max_len > 0 ? (max_len + kSplitQuantum - 1) / kSplitQuantum : 1;
-  int min_splits = max_len > 0 ? (max_len + kMaxSplitTokens - 1) / kMaxSplitTokens : 1;
-  if (req > 0 && (req > quanta || req < min_splits)) return KVQ_ERR_BAD_SHAPE;
+  if (req > quanta) return KVQ_ERR_BAD_SHAPE;
   *split_tokens = plan_split_tokens(batch, f->num_kv_heads, max_len, req);
   *nsplit = splits_for(max_len, *split_tokens);
   return KVQ_OK;

@@ -54,7 +54,7 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kThr = 8;          // lazy-max threshold in log2 units: P <= 2^kThr
-constexpr int kMaxGroups = kMaxSplitTokens / kGroup;
+constexpr int kMaxGroups = kChunkTokens / kGroup;
 
 __device__ inline h8 as_h8(u4 v) { return __builtin_bit_cast(h8, v); }
 __device__ inline f4 mfma(u4 a, u4 b, f4 c) {
@@ -218,11 +218,11 @@ struct Lds {
   static constexpr int QB_BYTES = (KAX == KVQ_CHANNEL_WISE ? kMaxGroups : 1) * 4 * 16 * 16;
   static constexpr int QZ = QB + QB_BYTES;                       // 256 B of zeros (off-diagonal B)
   static constexpr int KB = QZ + 256;                            // chan-K (scale, bias) [groups][4] / tok-K (s',z'') [tokens]
-  static constexpr int KB_BYTES = KAX == KVQ_CHANNEL_WISE ? kMaxGroups * 4 * 8 : kMaxSplitTokens * 8;
+  static constexpr int KB_BYTES = KAX == KVQ_CHANNEL_WISE ? kMaxGroups * 4 * 8 : kChunkTokens * 8;
   static constexpr int VA = KB + KB_BYTES;                       // tok-V coef [tokens] / chan-V (sigma,rho) [groups][128]
-  static constexpr int VA_BYTES = VAX == KVQ_TOKEN_WISE ? kMaxSplitTokens * 4 : kMaxGroups * 128 * 8;
+  static constexpr int VA_BYTES = VAX == KVQ_TOKEN_WISE ? kChunkTokens * 4 : kMaxGroups * 128 * 8;
   static constexpr int VR = VA + VA_BYTES;                       // tok-V rho hi / lo / zero rows, fp16, A-operand order
-  static constexpr int VR_BYTES = VAX == KVQ_TOKEN_WISE ? 3 * kMaxSplitTokens * 2 : 0;
+  static constexpr int VR_BYTES = VAX == KVQ_TOKEN_WISE ? 3 * kChunkTokens * 2 : 0;
   static constexpr int RED = VR + VR_BYTES;                      // float [32] reductions
   static constexpr int TOTAL = RED + 32 * 4;
   // merge area reuses the front of LDS after the main loop
@@ -231,13 +231,19 @@ struct Lds {
   static_assert(ML + 4 * 4 * 2 * 4 <= RED, "merge area overlaps reductions");
 };
 
+// Work-groups per CU the register allocation targets (4 waves of 256 threads
+// per SIMD leave 128 VGPRs, 3 leave 168): INT2 with token-wise V fits in 128;
+// channel-wise V keeps a second 8-tile accumulator and INT4 twice the codes.
+constexpr int groups_per_cu(int bits, int vax) { return (bits == 2 && vax == KVQ_TOKEN_WISE) ? 4 : 3; }
+
 template <int BITS, int KAX, int VAX, bool PAGED>
-__global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_kernel(DecodeArgs a) {
   using C = Cfg<BITS>;
   using M = Lds<KAX, VAX>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[M::TOTAL];
   float* qs = (float*)(lds + M::QS);
   float* red = (float*)(lds + M::RED);
+  unsigned* redu = (unsigned*)red;
 
   // work-item and work-group ids straight from the builtins: this file is
   // built with the IEEE mode bit cleared, which keeps the device library's
@@ -268,8 +274,6 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     }
     return;
   }
-  const int ntok = te - tb;
-  const int ng = (ntok + kGroup - 1) / kGroup;
   const float alpha = a.scale_log2;
 
   // ---- cache addressing -------------------------------------------------
@@ -301,9 +305,9 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
     u4 k[C::KDW / 4];
     u4 v[C::NVW];
   };
-  const uint32_t koff = (uint32_t)(C::tok(g, ri >> 2, ri & 3) * C::KROW);
-  const uint32_t voff = (uint32_t)(g * kHeadDim + 8 * ri);  // words
-  auto load_codes = [&](int t0, Codes& cd) {
+  auto lane_koff = [](int lg, int lr) { return (uint32_t)(C::tok(lg, lr >> 2, lr & 3) * C::KROW); };
+  auto lane_voff = [](int lg, int lr) { return (uint32_t)(lg * kHeadDim + 8 * lr); };  // words
+  auto load_codes = [&](int t0, Codes& cd, uint32_t koff, uint32_t voff) {
     const long ch = chunk_of(t0);
     const unsigned char* kb = a.k_codes + (ch * kPage + t0 % kPage) * C::KROW + koff;
 #pragma unroll
@@ -314,21 +318,20 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
       cd.v[e] = *(const u4*)(vb + (e >> 1) * 4 * kHeadDim + 4 * (e & 1));
   };
 
-  // first iteration's codes go out before the prologue
+  // Wave wv owns the 128-token groups wv, wv + 4, wv + 8, ... of the split
+  // (64-token iterations 2G and 2G + 1 of each such group G). It builds the
+  // fold operands of exactly those groups into LDS slots no other wave reads,
+  // so after the query is shared the waves never wait for each other until
+  // the final merge.
+  // The first iteration's codes go out before anything else; later
+  // iterations (also across chunk boundaries) are loaded one ahead.
   Codes cur;
   {
-    const int t0 = tb + wv * C::TIT;
-    if (t0 < te) load_codes(t0, cur);
+    const int t0 = tb + 2 * wv * C::TIT;
+    if (t0 < te) load_codes(t0, cur, lane_koff(g, ri), lane_voff(g, ri));
   }
 
-  // ---- prologue phase A: loads, per-wave maxima ----------------------------
-  // Token-wise (s, z): thread t owns the 8 tokens of one A-operand block of
-  // the extra PV tile (iteration t/8, k-step (t/4)%2, lane group t%4), loaded
-  // as two 16-byte runs of 4 tokens. Channel-wise V: thread t owns pairs
-  // 8t..8t+7 (one 32-byte load). Channel-wise K: thread (group t/16, k-step
-  // t%16) owns the 8 channels that k-step feeds. Values stay in registers
-  // for phase B.
-  unsigned* redu = (unsigned*)red;
+  // ---- query: once per split -------------------------------------------------
   {
     const int d = lane * 2;  // wave wv loads query head wv
     const uint32_t qq = *(const uint32_t*)(a.q + (row0 + wv) * kHeadDim + d);
@@ -350,116 +353,14 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
       if (lane == 0) { red[wv] = m; red[20 + wv] = sum; }
     }
   }
-  // tokens of this thread's block: run r (0, 1) covers tb_run[r] .. +3
-  int tb_run[2];
-  {
-    const int it = tid >> 3, ks = (tid >> 2) & 1, gg = tid & 3;
-    if (BITS == 2) {
-      tb_run[0] = it * C::TIT + 16 * gg + 4 * ks;
-      tb_run[1] = tb_run[0] + 8;
-    } else {
-      tb_run[0] = it * C::TIT + 32 * ks + 8 * gg;
-      tb_run[1] = tb_run[0] + 4;
-    }
-  }
-  const int r8 = 8 * tid;  // first pair (channel-wise V)
-  u4 vz[2] = {u4{0u, 0u, 0u, 0u}, u4{0u, 0u, 0u, 0u}};  // V (s, z): 2 runs of 4 tokens, or 8 pairs
-  u4 kz[2] = {u4{0u, 0u, 0u, 0u}, u4{0u, 0u, 0u, 0u}};  // K (s, z): 2 runs of 4 tokens, or 8 channels
-  if (VAX == KVQ_TOKEN_WISE) {
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      if (tb_run[rr] < ntok) {
-        vz[rr] = *(const u4*)vsz_tok(tb + tb_run[rr]);
-        if (tb_run[rr] + 4 > ntok) {  // tokens past the end contribute (s, z) = (0, 0)
-#pragma unroll
-          for (int e = 1; e < 4; ++e)
-            if (tb_run[rr] + e >= ntok) vz[rr][e] = 0u;
-        }
-      }
-    }
-    // largest scale of the split (scales are >= 0, so bit patterns order as values)
-    const uint32_t mb = wave_max_u(max_lo16(vz[0], vz[1]));
-    if (lane == 0) redu[8 + wv] = mb;
-  } else if (r8 < ng * kHeadDim) {
-    const u4* p = (const u4*)vsz_chan(tb + (r8 / kHeadDim) * kGroup, r8 % kHeadDim);
-    vz[0] = p[0];
-    vz[1] = p[1];
-  }
-  const int ck_s = tid & 15, ck_g = tid >> 4;  // channel-wise K: k-step, group
-  const bool ck_live = KAX == KVQ_CHANNEL_WISE && ck_g < ng;
-  if (KAX == KVQ_TOKEN_WISE) {
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr)
-      if (tb_run[rr] < ntok) kz[rr] = *(const u4*)ksz_tok(tb + tb_run[rr]);
-  } else if (ck_live) {
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) kz[hf] = *(const u4*)ksz_chan(tb + ck_g * kGroup, C::k_run(ck_s, hf));
-  }
-  // Channel-wise K, per channel of the thread's group: s' = s * 2^(14 - es)
-  // with every s of the group < 2^es (s' < 2^14), and the offset weight
-  // rho' = w * (z / s) * 2^(es - 14); a channel with s == 0 (all codes 0)
-  // takes s' = 2^13 and rho' = w * z * 2^-13, which gives the same offset.
-  uint32_t spk[4];
-  float rho[8];
-  int es = 0;
-  if (KAX == KVQ_CHANNEL_WISE) {
-    const uint32_t mb = row_max_u(max_lo16(kz[0], kz[1]));  // the 16 lanes of a row share the group
-    es = (int)(mb >> 10) - 14;
-    const float up = ldexpf(1.f, 14 - es), dn = ldexpf(1.f, es - 14);
-    float sp[8];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float sv = f16lo(kz[hf][m]), zv = f16hi(kz[hf][m]);
-        const bool nz = sv != 0.f;
-        sp[4 * hf + m] = nz ? sv * up : 8192.f;
-        rho[4 * hf + m] = zv * (nz ? __builtin_amdgcn_rcpf(sv) * (C::w(m) * dn) : C::w(m) * (1.f / 8192.f));
-      }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) spk[m] = pack_f16x2(sp[m], sp[4 + m]);
-  }
   if (tid < 16) ((u4*)(lds + M::QZ))[tid] = u4{0u, 0u, 0u, 0u};
   __syncthreads();
-  int F = kThr - 14;  // P'' = P * coef * 2^-F, max P'' < 2^14
-  if (VAX == KVQ_TOKEN_WISE) {
-    // every scale < 2^Fs (scales of 0 are replaced by 1, hence Fs >= 1)
-    const uint32_t mb = max(max(redu[8], redu[9]), max(redu[10], redu[11]));
-    F = max((int)(mb >> 10) - 14, 1) + kThr - 14;
-  }
-  const float two_mF = ldexpf(1.f, -F);
-
-  // ---- prologue phase B: fold operands into LDS ------------------------------
-  u4* qB = (u4*)(lds + M::QB);
-  int E = 0;  // token-wise K: q'' = q * 2^-E, max |q''| < 2^14
-  if (KAX == KVQ_CHANNEL_WISE) {
-    // q'' = (q 2^-Eq / w) * s' rounded once to binary16 (one packed multiply
-    // per two channels); S = alpha 2^(10 + es + Eq) acc + alpha 2^Eq sum q'' rho'
-    // uses the rounded q'' in both terms, so rounding moves only the weight of x^
-    float2* kb = (float2*)(lds + M::KB);
-    const u4* qh = (const u4*)(lds + M::QS);
-#pragma unroll
-    for (int qh_i = 0; qh_i < 4; ++qh_i) {
-      const u4 qv = qh[qh_i * 16 + ck_s];
-      u4 wds;
-      float bias = 0.f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        wds[m] = mul_f16x2(qv[m], spk[m]);
-        bias = fmaf(f16lo(wds[m]), rho[m], fmaf(f16hi(wds[m]), rho[4 + m], bias));
-      }
-      if (ck_live) qB[(ck_g * 4 + qh_i) * 16 + ck_s] = wds;
-      bias = row_sum(bias);
-      if (ck_live && ck_s == 0) {
-        const int Eq = (int)redu[qh_i];
-        kb[ck_g * 4 + qh_i] = make_float2(alpha * ldexpf(1.f, 10 + es + Eq), alpha * ldexpf(bias, Eq));
-      }
-    }
-  } else {
+  if (KAX == KVQ_TOKEN_WISE) {
+    // token-wise K: q'' = q * 2^-E / w (max |q''| < 2^14), shared by all waves
     const float qmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    E = exp_above(qmax) - 14;
-    const float two_mE = ldexpf(1.f, -E);
+    const int E = exp_above(qmax) - 14;
     if (tid < 64) {
+      const float two_mE = ldexpf(1.f, -E);
       const int s = tid & 15, qh = tid >> 4;
       uint32_t wds[4];
 #pragma unroll
@@ -468,225 +369,373 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs a) {
         float v1 = qs[qh * 128 + C::k_run(s, 1) + m] * two_mE * C::inv_w(m);
         wds[m] = pack_f16x2(v0, v1);
       }
-      qB[qh * 16 + s] = u4{wds[0], wds[1], wds[2], wds[3]};
+      ((u4*)(lds + M::QB))[qh * 16 + s] = u4{wds[0], wds[1], wds[2], wds[3]};
     }
-    float4* ktok = (float4*)(lds + M::KB);  // (s', z'') of two tokens per float4
-    const float sc = alpha * ldexpf(1.f, E + 24);
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int t4 = tb_run[rr];  // 4 tokens
-      if (t4 < kMaxSplitTokens) {
-#pragma unroll
-        for (int e = 0; e < 4; e += 2) {
-          const bool v0 = t4 + e < ntok, v1 = t4 + e + 1 < ntok;
-          const uint32_t p0 = kz[rr][e], p1 = kz[rr][e + 1];
-          ktok[(t4 + e) / 2] = make_float4(v0 ? f16lo(p0) * sc : 0.f, v0 ? f16hi(p0) * alpha : 0.f,
-                                           v1 ? f16lo(p1) * sc : 0.f, v1 ? f16hi(p1) * alpha : 0.f);
-        }
-      }
-    }
+    __syncthreads();
   }
-  if (VAX == KVQ_TOKEN_WISE) {
-    // coef[t] = sigma * 2^-F / w(t); extra-tile rows hold w(t) * rho as hi + lo
-    // fp16 (sigma = s, or 1 where s == 0; rho = z / sigma). Runs start at a
-    // multiple of 4 tokens, so token e of a run has slot e % SLOTS.
-    float4* coef = (float4*)(lds + M::VA);
-    _Float16* rh = (_Float16*)(lds + M::VR);
-    float rw[2][4];
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      float cf[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float wt = (float)(1 << (BITS * (e % C::SLOTS)));
-        const float sv = f16lo(vz[rr][e]), zv = f16hi(vz[rr][e]);
-        const float sg = sv != 0.f ? sv : 1.f;
-        cf[e] = sg * (two_mF / wt);
-        rw[rr][e] = zv * (__builtin_amdgcn_rcpf(sg) * wt);
-      }
-      coef[tb_run[rr] / 4] = make_float4(cf[0], cf[1], cf[2], cf[3]);
-    }
-    // A-operand element 2 m + hf of this block is token run hf, slot m
-    uint32_t hi[4], lo[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float a0 = rw[0][m], a1 = rw[1][m];
-      hi[m] = pack_f16x2(a0, a1);
-      lo[m] = pack_f16x2(a0 - f16lo(hi[m]), a1 - f16hi(hi[m]));
-    }
-    ((u4*)rh)[tid] = u4{hi[0], hi[1], hi[2], hi[3]};
-    ((u4*)(rh + kMaxSplitTokens))[tid] = u4{lo[0], lo[1], lo[2], lo[3]};
-    ((u4*)(rh + 2 * kMaxSplitTokens))[tid] = u4{0u, 0u, 0u, 0u};  // the zero row
-  } else if (r8 < ng * kHeadDim) {
-    float4* vg = (float4*)(lds + M::VA);  // (sigma, rho) of two pairs per float4
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const uint32_t p0 = vz[e >> 2][e & 3], p1 = vz[e >> 2][(e + 1) & 3];
-      const float s0 = f16lo(p0), z0 = f16hi(p0), s1 = f16lo(p1), z1 = f16hi(p1);
-      vg[(r8 + e) / 2] = make_float4(s0 != 0.f ? s0 : 1.f, s0 != 0.f ? z0 * __builtin_amdgcn_rcpf(s0) : z0,
-                                     s1 != 0.f ? s1 : 1.f, s1 != 0.f ? z1 * __builtin_amdgcn_rcpf(s1) : z1);
-    }
-  }
-  __syncthreads();
+  const float ktok_sc = KAX == KVQ_TOKEN_WISE
+      ? alpha * ldexpf(1.f, exp_above(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))) - 14 + 24)
+      : 0.f;
 
-  // ---- per-lane constants of the main loop ---------------------------------
-  // compact scores: lane (n, g) holds tokens tk0 + {0, D2, 1, D2 + 1} (j = 0..3)
-  const int tk0 = C::tok(nq, g, 0);
-  // B operand of QK^T is block diagonal: column (head, q) is nonzero only in
-  // k-group q, so only lanes with g == q read q''; the others read zeros
-  const bool qlive = g == nq;
-  // PV B operand VGPR m of k-step k comes from lane src[k][m >> 1], register pk[m & 1]
-  int src[2][2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k)
-#pragma unroll
-    for (int m2 = 0; m2 < 2; ++m2) {
-      const int sq = BITS == 2 ? g : 2 * k + (g >> 1);
-      const int sg = BITS == 2 ? 2 * k + m2 : 2 * (g & 1) + m2;
-      src[k][m2] = 4 * (hh + 4 * sq + 16 * sg);  // byte address for ds_bpermute
-    }
-  // channel-wise V: 2^-F / weight of the compact values' tokens (pairs a = 0, 1)
-  float cw[2];
-#pragma unroll
-  for (int aa = 0; aa < 2; ++aa) {
-    const int slot = (tk0 + aa) % C::TPW;
-    cw[aa] = two_mF / (float)(1 << (BITS * (slot % C::SLOTS)));
-  }
-
+  // accumulators: O and X in units of 2^-F, m_run in log2 units
   f4 O[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) O[c] = f4{0.f, 0.f, 0.f, 0.f};
   f4 X = f4{0.f, 0.f, 0.f, 0.f};  // extra tile accumulator
   float m_run = -INFINITY;
   float lsum = 0.f;
-  const float Qh = red[20 + hh];
-  const _Float16* rbase = (const _Float16*)(lds + M::VR);
-  // extra-tile rows: 0 = hi part, 1 = lo part, 2..15 = the zero row
-  const int rrow = (ri < 2 ? ri : 2) * kMaxSplitTokens + 8 * g;
+  // P'' = P * coef * 2^-F with max P'' < 2^14. Token-wise V: F follows the
+  // largest scale this wave has seen and only grows (the accumulators are
+  // rescaled by the exact power of two when it does); channel-wise V: constant.
+  int F = kThr - 14;
 
-  // the next iteration's codes are in flight while this one is computed
-  for (int it = wv;; it += kWaves) {
-    const int t0 = tb + it * C::TIT;
-    if (t0 >= te) break;
-    Codes nxt;
-    const int t1 = t0 + kWaves * C::TIT;
-    if (t1 < te) load_codes(t1, nxt);
-    const int rel = t0 - tb;
-    const int gi = rel / kGroup;
+  // ---- chunks of up to kChunkTokens tokens: prologue, then the main loop ----
+  for (int cb = tb; cb < te; cb += kChunkTokens) {
+    const int ce = min(cb + kChunkTokens, te);
+    const int ntok = ce - cb;
+    const int ng = (ntok + kGroup - 1) / kGroup;
 
-    // QK^T over 16 k-steps of 8 channels per k-group: 64 tokens x 4 heads
-    float S[4];
+    // Per-lane prologue indices are derived from a copy of the lane id that
+    // the compiler must treat as new in every chunk: otherwise it hoists them
+    // (and the addresses built from them) out of the chunk loop and keeps
+    // them live through the main loop, which costs registers and occupancy.
+    int pl = lane;
+    asm volatile("" : "+v"(pl));
+    // lane l serves group gl = wv + 4 (l / 16) of the chunk: the 16 lanes of
+    // a DPP row share a group
+    const int gl = wv + 4 * (pl >> 4);
+    const bool glive = gl < ng;
+    // token-wise (s, z): lane l owns the 8 tokens of one A-operand block of
+    // the extra PV tile (iteration 2 gl + (l/8)%2, k-step (l/4)%2, lane group
+    // l%4) as two runs of 4 tokens, tb_run[r] .. +3
+    const int pit = 2 * gl + ((pl >> 3) & 1);
+    const int pblk = pit * 8 + (pl & 7);  // the block's index in A-operand order
+    int tb_run[2];
     {
-      const u4* qb = (const u4*)(lds + (qlive ? M::QB + ((KAX == KVQ_CHANNEL_WISE ? gi : 0) * 4 + hh) * 256
-                                              : M::QZ));
-      f4 c0 = f4{0.f, 0.f, 0.f, 0.f}, c1 = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const uint32_t w = BITS == 4 ? cur.k[s >> 2][s & 3] : cur.k[s >> 3][(s >> 1) & 3];
-        const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, s & 1);
-        if (s & 1) c1 = mfma(av, qb[s], c1);
-        else c0 = mfma(av, qb[s], c0);
-      }
-      const f4 acc = c0 + c1;
-      if (KAX == KVQ_CHANNEL_WISE) {
-        const float2 sb = ((const float2*)(lds + M::KB))[gi * 4 + hh];  // (2^(E+24), bias)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) S[j] = fmaf(acc[j], sb.x, sb.y);
+      const int ks = (pl >> 2) & 1, gg = pl & 3;
+      if (BITS == 2) {
+        tb_run[0] = pit * C::TIT + 16 * gg + 4 * ks;
+        tb_run[1] = tb_run[0] + 8;
       } else {
-        const float4* kt = (const float4*)(lds + M::KB);  // (s', z'') per token, two per float4
-        const float4 p0 = kt[(rel + tk0) / 2], p1 = kt[(rel + tk0 + C::D2) / 2];
-        S[0] = fmaf(acc[0], p0.x, p0.y * Qh);  // token tk0
-        S[1] = fmaf(acc[1], p1.x, p1.y * Qh);  // tk0 + D2
-        S[2] = fmaf(acc[2], p0.z, p0.w * Qh);  // tk0 + 1
-        S[3] = fmaf(acc[3], p1.z, p1.w * Qh);  // tk0 + D2 + 1
+        tb_run[0] = pit * C::TIT + 32 * ks + 8 * gg;
+        tb_run[1] = tb_run[0] + 4;
       }
     }
-    if (t0 + C::TIT > te) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (t0 + tk0 + (j >> 1) + C::D2 * (j & 1) >= te) S[j] = -INFINITY;
-    }
-    const float mx = head_max(fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3])));
-    if (__any(mx > m_run + (float)kThr)) {
-      const float mn = fmaxf(m_run, mx);
-      const float sc = exp2_fast(m_run - mn);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) O[c] *= sc;
-      X *= sc;
-      lsum *= sc;
-      m_run = mn;
-    }
-    float P[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) P[j] = exp2_fast(S[j] - m_run);
+    const int ck_s = pl & 15;                 // channel-wise K: k-step of group gl
+    const int r8 = gl * kHeadDim + 8 * ck_s;  // channel-wise V: first (s, z) pair
 
-    // P'' into packed pairs: pk[a] = (token tk0 + a, token tk0 + a + D2)
-    uint32_t pk[2];
+    // ---- prologue: (s, z) loads -------------------------------------------
+    u4 vz[2] = {u4{0u, 0u, 0u, 0u}, u4{0u, 0u, 0u, 0u}};  // V (s, z): 2 runs of 4 tokens, or 8 pairs
+    u4 kz[2] = {u4{0u, 0u, 0u, 0u}, u4{0u, 0u, 0u, 0u}};  // K (s, z): 2 runs of 4 tokens, or 8 channels
     if (VAX == KVQ_TOKEN_WISE) {
-      const float2* cf = (const float2*)(lds + M::VA);
-      const float2 c0 = cf[(rel + tk0) / 2], c1 = cf[(rel + tk0 + C::D2) / 2];
-      pk[0] = pack_f16x2(P[0] * c0.x, P[1] * c1.x);
-      pk[1] = pack_f16x2(P[2] * c0.y, P[3] * c1.y);
-      lsum += (P[0] + P[1]) + (P[2] + P[3]);
-    } else {
-      pk[0] = pack_f16x2(P[0] * cw[0], P[1] * cw[0]);
-      pk[1] = pack_f16x2(P[2] * cw[1], P[3] * cw[1]);
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        if (tb_run[rr] < ntok) {
+          vz[rr] = *(const u4*)vsz_tok(cb + tb_run[rr]);
+          if (tb_run[rr] + 4 > ntok) {  // tokens past the end contribute (s, z) = (0, 0)
+#pragma unroll
+            for (int e = 1; e < 4; ++e)
+              if (tb_run[rr] + e >= ntok) vz[rr][e] = 0u;
+          }
+        }
+      }
+    } else if (glive) {
+      const u4* p = (const u4*)vsz_chan(cb + gl * kGroup, 8 * ck_s);
+      vz[0] = p[0];
+      vz[1] = p[1];
     }
-    u4 bp[2];
+    if (KAX == KVQ_TOKEN_WISE) {
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+        if (tb_run[rr] < ntok) kz[rr] = *(const u4*)ksz_tok(cb + tb_run[rr]);
+    } else if (glive) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) kz[hf] = *(const u4*)ksz_chan(cb + gl * kGroup, C::k_run(ck_s, hf));
+    }
+
+    // ---- prologue: fold operands into this wave's LDS slots -----------------
+    // the previous chunk's main loop of this wave has issued all its reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // V first: its (s, z) registers are free before the K part needs its own
+    if (VAX == KVQ_TOKEN_WISE) {
+      // every scale of this wave's tokens < 2^Fs (scales of 0 are replaced by
+      // 1, hence Fs >= 1; bit patterns of scales >= 0 order as values)
+      const uint32_t mb = wave_max_u(max_lo16(vz[0], vz[1]));
+      const int Fc = max((int)(mb >> 10) - 14, 1) + kThr - 14;
+      if (cb == tb) {
+        F = Fc;
+      } else if (Fc > F) {
+        const float sc = ldexpf(1.f, F - Fc);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) O[c] *= sc;
+        X *= sc;
+        F = Fc;
+      }
+      const float two_mF = ldexpf(1.f, -F);
+      // coef[t] = sigma * 2^-F / w(t); extra-tile rows hold w(t) * rho as hi + lo
+      // fp16 (sigma = s, or 1 where s == 0; rho = z / sigma). Runs start at a
+      // multiple of 4 tokens, so token e of a run has slot e % SLOTS.
+      float4* coef = (float4*)(lds + M::VA);
+      _Float16* rh = (_Float16*)(lds + M::VR);
+      float rw[2][4];
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        float cf[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float wt = (float)(1 << (BITS * (e % C::SLOTS)));
+          const float sv = f16lo(vz[rr][e]), zv = f16hi(vz[rr][e]);
+          const float sg = sv != 0.f ? sv : 1.f;
+          cf[e] = sg * (two_mF / wt);
+          rw[rr][e] = zv * (__builtin_amdgcn_rcpf(sg) * wt);
+        }
+        coef[tb_run[rr] / 4] = make_float4(cf[0], cf[1], cf[2], cf[3]);
+      }
+      // A-operand element 2 m + hf of this block is token run hf, slot m
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float a0 = rw[0][m], a1 = rw[1][m];
+        hi[m] = pack_f16x2(a0, a1);
+        lo[m] = pack_f16x2(a0 - f16lo(hi[m]), a1 - f16hi(hi[m]));
+      }
+      ((u4*)rh)[pblk] = u4{hi[0], hi[1], hi[2], hi[3]};
+      ((u4*)(rh + kChunkTokens))[pblk] = u4{lo[0], lo[1], lo[2], lo[3]};
+      if (cb == tb) ((u4*)(rh + 2 * kChunkTokens))[pblk] = u4{0u, 0u, 0u, 0u};  // the zero row
+    } else if (glive) {
+      float4* vg = (float4*)(lds + M::VA);  // (sigma, rho) of two pairs per float4
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t p0 = vz[e >> 2][e & 3], p1 = vz[e >> 2][(e + 1) & 3];
+        const float s0 = f16lo(p0), z0 = f16hi(p0), s1 = f16lo(p1), z1 = f16hi(p1);
+        vg[(r8 + e) / 2] = make_float4(s0 != 0.f ? s0 : 1.f, s0 != 0.f ? z0 * __builtin_amdgcn_rcpf(s0) : z0,
+                                       s1 != 0.f ? s1 : 1.f, s1 != 0.f ? z1 * __builtin_amdgcn_rcpf(s1) : z1);
+      }
+    }
+    if (KAX == KVQ_CHANNEL_WISE) {
+      // s' = s * 2^(14 - es) with every s of the group < 2^es (s' < 2^14), and
+      // the offset weight rho' = w * (z / s) * 2^(es - 14); a channel with
+      // s == 0 (all codes 0) takes s' = 2^13 and rho' = w * z * 2^-13, which
+      // gives the same offset. q'' = (q 2^-Eq / w) * s' is rounded once to
+      // binary16 (one packed multiply per two channels), and
+      // S = alpha 2^(10 + es + Eq) acc + alpha 2^Eq sum q'' rho' uses the
+      // rounded q'' in both terms, so rounding moves only the weight of x^.
+      const uint32_t mb = row_max_u(max_lo16(kz[0], kz[1]));
+      const int es = (int)(mb >> 10) - 14;
+      const float up = ldexpf(1.f, 14 - es), dn = ldexpf(1.f, es - 14);
+      uint32_t spk[4];
+      float rho[8];
+      {
+        float sp8[8];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const float sv = f16lo(kz[hf][m]), zv = f16hi(kz[hf][m]);
+            const bool nz = sv != 0.f;
+            sp8[4 * hf + m] = nz ? sv * up : 8192.f;
+            rho[4 * hf + m] = zv * (nz ? __builtin_amdgcn_rcpf(sv) * (C::w(m) * dn) : C::w(m) * (1.f / 8192.f));
+          }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) spk[m] = pack_f16x2(sp8[m], sp8[4 + m]);
+      }
+      u4* qB = (u4*)(lds + M::QB);
+      float2* kb = (float2*)(lds + M::KB);
+      const u4* qh = (const u4*)(lds + M::QS);
+#pragma unroll 1
+      for (int qh_i = 0; qh_i < 4; ++qh_i) {  // one head at a time keeps few registers live
+        const u4 qv = qh[qh_i * 16 + ck_s];
+        u4 wds;
+        float bias = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          wds[m] = mul_f16x2(qv[m], spk[m]);
+          bias = fmaf(f16lo(wds[m]), rho[m], fmaf(f16hi(wds[m]), rho[4 + m], bias));
+        }
+        if (glive) qB[(gl * 4 + qh_i) * 16 + ck_s] = wds;
+        bias = row_sum(bias);
+        if (glive && ck_s == 0) {
+          const int Eq = (int)redu[qh_i];
+          kb[gl * 4 + qh_i] = make_float2(alpha * ldexpf(1.f, 10 + es + Eq), alpha * ldexpf(bias, Eq));
+        }
+      }
+    } else {
+      float4* ktok = (float4*)(lds + M::KB);  // (s', z'') of two tokens per float4
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int t4 = tb_run[rr];  // 4 tokens
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+          const bool v0 = t4 + e < ntok, v1 = t4 + e + 1 < ntok;
+          const uint32_t p0 = kz[rr][e], p1 = kz[rr][e + 1];
+          ktok[(t4 + e) / 2] = make_float4(v0 ? f16lo(p0) * ktok_sc : 0.f, v0 ? f16hi(p0) * alpha : 0.f,
+                                           v1 ? f16lo(p1) * ktok_sc : 0.f, v1 ? f16hi(p1) * alpha : 0.f);
+        }
+      }
+    }
+    // LDS operations of one wave complete in order; the fence keeps the
+    // compiler from moving the main loop's reads above the writes
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+    // ---- per-lane constants of the main loop, rebuilt per chunk from a
+    // laundered lane id so that none of them is live through the prologue
+    int mlane = lane;
+    asm volatile("" : "+v"(mlane));
+    const int mn_ = mlane & 15, mg = mlane >> 4, mhh = mn_ & 3, mnq = mn_ >> 2;
+    const uint32_t koff = lane_koff(mg, mn_), voff = lane_voff(mg, mn_);
+    // compact scores: lane (n, g) holds tokens tk0 + {0, D2, 1, D2 + 1} (j = 0..3)
+    const int tk0 = C::tok(mnq, mg, 0);
+    // B operand of QK^T is block diagonal: column (head, q) is nonzero only in
+    // k-group q, so only lanes with g == q read q''; the others read zeros
+    const bool qlive = mg == mnq;
+    // PV B operand VGPR m of k-step k comes from lane src[k][m >> 1], register pk[m & 1]
+    int src[2][2];
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) bp[k][m] = (uint32_t)__builtin_amdgcn_ds_bpermute(src[k][m >> 1], (int)pk[m & 1]);
-
-    // PV: 8 channel tiles + the extra tile, 2 k-steps of 32 tokens
-    if (VAX == KVQ_TOKEN_WISE) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint32_t w = BITS == 4 ? cur.v[2 * k + (c >> 2)][c & 3] : cur.v[c >> 2][c & 3];
-          const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
-          O[c] = mfma(av, bp[k], O[c]);
-        }
-        const int pos = ((rel / C::TIT) * C::NK + k) * 32;  // wave-uniform part
-        X = mfma(*(const u4*)(rbase + rrow + pos), bp[k], X);
+      for (int m2 = 0; m2 < 2; ++m2) {
+        const int sq = BITS == 2 ? mg : 2 * k + (mg >> 1);
+        const int sg = BITS == 2 ? 2 * k + m2 : 2 * (mg & 1) + m2;
+        src[k][m2] = 4 * (mhh + 4 * sq + 16 * sg);  // byte address for ds_bpermute
       }
-    } else {
-      f4 G8[8];
-      f4 Xg = f4{0.f, 0.f, 0.f, 0.f};
+    const _Float16* rbase = (const _Float16*)(lds + M::VR);
+    // extra-tile rows: 0 = hi part, 1 = lo part, 2..15 = the zero row
+    const int rrow = (mn_ < 2 ? mn_ : 2) * kChunkTokens + 8 * mg;
+    float cw[2];  // channel-wise V: 2^-F / weight of the compact values' tokens
 #pragma unroll
-      for (int c = 0; c < 8; ++c) G8[c] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint32_t w = BITS == 4 ? cur.v[2 * k + (c >> 2)][c & 3] : cur.v[c >> 2][c & 3];
-          const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
-          G8[c] = mfma(av, bp[k], G8[c]);
-        }
-        u4 ones = u4{0u, 0u, 0u, 0u};
-        if (ri == 0) {
-#pragma unroll
-          for (int m = 0; m < 4; ++m) ones[m] = 0x00010001u << (BITS * (m % C::SLOTS));
-        }
-        Xg = mfma(ones, bp[k], Xg);
-      }
-      // fold this group's partial: O_d += sigma_d (G_d + rho_d * sum P)
-      const float psum = __shfl(Xg[0], n);  // row 0 lives in lane group 0
-      const float4* vg = (const float4*)(lds + M::VA) + (gi * kHeadDim + 32 * g) / 2;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int c = 0; c < 8; c += 2) {
-          // channels 32g + 8j + c and +1: (sigma, rho, sigma, rho)
-          float4 sr = vg[(8 * j + c) / 2];
-          O[c][j] = fmaf(sr.x, fmaf(sr.y, psum, G8[c][j]), O[c][j]);
-          O[c + 1][j] = fmaf(sr.z, fmaf(sr.w, psum, G8[c + 1][j]), O[c + 1][j]);
-        }
-      }
-      lsum += psum;
+    for (int aa = 0; aa < 2; ++aa) {
+      const int slot = (tk0 + aa) % C::TPW;
+      cw[aa] = ldexpf(1.f, -F) / (float)(1 << (BITS * (slot % C::SLOTS)));
     }
-    cur = nxt;
+    const float Qh = KAX == KVQ_TOKEN_WISE ? red[20 + mhh] : 0.f;
+
+    // ---- main loop over this wave's iterations of the chunk: the next
+    // iteration's codes are in flight while this one is computed
+    for (int jj = 0;; ++jj) {
+      const int it = 2 * (wv + 4 * (jj >> 1)) + (jj & 1);
+      const int t0 = cb + it * C::TIT;
+      if (t0 >= ce) break;
+      Codes nxt;
+      const int t1 = t0 + ((jj & 1) ? 7 : 1) * C::TIT;  // this wave's next iteration
+      if (t1 < te) load_codes(t1, nxt, koff, voff);
+      const int rel = t0 - cb;
+      const int gi = rel / kGroup;
+
+      // QK^T over 16 k-steps of 8 channels per k-group: 64 tokens x 4 heads
+      float S[4];
+      {
+        const u4* qb = (const u4*)(lds + (qlive ? M::QB + ((KAX == KVQ_CHANNEL_WISE ? gi : 0) * 4 + mhh) * 256
+                                                : M::QZ));
+        f4 c0 = f4{0.f, 0.f, 0.f, 0.f}, c1 = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+          const uint32_t w = BITS == 4 ? cur.k[s >> 2][s & 3] : cur.k[s >> 3][(s >> 1) & 3];
+          const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, s & 1);
+          if (s & 1) c1 = mfma(av, qb[s], c1);
+          else c0 = mfma(av, qb[s], c0);
+        }
+        const f4 acc = c0 + c1;
+        if (KAX == KVQ_CHANNEL_WISE) {
+          const float2 sb = ((const float2*)(lds + M::KB))[gi * 4 + mhh];  // scale, bias
+#pragma unroll
+          for (int j = 0; j < 4; ++j) S[j] = fmaf(acc[j], sb.x, sb.y);
+        } else {
+          const float4* kt = (const float4*)(lds + M::KB);  // (s', z'') per token, two per float4
+          const float4 p0 = kt[(rel + tk0) / 2], p1 = kt[(rel + tk0 + C::D2) / 2];
+          S[0] = fmaf(acc[0], p0.x, p0.y * Qh);  // token tk0
+          S[1] = fmaf(acc[1], p1.x, p1.y * Qh);  // tk0 + D2
+          S[2] = fmaf(acc[2], p0.z, p0.w * Qh);  // tk0 + 1
+          S[3] = fmaf(acc[3], p1.z, p1.w * Qh);  // tk0 + D2 + 1
+        }
+      }
+      if (t0 + C::TIT > te) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (t0 + tk0 + (j >> 1) + C::D2 * (j & 1) >= te) S[j] = -INFINITY;
+      }
+      const float mx = head_max(fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3])));
+      if (__any(mx > m_run + (float)kThr)) {
+        const float mn = fmaxf(m_run, mx);
+        const float sc = exp2_fast(m_run - mn);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) O[c] *= sc;
+        X *= sc;
+        lsum *= sc;
+        m_run = mn;
+      }
+      float P[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) P[j] = exp2_fast(S[j] - m_run);
+
+      // P'' into packed pairs: pk[a] = (token tk0 + a, token tk0 + a + D2)
+      uint32_t pk[2];
+      if (VAX == KVQ_TOKEN_WISE) {
+        const float2* cf = (const float2*)(lds + M::VA);
+        const float2 c0 = cf[(rel + tk0) / 2], c1 = cf[(rel + tk0 + C::D2) / 2];
+        pk[0] = pack_f16x2(P[0] * c0.x, P[1] * c1.x);
+        pk[1] = pack_f16x2(P[2] * c0.y, P[3] * c1.y);
+        lsum += (P[0] + P[1]) + (P[2] + P[3]);
+      } else {
+        pk[0] = pack_f16x2(P[0] * cw[0], P[1] * cw[0]);
+        pk[1] = pack_f16x2(P[2] * cw[1], P[3] * cw[1]);
+      }
+      u4 bp[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) bp[k][m] = (uint32_t)__builtin_amdgcn_ds_bpermute(src[k][m >> 1], (int)pk[m & 1]);
+
+      // PV: 8 channel tiles + the extra tile, 2 k-steps of 32 tokens
+      if (VAX == KVQ_TOKEN_WISE) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const uint32_t w = BITS == 4 ? cur.v[2 * k + (c >> 2)][c & 3] : cur.v[c >> 2][c & 3];
+            const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
+            O[c] = mfma(av, bp[k], O[c]);
+          }
+          const int pos = ((rel / C::TIT) * C::NK + k) * 32;  // wave-uniform part
+          X = mfma(*(const u4*)(rbase + rrow + pos), bp[k], X);
+        }
+      } else {
+        f4 G8[8];
+        f4 Xg = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) G8[c] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const uint32_t w = BITS == 4 ? cur.v[2 * k + (c >> 2)][c & 3] : cur.v[c >> 2][c & 3];
+            const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
+            G8[c] = mfma(av, bp[k], G8[c]);
+          }
+          u4 ones = u4{0u, 0u, 0u, 0u};
+          if (mn_ == 0) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) ones[m] = 0x00010001u << (BITS * (m % C::SLOTS));
+          }
+          Xg = mfma(ones, bp[k], Xg);
+        }
+        // fold this group's partial: O_d += sigma_d (G_d + rho_d * sum P)
+        const float psum = __shfl(Xg[0], mn_);  // row 0 lives in lane group 0
+        const float4* vg = (const float4*)(lds + M::VA) + (gi * kHeadDim + 32 * mg) / 2;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int c = 0; c < 8; c += 2) {
+            // channels 32g + 8j + c and +1: (sigma, rho, sigma, rho)
+            float4 sr = vg[(8 * j + c) / 2];
+            O[c][j] = fmaf(sr.x, fmaf(sr.y, psum, G8[c][j]), O[c][j]);
+            O[c + 1][j] = fmaf(sr.z, fmaf(sr.w, psum, G8[c + 1][j]), O[c + 1][j]);
+          }
+        }
+        lsum += psum;
+      }
+      cur = nxt;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   }
 
   // ---- per-wave result: numerator N and normaliser l (same scale) --------

@@ -14,7 +14,7 @@ constexpr int kGroup = 128;
 constexpr int kGqa = 4;            // query heads per KV head
 constexpr int kPage = 64;          // tokens per page
 constexpr int kSplitQuantum = 256; // split lengths are multiples of this
-constexpr int kMaxSplitTokens = 2048;
+constexpr int kChunkTokens = 2048;    // decode prologue chunk: fold operands in LDS
 
 // Launch arguments of the quantised decode (one layer).
 struct DecodeArgs {
@@ -30,7 +30,7 @@ struct DecodeArgs {
   int num_kv_heads;
   int max_len;             // sequence lengths are clamped to [0, max_len]
   int padded_len;          // contiguous Lp
-  int split_tokens;        // multiple of kSplitQuantum, <= kMaxSplitTokens
+  int split_tokens;        // multiple of kSplitQuantum
   int num_splits;
   float scale_log2;        // softmax_scale * log2(e)
   float* part_o;           // [B][Hq][num_splits][D]   (num_splits > 1)

@@ -70,15 +70,18 @@ def test_cache_sizes(L):
 def test_split_plan_and_workspace(L):
     f = kvq.make_format(2, "channel", "token", 8)
     ns = kvq.kvq_plan_splits(f, 128, 32768)
-    assert ns * 2048 >= 32768 and ns >= 16
-    assert kvq.kvq_workspace_size(f, 128, 32768) == 128 * 32 * ns * 130 * 4
-    assert kvq.kvq_plan_splits(kvq.make_format(4, num_kv_heads=1), 1, 1024) >= 1
-    # explicit splits: at least ceil(L / 2048), at most ceil(L / 256)
-    with pytest.raises(kvq.KvqError):
-        kvq.kvq_workspace_size(f, 2, 32768, 3)
+    assert 1 <= ns <= 128
+    assert kvq.kvq_workspace_size(f, 128, 32768) == (0 if ns == 1 else 128 * 32 * ns * 130 * 4)
+    # a single sequence is split finely enough to occupy the chip
+    assert kvq.kvq_plan_splits(kvq.make_format(4, num_kv_heads=1), 1, 32768) >= 64
+    assert kvq.kvq_plan_splits(kvq.make_format(4, num_kv_heads=1), 1, 1024) == 4
+    # explicit splits: any count from 1 to ceil(L / 256); one split needs no workspace
+    assert kvq.kvq_workspace_size(f, 2, 32768, 1) == 0
+    assert kvq.kvq_workspace_size(f, 2, 32768, 3) == 2 * 32 * 3 * 130 * 4
     with pytest.raises(kvq.KvqError):
         kvq.kvq_workspace_size(f, 2, 1024, 5)
-    assert kvq.kvq_workspace_size(f, 2, 2048, 1) == 0
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_workspace_size(f, 2, 1024, -1)
 
 
 def _call_decode(L, fmt, q=16, cache=(16, 16, 16, 16), lens=16, table=None, maxp=0, B=1,
