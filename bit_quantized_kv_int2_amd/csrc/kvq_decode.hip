@@ -210,26 +210,53 @@ struct Cfg {
   __device__ static inline float inv_wd(int d) { return 1.0f / (float)(1 << (BITS * (d % SLOTS))); }
 };
 
-// LDS layout (bytes), sized for the largest split.
+// LDS layout (bytes) for one chunk. LDS serves 128 bytes per clock in 32
+// four-byte banks; the q'' rows of the four heads are 288 bytes apart (16 k-steps
+// of 16 bytes plus 32 bytes of padding) and the block of zeros starts 16 bytes
+// into a 128-byte line, so the five distinct 16-byte addresses of one
+// B-operand read (four heads, zeros) fall in five different bank groups.
 template <int KAX, int VAX>
 struct Lds {
-  static constexpr int QS = 0;                                   // float [4][128]
-  static constexpr int QB = QS + 4 * 128 * 4;                    // u4 [groups][4 heads][16 k-steps]
-  static constexpr int QB_BYTES = (KAX == KVQ_CHANNEL_WISE ? kMaxGroups : 1) * 4 * 16 * 16;
-  static constexpr int QZ = QB + QB_BYTES;                       // 256 B of zeros (off-diagonal B)
-  static constexpr int KB = QZ + 256;                            // chan-K (scale, bias) [groups][4] / tok-K (s',z'') [tokens]
+  static constexpr int HEAD_STRIDE = 288;                       // bytes per head's 16 k-steps of q''
+  static constexpr int GROUP_STRIDE = 4 * HEAD_STRIDE;           // 9 x 128 bytes
+  static constexpr int QS = 0;                                   // float [4][128] / binary16 q
+  static constexpr int QB = QS + 4 * 128 * 4;                    // u4 [groups][4 heads][18] (16 used)
+  static constexpr int QB_BYTES = (KAX == KVQ_CHANNEL_WISE ? kMaxGroups : 1) * GROUP_STRIDE;
+  static constexpr int QZ = QB + QB_BYTES + 16;                  // 256 B of zeros (off-diagonal B)
+  static constexpr int KB = QZ + 256 + 112;                      // chan-K (scale, bias) [groups][4] / tok-K (s',z'') [tokens]
   static constexpr int KB_BYTES = KAX == KVQ_CHANNEL_WISE ? kMaxGroups * 4 * 8 : kChunkTokens * 8;
   static constexpr int VA = KB + KB_BYTES;                       // tok-V coef [tokens] / chan-V (sigma,rho) [groups][128]
-  static constexpr int VA_BYTES = VAX == KVQ_TOKEN_WISE ? kChunkTokens * 4 : kMaxGroups * 128 * 8;
-  static constexpr int VR = VA + VA_BYTES;                       // tok-V rho hi / lo / zero rows, fp16, A-operand order
-  static constexpr int VR_BYTES = VAX == KVQ_TOKEN_WISE ? 3 * kChunkTokens * 2 : 0;
+  static constexpr int VG_BLOCK = 32 * 8 + 16;                   // chan-V: 32 channels' (sigma, rho) + 16 B padding
+  static constexpr int VG_GROUP = 4 * VG_BLOCK;                  // chan-V: one 128-token group
+  static constexpr int VA_BYTES = VAX == KVQ_TOKEN_WISE ? kChunkTokens * 4 : kMaxGroups * VG_GROUP;
+  static constexpr int VR = VA + VA_BYTES;                       // tok-V rho hi, lo rows, fp16, A-operand order
+  static constexpr int VR_LO = kChunkTokens + 32;                // lo row offset in halfwords (64 B off the hi row's banks)
+  static constexpr int VR_BYTES = VAX == KVQ_TOKEN_WISE ? 2 * VR_LO * 2 : 0;
   static constexpr int RED = VR + VR_BYTES;                      // float [32] reductions
   static constexpr int TOTAL = RED + 32 * 4;
   // merge area reuses the front of LDS after the main loop
   static constexpr int MO = 0;                                   // float [4 waves][4 heads][128]
   static constexpr int ML = MO + 4 * 4 * 128 * 4;                // float [4 waves][4 heads][2]
   static_assert(ML + 4 * 4 * 2 * 4 <= RED, "merge area overlaps reductions");
+  static_assert(QB % 128 == 0 && GROUP_STRIDE % 128 == 0 && (QZ - QB) % 128 == 16, "bank layout");
+  static_assert(KB % 16 == 0 && VA % 16 == 0 && VR % 16 == 0, "alignment");
 };
+
+// Token-wise V: byte offset of the coefficient pair p (tokens 2p, 2p + 1).
+// Within every odd 128-byte block of 16 pairs the offset is XORed with 32 B
+// (INT2) or 16 B (INT4), a permutation inside the block, so that the 16
+// pairs one read instruction gathers (lanes of different token quarters,
+// spread over two adjacent blocks) land in distinct banks. Pairs 2i, 2i + 1
+// stay adjacent (a 16-byte write covers both).
+template <int BITS>
+__device__ inline int coef_off(int p) { return (8 * p) ^ ((BITS == 2 ? 32 : 16) * ((p >> 4) & 1)); }
+// Channel-wise V: byte offset of channel d's (sigma, rho) in group gi; each
+// 32-channel block is padded by 16 B so the four lane groups' reads (one
+// block each) fall in different banks.
+template <int KAX, int VAX>
+__device__ inline int vg_off(int gi, int d) {
+  return gi * Lds<KAX, VAX>::VG_GROUP + (d >> 5) * Lds<KAX, VAX>::VG_BLOCK + (d & 31) * 8;
+}
 
 // Work-groups per CU the register allocation targets (4 waves of 256 threads
 // per SIMD leave 128 VGPRs, 3 leave 168): INT2 with token-wise V fits in 128;
@@ -369,7 +396,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         float v1 = qs[qh * 128 + C::k_run(s, 1) + m] * two_mE * C::inv_w(m);
         wds[m] = pack_f16x2(v0, v1);
       }
-      ((u4*)(lds + M::QB))[qh * 16 + s] = u4{wds[0], wds[1], wds[2], wds[3]};
+      ((u4*)(lds + M::QB + qh * M::HEAD_STRIDE))[s] = u4{wds[0], wds[1], wds[2], wds[3]};
     }
     __syncthreads();
   }
@@ -421,8 +448,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         tb_run[1] = tb_run[0] + 4;
       }
     }
-    const int ck_s = pl & 15;                 // channel-wise K: k-step of group gl
-    const int r8 = gl * kHeadDim + 8 * ck_s;  // channel-wise V: first (s, z) pair
+    const int ck_s = pl & 15;  // channel-wise K: k-step of group gl; channel-wise V: channels 8 ck_s ..
 
     // ---- prologue: (s, z) loads -------------------------------------------
     u4 vz[2] = {u4{0u, 0u, 0u, 0u}, u4{0u, 0u, 0u, 0u}};  // V (s, z): 2 runs of 4 tokens, or 8 pairs
@@ -475,7 +501,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       // coef[t] = sigma * 2^-F / w(t); extra-tile rows hold w(t) * rho as hi + lo
       // fp16 (sigma = s, or 1 where s == 0; rho = z / sigma). Runs start at a
       // multiple of 4 tokens, so token e of a run has slot e % SLOTS.
-      float4* coef = (float4*)(lds + M::VA);
+      unsigned char* coef = lds + M::VA;
       _Float16* rh = (_Float16*)(lds + M::VR);
       float rw[2][4];
 #pragma unroll
@@ -489,7 +515,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
           cf[e] = sg * (two_mF / wt);
           rw[rr][e] = zv * (__builtin_amdgcn_rcpf(sg) * wt);
         }
-        coef[tb_run[rr] / 4] = make_float4(cf[0], cf[1], cf[2], cf[3]);
+        *(float4*)(coef + coef_off<BITS>(tb_run[rr] / 2)) = make_float4(cf[0], cf[1], cf[2], cf[3]);
       }
       // A-operand element 2 m + hf of this block is token run hf, slot m
       uint32_t hi[4], lo[4];
@@ -500,15 +526,14 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         lo[m] = pack_f16x2(a0 - f16lo(hi[m]), a1 - f16hi(hi[m]));
       }
       ((u4*)rh)[pblk] = u4{hi[0], hi[1], hi[2], hi[3]};
-      ((u4*)(rh + kChunkTokens))[pblk] = u4{lo[0], lo[1], lo[2], lo[3]};
-      if (cb == tb) ((u4*)(rh + 2 * kChunkTokens))[pblk] = u4{0u, 0u, 0u, 0u};  // the zero row
+      ((u4*)(rh + M::VR_LO))[pblk] = u4{lo[0], lo[1], lo[2], lo[3]};
     } else if (glive) {
-      float4* vg = (float4*)(lds + M::VA);  // (sigma, rho) of two pairs per float4
+      // (sigma, rho) of two channels per float4
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const uint32_t p0 = vz[e >> 2][e & 3], p1 = vz[e >> 2][(e + 1) & 3];
         const float s0 = f16lo(p0), z0 = f16hi(p0), s1 = f16lo(p1), z1 = f16hi(p1);
-        vg[(r8 + e) / 2] = make_float4(s0 != 0.f ? s0 : 1.f, s0 != 0.f ? z0 * __builtin_amdgcn_rcpf(s0) : z0,
+        *(float4*)(lds + M::VA + vg_off<KAX, VAX>(gl, 8 * ck_s + e)) = make_float4(s0 != 0.f ? s0 : 1.f, s0 != 0.f ? z0 * __builtin_amdgcn_rcpf(s0) : z0,
                                        s1 != 0.f ? s1 : 1.f, s1 != 0.f ? z1 * __builtin_amdgcn_rcpf(s1) : z1);
       }
     }
@@ -539,7 +564,6 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
 #pragma unroll
         for (int m = 0; m < 4; ++m) spk[m] = pack_f16x2(sp8[m], sp8[4 + m]);
       }
-      u4* qB = (u4*)(lds + M::QB);
       float2* kb = (float2*)(lds + M::KB);
       const u4* qh = (const u4*)(lds + M::QS);
 #pragma unroll 1
@@ -552,7 +576,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
           wds[m] = mul_f16x2(qv[m], spk[m]);
           bias = fmaf(f16lo(wds[m]), rho[m], fmaf(f16hi(wds[m]), rho[4 + m], bias));
         }
-        if (glive) qB[(gl * 4 + qh_i) * 16 + ck_s] = wds;
+        if (glive) ((u4*)(lds + M::QB + gl * M::GROUP_STRIDE + qh_i * M::HEAD_STRIDE))[ck_s] = wds;
         bias = row_sum(bias);
         if (glive && ck_s == 0) {
           const int Eq = (int)redu[qh_i];
@@ -599,8 +623,9 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         src[k][m2] = 4 * (mhh + 4 * sq + 16 * sg);  // byte address for ds_bpermute
       }
     const _Float16* rbase = (const _Float16*)(lds + M::VR);
-    // extra-tile rows: 0 = hi part, 1 = lo part, 2..15 = the zero row
-    const int rrow = (mn_ < 2 ? mn_ : 2) * kChunkTokens + 8 * mg;
+    // extra-tile rows: even = hi part, odd = lo part; only rows 0 and 1 of
+    // the accumulator are used, the others repeat them
+    const int rrow = (mn_ & 1) * M::VR_LO + 8 * mg;
     float cw[2];  // channel-wise V: 2^-F / weight of the compact values' tokens
 #pragma unroll
     for (int aa = 0; aa < 2; ++aa) {
@@ -624,7 +649,8 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       // QK^T over 16 k-steps of 8 channels per k-group: 64 tokens x 4 heads
       float S[4];
       {
-        const u4* qb = (const u4*)(lds + (qlive ? M::QB + ((KAX == KVQ_CHANNEL_WISE ? gi : 0) * 4 + mhh) * 256
+        const u4* qb = (const u4*)(lds + (qlive ? M::QB + (KAX == KVQ_CHANNEL_WISE ? gi : 0) * M::GROUP_STRIDE +
+                                                      mhh * M::HEAD_STRIDE
                                                 : M::QZ));
         f4 c0 = f4{0.f, 0.f, 0.f, 0.f}, c1 = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -670,8 +696,9 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       // P'' into packed pairs: pk[a] = (token tk0 + a, token tk0 + a + D2)
       uint32_t pk[2];
       if (VAX == KVQ_TOKEN_WISE) {
-        const float2* cf = (const float2*)(lds + M::VA);
-        const float2 c0 = cf[(rel + tk0) / 2], c1 = cf[(rel + tk0 + C::D2) / 2];
+        const unsigned char* cf = lds + M::VA;
+        const float2 c0 = *(const float2*)(cf + coef_off<BITS>((rel + tk0) / 2));
+        const float2 c1 = *(const float2*)(cf + coef_off<BITS>((rel + tk0 + C::D2) / 2));
         pk[0] = pack_f16x2(P[0] * c0.x, P[1] * c1.x);
         pk[1] = pack_f16x2(P[2] * c0.y, P[3] * c1.y);
         lsum += (P[0] + P[1]) + (P[2] + P[3]);
@@ -720,7 +747,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         }
         // fold this group's partial: O_d += sigma_d (G_d + rho_d * sum P)
         const float psum = __shfl(Xg[0], mn_);  // row 0 lives in lane group 0
-        const float4* vg = (const float4*)(lds + M::VA) + (gi * kHeadDim + 32 * mg) / 2;
+        const float4* vg = (const float4*)(lds + M::VA + vg_off<KAX, VAX>(gi, 32 * mg));
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
