@@ -80,7 +80,7 @@ kvq_status kvq_cache_sizes(const kvq_format* f, int32_t batch, int32_t max_len,
 // operands of one chunk sit in LDS), so a split may span the whole sequence;
 // the automatic plan splits only as far as needed for kTargetGroups
 // work-groups over the chip.
-static constexpr long kTargetGroups = 2048;
+static constexpr long kTargetGroups = 1024;
 
 static int plan_split_tokens(int batch, int num_kv_heads, int max_len, int num_splits) {
   if (max_len <= 0) return kSplitQuantum;
