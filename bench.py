@@ -198,6 +198,25 @@ def main():
         else:
             out4 = out.clone()
 
+    # ---- streaming-read reference over the same byte count (context) --------
+    stream_ref = {}
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    ref_buf = torch.ones(max(sum(kvq.kvq_cache_sizes(fmts[b], B, L)) for b in widths),
+                         dtype=torch.uint8, device=dev)
+    for bits in widths:
+        nbytes = sum(kvq.kvq_cache_sizes(fmts[bits], B, L))
+
+        def calls():
+            kvq.kvq_stream_read(ref_buf, sink, nbytes=nbytes)
+
+        per, total_ms = time_calls(calls, args.steps, args.warmup, stream)
+        us = total_ms * 1e3 / args.steps
+        stream_ref[bits] = dict(us=us, gbs=nbytes / (us * 1e-6) / 1e9,
+                                pct_peak=100.0 * nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS)
+        log(f"stream read of the INT{bits} cache byte count: {us:.1f} us, "
+            f"{stream_ref[bits]['gbs']:.0f} GB/s")
+    del ref_buf
+
     bf16 = None
     if need_bf16:
         fmt = fmts[2]
@@ -248,7 +267,9 @@ def main():
         unit_bytes = results[bits]["effective_bytes"] / (B * H)
         cpu_gbs = n_rows * H * unit_bytes / dt_cpu / 1e9
         used = min(threads, n_rows * H)
+        unit_b = results[bits]["effective_bytes"] / (B * H)
         cpu = {"value": cpu_gbs, "unit": "GB/s", "cores": used, "kind": "oracle",
+               "single_thread_value": unit_b / one / 1e9,
                "sample": f"INT{bits} headline rows {b0}..{b0 + n_rows - 1} ({n_rows * H} KV-head "
                          f"units x {L} tokens, fp64 dequantise + attention), {dt_cpu:.1f} s on "
                          f"{used} threads; value scaled to GB/s of effective cache bytes"}
@@ -284,15 +305,20 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(r["gbs"] / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(main_bits),
-                     "kernel": "decode_kernel + combine_kernel (one decode_attention_quant call; "
-                               "achieved = algorithmic bytes / event-timed call)",
+                     "kernel": ("decode_kernel" if r["num_splits"] == 1 else
+                                "decode_kernel + combine_kernel") +
+                               " (one decode_attention_quant call; achieved = algorithmic bytes / "
+                               "event-timed call)",
                      "algorithmic_bytes_per_launch": r["effective_bytes"]},
         "cpu_baseline": cpu,
         "parity_sample": parity or None,
         "int2": results.get(2),
         "int4": results.get(4),
         "bf16": bf16,
+        "stream_read_reference": {f"int{b}_bytes": v for b, v in stream_ref.items()},
     }
+    for b, v in stream_ref.items():
+        line[f"int{b}_vs_stream_read"] = round(v["us"] / results[b]["us_per_call"], 4)
     if bf16 is not None:
         for bits in results:
             line[f"speedup_int{bits}_vs_bf16"] = round(bf16["us_per_call"] / results[bits]["us_per_call"], 3)

@@ -85,8 +85,10 @@ def lib():
                                              ctypes.c_float, _P, _I, _I, _P, ctypes.c_size_t, _P]
         L.decode_attention_bf16.argtypes = [FP, _P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_float,
                                             _P, _I, _I, _P, ctypes.c_size_t, _P]
+        L.kvq_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
         for fn in ("kvq_check_format", "kvq_cache_sizes", "kvq_plan_splits", "kvq_workspace_size",
-                   "kv_quantize_pack", "decode_attention_quant", "decode_attention_bf16"):
+                   "kv_quantize_pack", "decode_attention_quant", "decode_attention_bf16",
+                   "kvq_stream_read"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -213,3 +215,10 @@ def decode_attention_bf16(fmt: Format, q, k, v, seq_lens, max_len, softmax_scale
                                        _ptr(workspace), workspace.numel(), _stream(stream)),
            "decode_attention_bf16")
     return out
+
+
+def kvq_stream_read(buf, sink, nbytes=None, stream=None):
+    """Measurement reference: read nbytes of a device tensor once (128-bit loads)."""
+    _require_gpu(buf, sink)
+    n = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    _check(lib().kvq_stream_read(_ptr(buf), n, _ptr(sink), _stream(stream)), "kvq_stream_read")

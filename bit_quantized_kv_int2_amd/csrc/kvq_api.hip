@@ -313,4 +313,12 @@ kvq_status decode_attention_bf16(const kvq_format* f, const void* q, const void*
                                    a.out_bf16, s));
 }
 
+kvq_status kvq_stream_read(const void* data, size_t bytes, uint32_t* sink, void* stream) {
+  if (!data || !sink) return KVQ_ERR_NULL_POINTER;
+  if (!aligned16(data) || ((uintptr_t)sink & 3u)) return KVQ_ERR_MISALIGNED;
+  if (bytes % 16 != 0) return KVQ_ERR_BAD_SHAPE;
+  if (bytes == 0) return KVQ_OK;
+  return hip_status(launch_stream_read(data, bytes, sink, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -86,4 +86,7 @@ hipError_t launch_decode_bf16(const Bf16Args& a, hipStream_t s);
 hipError_t launch_combine(const float* part_o, const float* part_ml, int rows, int num_splits,
                           void* out, int out_bf16, hipStream_t s);
 
+// Reads bytes (a multiple of 16) once; the HBM read reference for measurement.
+hipError_t launch_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t s);
+
 }  // namespace kvq

@@ -164,6 +164,21 @@ kvq_status decode_attention_bf16(const kvq_format* fmt, const void* q, const voi
                                  int32_t out_dtype, int32_t num_splits, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/*
+ * kvq_stream_read -- measurement reference, not part of the method: reads
+ * `bytes` of device memory once with 128-bit loads (grid-stride over 256 CUs)
+ * and nothing else, giving the practical HBM read rate that the decode
+ * kernels' effective rates are compared with (the pages compare against the
+ * chip's peak bandwidth: grafy.ai "What did benchmarks show"; rag-lover.com
+ * TL;DR).
+ *   data   device pointer, 16-byte aligned; bytes a multiple of 16.
+ *   sink   device uint32; written only if the XOR of all words read equals
+ *          0x9E3779B9 (it exists so the loads cannot be elided).
+ * Returns KVQ_ERR_NULL_POINTER / KVQ_ERR_MISALIGNED / KVQ_ERR_BAD_SHAPE on bad
+ * arguments (nothing launched), KVQ_ERR_HIP on a failed launch.
+ */
+kvq_status kvq_stream_read(const void* data, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,18 @@ def test_exports_every_declared_function(L):
         assert hasattr(L, n), n
 
 
+def test_stream_read_validation_without_gpu(L):
+    f = L.kvq_stream_read
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    A = 4096
+    assert f(None, 16, A, None) == NULLP
+    assert f(A, 16, None, None) == NULLP
+    assert f(A + 8, 16, A, None) == MISALIGNED
+    assert f(A, 16, A + 2, None) == MISALIGNED
+    assert f(A, 24, A, None) == BADSHAPE
+    assert f(A, 0, A, None) == OK  # nothing to read, nothing launched
+
+
 def test_layout_version_and_status_strings(L):
     assert L.kvq_layout_version() == kvq.LAYOUT_VERSION
     for s in range(7):
