@@ -47,6 +47,7 @@ def parse():
                    help="target CPU time of the oracle baseline sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     p.add_argument("--no-bf16", action="store_true")
+    p.add_argument("--no-append", action="store_true", help="skip the append / window timings")
     p.add_argument("--only", choices=["int2", "int4"], default=None,
                    help="time one bit width only (profiling runs)")
     return p.parse_args()
@@ -279,6 +280,49 @@ def main():
                   "rows": [b0, b0 + n_rows], "bits": bits}
         log(f"oracle: {cpu_gbs:.4f} GB/s on {used} threads ({dt_cpu:.1f} s); sampled parity {parity}")
 
+    # ---- decode-time append and the residual-window decode (after the parity
+    # sample: a flush rewrites the last group of the cache) ---------------------
+    append = None
+    if not args.no_append:
+        bits = widths[0]
+        fmt = fmts[bits]
+        kwin = torch.zeros((B, H, 128, D), dtype=torch.bfloat16, device=dev)
+        vwin = torch.zeros_like(kwin)
+        gen = torch.Generator(device=dev).manual_seed(7)
+        k_new = torch.randn((B, H, D), generator=gen, device=dev).to(torch.bfloat16)
+        v_new = torch.randn((B, H, D), generator=gen, device=dev).to(torch.bfloat16)
+        cache = caches[bits]
+        pos_mid = torch.full((B,), L - 64, dtype=torch.int32, device=dev)   # slot 64: no flush
+        pos_end = torch.full((B,), L - 1, dtype=torch.int32, device=dev)    # slot 127: flush a group
+
+        def app_mid():
+            kvq.kv_append(fmt, k_new, v_new, pos_mid, cache, kwin, vwin, L)
+
+        def app_end():
+            kvq.kv_append(fmt, k_new, v_new, pos_end, cache, kwin, vwin, L)
+
+        _, t_mid = time_calls(app_mid, args.steps, 10, stream)
+        _, t_end = time_calls(app_end, args.steps, 10, stream)
+        wlen = torch.full((B,), L - 64, dtype=torch.int32, device=dev)  # 64 tokens in the window
+        wws = torch.zeros(kvq.kvq_window_workspace_size(fmt, B, L), dtype=torch.uint8, device=dev)
+        outw = torch.empty_like(out)
+
+        def dec_win():
+            kvq.decode_attention_quant_window(fmt, q, cache, kwin, vwin, wlen, L, scale, outw,
+                                              workspace=wws)
+
+        _, t_win = time_calls(dec_win, args.steps, args.warmup, stream)
+        append = {"bits": bits,
+                  "append_us": round(t_mid * 1e3 / args.steps, 2),
+                  "append_with_flush_us": round(t_end * 1e3 / args.steps, 2),
+                  "window_decode_us": round(t_win * 1e3 / args.steps, 2),
+                  "window_tokens": 64,
+                  "note": "one bf16 token per (sequence, KV head) per append; the flush quantises "
+                          "and packs a whole 128-token group per (sequence, KV head); the window "
+                          "decode reads L - 64 tokens from the packed cache and 64 from the window"}
+        log(f"append: {append['append_us']} us, with group flush {append['append_with_flush_us']} "
+            f"us; window decode {append['window_decode_us']} us")
+
     main_bits = 2 if 2 in results else widths[0]
     r = results[main_bits]
     line = {
@@ -316,6 +360,7 @@ def main():
         "int4": results.get(4),
         "bf16": bf16,
         "stream_read_reference": {f"int{b}_bytes": v for b, v in stream_ref.items()},
+        "append": append,
     }
     for b, v in stream_ref.items():
         line[f"int{b}_vs_stream_read"] = round(v["us"] / results[b]["us_per_call"], 4)

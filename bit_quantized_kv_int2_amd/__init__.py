@@ -86,9 +86,15 @@ def lib():
         L.decode_attention_bf16.argtypes = [FP, _P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_float,
                                             _P, _I, _I, _P, ctypes.c_size_t, _P]
         L.kvq_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
+        L.kv_append.argtypes = [FP, _P, _P, _P, _P, _I, _I, _I, ctypes.POINTER(Cache), _P, _P, _P]
+        L.kvq_window_workspace_size.argtypes = [FP, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]
+        L.decode_attention_quant_window.argtypes = [FP, _P, ctypes.POINTER(Cache), _P, _P, _P, _P,
+                                                    _I, _I, _I, ctypes.c_float, _P, _I, _I, _P,
+                                                    ctypes.c_size_t, _P]
         for fn in ("kvq_check_format", "kvq_cache_sizes", "kvq_plan_splits", "kvq_workspace_size",
                    "kv_quantize_pack", "decode_attention_quant", "decode_attention_bf16",
-                   "kvq_stream_read"):
+                   "kvq_stream_read", "kv_append", "kvq_window_workspace_size",
+                   "decode_attention_quant_window"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -214,6 +220,54 @@ def decode_attention_bf16(fmt: Format, q, k, v, seq_lens, max_len, softmax_scale
                                        float(softmax_scale), _ptr(out), od, num_splits,
                                        _ptr(workspace), workspace.numel(), _stream(stream)),
            "decode_attention_bf16")
+    return out
+
+
+def kvq_window_workspace_size(fmt: Format, batch: int, max_len: int, num_splits: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().kvq_window_workspace_size(ctypes.byref(fmt), batch, max_len, num_splits,
+                                           ctypes.byref(n)), "kvq_window_workspace_size")
+    return int(n.value)
+
+
+def window_tensors(fmt: Format, batch: int, device="cuda"):
+    """Zero-filled bf16 residual windows (K, V) [batch][Hkv][128][D] for kv_append."""
+    import torch
+    shape = (batch, fmt.num_kv_heads, 128, fmt.head_dim)
+    return (torch.zeros(shape, dtype=torch.bfloat16, device=device),
+            torch.zeros(shape, dtype=torch.bfloat16, device=device))
+
+
+def kv_append(fmt: Format, k_new, v_new, seq_lens, cache, k_window, v_window, max_len,
+              page_table=None, stream=None):
+    """Append one token per sequence (bf16 [B][Hkv][D]) at index seq_lens[b]."""
+    _require_gpu(k_new, v_new, seq_lens, k_window, v_window, page_table)
+    B = k_new.shape[0]
+    maxp = 0 if page_table is None else page_table.shape[1]
+    cs = _cache_struct(cache)
+    _check(lib().kv_append(ctypes.byref(fmt), _ptr(k_new), _ptr(v_new), _ptr(seq_lens),
+                           _ptr(page_table), maxp, B, max_len, ctypes.byref(cs), _ptr(k_window),
+                           _ptr(v_window), _stream(stream)), "kv_append")
+
+
+def decode_attention_quant_window(fmt: Format, q, cache, k_window, v_window, seq_lens, max_len,
+                                  softmax_scale, out, page_table=None, num_splits=0,
+                                  workspace=None, stream=None):
+    """Decode over whole groups in the packed cache plus the bf16 residual window."""
+    import torch
+    _require_gpu(q, seq_lens, out, k_window, v_window, page_table)
+    B = q.shape[0]
+    if workspace is None:
+        ws = kvq_window_workspace_size(fmt, B, max_len, num_splits)
+        workspace = torch.zeros(max(ws, 16), dtype=torch.uint8, device=q.device)
+    maxp = 0 if page_table is None else page_table.shape[1]
+    od = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
+    cs = _cache_struct(cache)
+    _check(lib().decode_attention_quant_window(
+        ctypes.byref(fmt), _ptr(q), ctypes.byref(cs), _ptr(k_window), _ptr(v_window),
+        _ptr(seq_lens), _ptr(page_table), maxp, B, max_len, float(softmax_scale), _ptr(out), od,
+        num_splits, _ptr(workspace), workspace.numel(), _stream(stream)),
+        "decode_attention_quant_window")
     return out
 
 

@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvq.so")
-SOURCES = ["kvq_api.hip", "kvq_pack.hip", "kvq_decode.hip", "kvq_bf16.hip", "kvq_stream.hip"]
+SOURCES = ["kvq_api.hip", "kvq_pack.hip", "kvq_decode.hip", "kvq_bf16.hip", "kvq_stream.hip",
+           "kvq_append.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fno-fast-math",

@@ -248,6 +248,8 @@ kvq_status decode_attention_quant(const kvq_format* f, const void* q, const kvq_
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.out = out;
   a.out_bf16 = out_dtype == KVQ_OUT_BF16;
+  a.direct_out = nsplit == 1;
+  a.part_stride = nsplit;
   if (nsplit > 1) {
     const size_t rows = (size_t)batch * f->num_q_heads;
     a.part_o = (float*)workspace;
@@ -301,6 +303,8 @@ kvq_status decode_attention_bf16(const kvq_format* f, const void* q, const void*
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.out = out;
   a.out_bf16 = out_dtype == KVQ_OUT_BF16;
+  a.direct_out = nsplit == 1;
+  a.part_stride = nsplit;
   if (nsplit > 1) {
     const size_t rows = (size_t)batch * f->num_q_heads;
     a.part_o = (float*)workspace;
@@ -311,6 +315,141 @@ kvq_status decode_attention_bf16(const kvq_format* f, const void* q, const void*
   if (st != KVQ_OK || nsplit == 1) return st;
   return hip_status(launch_combine(a.part_o, a.part_ml, batch * f->num_q_heads, nsplit, out,
                                    a.out_bf16, s));
+}
+
+kvq_status kv_append(const kvq_format* f, const void* k_new, const void* v_new,
+                     const int32_t* seq_lens, const int32_t* page_table, int32_t max_pages_per_seq,
+                     int32_t batch, int32_t max_len, const kvq_cache* cache, void* k_window,
+                     void* v_window, void* stream) {
+  kvq_status st = kvq_check_format(f);
+  if (st != KVQ_OK) return st;
+  if (!k_new || !v_new || !k_window || !v_window) return KVQ_ERR_NULL_POINTER;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_window) || !aligned16(v_window))
+    return KVQ_ERR_MISALIGNED;
+  st = check_cache_ptrs(cache);
+  if (st != KVQ_OK) return st;
+  st = check_common(f, seq_lens, page_table, max_pages_per_seq, batch, max_len);
+  if (st != KVQ_OK) return st;
+  if (batch == 0 || max_len == 0) return KVQ_OK;
+  AppendArgs a;
+  memset(&a, 0, sizeof a);
+  a.k_new = (const uint16_t*)k_new;
+  a.v_new = (const uint16_t*)v_new;
+  a.seq_lens = seq_lens;
+  a.page_table = f->page_size ? page_table : nullptr;
+  a.max_pages = max_pages_per_seq;
+  a.batch = batch;
+  a.max_len = max_len;
+  a.num_kv_heads = f->num_kv_heads;
+  a.bits = f->bits;
+  a.k_axis = f->k_axis;
+  a.v_axis = f->v_axis;
+  a.paged = f->page_size != 0;
+  a.padded_len = padded_len(max_len);
+  a.k_win = (uint16_t*)k_window;
+  a.v_win = (uint16_t*)v_window;
+  a.k_codes = (uint8_t*)cache->k_codes;
+  a.v_words = (uint32_t*)cache->v_codes;
+  a.k_sz = (uint16_t*)cache->k_scale_offset;
+  a.v_sz = (uint16_t*)cache->v_scale_offset;
+  return hip_status(launch_append(a, (hipStream_t)stream));
+}
+
+static size_t window_workspace_bytes(const kvq_format* f, int batch, int nsplit) {
+  return (size_t)batch * f->num_q_heads * (nsplit + 1) * (kHeadDim + 2) * sizeof(float);
+}
+
+kvq_status kvq_window_workspace_size(const kvq_format* f, int32_t batch, int32_t max_len,
+                                     int32_t num_splits, size_t* bytes) {
+  kvq_status st = kvq_check_format(f);
+  if (st != KVQ_OK) return st;
+  if (!bytes) return KVQ_ERR_NULL_POINTER;
+  if (batch < 0 || max_len < 0) return KVQ_ERR_BAD_SHAPE;
+  int split_tokens, nsplit;
+  st = resolve_splits(f, batch, max_len, num_splits, &split_tokens, &nsplit);
+  if (st != KVQ_OK) return st;
+  *bytes = window_workspace_bytes(f, batch, nsplit);
+  return KVQ_OK;
+}
+
+kvq_status decode_attention_quant_window(const kvq_format* f, const void* q,
+                                         const kvq_cache* cache, const void* k_window,
+                                         const void* v_window, const int32_t* seq_lens,
+                                         const int32_t* page_table, int32_t max_pages_per_seq,
+                                         int32_t batch, int32_t max_len, float softmax_scale,
+                                         void* out, int32_t out_dtype, int32_t num_splits,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  kvq_status st = kvq_check_format(f);
+  if (st != KVQ_OK) return st;
+  st = check_out(q, out, out_dtype);
+  if (st != KVQ_OK) return st;
+  st = check_cache_ptrs(cache);
+  if (st != KVQ_OK) return st;
+  if (!k_window || !v_window) return KVQ_ERR_NULL_POINTER;
+  if (!aligned16(k_window) || !aligned16(v_window)) return KVQ_ERR_MISALIGNED;
+  st = check_common(f, seq_lens, page_table, max_pages_per_seq, batch, max_len);
+  if (st != KVQ_OK) return st;
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVQ_ERR_BAD_SHAPE;
+  int split_tokens, nsplit;
+  st = resolve_splits(f, batch, max_len, num_splits, &split_tokens, &nsplit);
+  if (st != KVQ_OK) return st;
+  const size_t need = window_workspace_bytes(f, batch, nsplit);
+  if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KVQ_ERR_MISALIGNED;
+  if (batch == 0) return KVQ_OK;
+  const size_t rows = (size_t)batch * f->num_q_heads;
+  const int slots = nsplit + 1;  // the quantised splits, then the window
+  float* part_o = (float*)workspace;
+  float* part_ml = part_o + rows * slots * kHeadDim;
+  const float scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipStream_t s = (hipStream_t)stream;
+
+  DecodeArgs a;
+  memset(&a, 0, sizeof a);
+  a.q = (const uint16_t*)q;
+  a.k_codes = (const uint8_t*)cache->k_codes;
+  a.v_words = (const uint32_t*)cache->v_codes;
+  a.k_sz = (const uint16_t*)cache->k_scale_offset;
+  a.v_sz = (const uint16_t*)cache->v_scale_offset;
+  a.seq_lens = seq_lens;
+  a.page_table = f->page_size ? page_table : nullptr;
+  a.max_pages = max_pages_per_seq;
+  a.batch = batch;
+  a.num_kv_heads = f->num_kv_heads;
+  a.max_len = max_len;
+  a.padded_len = padded_len(max_len);
+  a.split_tokens = split_tokens;
+  a.num_splits = nsplit;
+  a.scale_log2 = scale_log2;
+  a.part_o = part_o;
+  a.part_ml = part_ml;
+  a.part_stride = slots;
+  a.len_mode = 1;  // whole groups from the cache
+  st = hip_status(launch_decode_quant(*f, a, s));
+  if (st != KVQ_OK) return st;
+
+  Bf16Args w;
+  memset(&w, 0, sizeof w);
+  w.q = (const uint16_t*)q;
+  w.k = (const uint16_t*)k_window;
+  w.v = (const uint16_t*)v_window;
+  w.seq_lens = seq_lens;
+  w.batch = batch;
+  w.num_kv_heads = f->num_kv_heads;
+  w.max_len = kGroup;  // window rows per (sequence, KV head)
+  w.page_size = 0;
+  w.split_tokens = kGroup;
+  w.num_splits = 1;
+  w.scale_log2 = scale_log2;
+  w.part_o = part_o;
+  w.part_ml = part_ml;
+  w.part_stride = slots;
+  w.part_base = nsplit;
+  w.len_mode = 2;  // the tokens past the last whole group
+  st = hip_status(launch_decode_bf16(w, s));
+  if (st != KVQ_OK) return st;
+  return hip_status(launch_combine(part_o, part_ml, (int)rows, slots, out,
+                                   out_dtype == KVQ_OUT_BF16, s));
 }
 
 kvq_status kvq_stream_read(const void* data, size_t bytes, uint32_t* sink, void* stream) {

@@ -47,21 +47,24 @@ __global__ void __launch_bounds__(kThreads) bf16_kernel(Bf16Args a) {
   const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.num_kv_heads, Hq = H * kGqa;
-  const int L = min(max(a.seq_lens[b], 0), a.max_len);  // contract: 0 <= len <= max_len
+  int L = max(a.seq_lens[b], 0);
+  if (a.len_mode == 2) L %= kGroup;  // the residual window holds the tokens past the last whole group
+  L = min(L, a.max_len);  // contract: 0 <= len <= max_len
   const int tb = sp * a.split_tokens;
   const int te = min(tb + a.split_tokens, L);
   const long row0 = (long)b * Hq + (long)h * kGqa;
   if (te <= tb) {
     for (int e = tid; e < kGqa * kHeadDim; e += kThreads) {
       int hh = e / kHeadDim, d = e % kHeadDim;
-      if (a.num_splits == 1) {
+      if (a.direct_out) {
         if (a.out_bf16) ((uint16_t*)a.out)[(row0 + hh) * kHeadDim + d] = 0;
         else ((float*)a.out)[(row0 + hh) * kHeadDim + d] = 0.f;
       } else {
-        a.part_o[((row0 + hh) * a.num_splits + sp) * kHeadDim + d] = 0.f;
+        const long pr = (row0 + hh) * a.part_stride + a.part_base + sp;
+        a.part_o[pr * kHeadDim + d] = 0.f;
         if (d == 0) {
-          a.part_ml[((row0 + hh) * a.num_splits + sp) * 2] = -INFINITY;
-          a.part_ml[((row0 + hh) * a.num_splits + sp) * 2 + 1] = 0.f;
+          a.part_ml[pr * 2] = -INFINITY;
+          a.part_ml[pr * 2 + 1] = 0.f;
         }
       }
     }
@@ -204,11 +207,11 @@ __global__ void __launch_bounds__(kThreads) bf16_kernel(Bf16Args a) {
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const float o0 = n0 * inv, o1 = n1 * inv;
   const long row = row0 + qh;
-  if (a.num_splits == 1) {
+  if (a.direct_out) {
     if (a.out_bf16) *(uint32_t*)((uint16_t*)a.out + row * kHeadDim + d) = pack_bf16x2(o0, o1);
     else *(float2*)((float*)a.out + row * kHeadDim + d) = make_float2(o0, o1);
   } else {
-    const long pr = row * a.num_splits + sp;
+    const long pr = row * a.part_stride + a.part_base + sp;
     *(float2*)(a.part_o + pr * kHeadDim + d) = make_float2(o0, o1);
     if (d == 0) {
       a.part_ml[pr * 2] = ml[qh * 2];

@@ -280,7 +280,8 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps addressing scalar
   const int H = a.num_kv_heads, Hq = H * kGqa;
-  const int L = min(max(a.seq_lens[b], 0), a.max_len);  // contract: 0 <= len <= max_len
+  int L = min(max(a.seq_lens[b], 0), a.max_len);  // contract: 0 <= len <= max_len
+  if (a.len_mode == 1) L -= L % kGroup;  // whole groups only (the rest is a residual window)
   const int tb = sp * a.split_tokens;
   const int te = min(tb + a.split_tokens, L);
   const long row0 = (long)b * Hq + (long)h * kGqa;  // first query head row of this KV head
@@ -288,14 +289,15 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   if (te <= tb) {  // nothing in this split (or an empty sequence)
     for (int e = tid; e < kGqa * kHeadDim; e += kThreads) {
       int hh = e / kHeadDim, d = e % kHeadDim;
-      if (a.num_splits == 1) {
+      if (a.direct_out) {
         if (a.out_bf16) ((uint16_t*)a.out)[(row0 + hh) * kHeadDim + d] = 0;
         else ((float*)a.out)[(row0 + hh) * kHeadDim + d] = 0.f;
       } else {
-        a.part_o[((row0 + hh) * a.num_splits + sp) * kHeadDim + d] = 0.f;
+        const long pr = (row0 + hh) * a.part_stride + a.part_base + sp;
+        a.part_o[pr * kHeadDim + d] = 0.f;
         if (d == 0) {
-          a.part_ml[((row0 + hh) * a.num_splits + sp) * 2] = -INFINITY;
-          a.part_ml[((row0 + hh) * a.num_splits + sp) * 2 + 1] = 0.f;
+          a.part_ml[pr * 2] = -INFINITY;
+          a.part_ml[pr * 2 + 1] = 0.f;
         }
       }
     }
@@ -818,7 +820,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float o0 = n0 * inv, o1 = n1 * inv;
     const long row = row0 + qh;
-    if (a.num_splits == 1) {
+    if (a.direct_out) {
       if (a.out_bf16) {
         __bf16 b0 = (__bf16)o0, b1 = (__bf16)o1;
         uint32_t pk = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
@@ -828,7 +830,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         *(float2*)((float*)a.out + row * kHeadDim + d) = make_float2(o0, o1);
       }
     } else {
-      const long pr = row * a.num_splits + sp;
+      const long pr = row * a.part_stride + a.part_base + sp;
       *(float2*)(a.part_o + pr * kHeadDim + d) = make_float2(o0, o1);
       if (d == 0) {
         // m in log2 units, l in units of 2^(S - m)

@@ -16,6 +16,29 @@ constexpr int kPage = 64;          // tokens per page
 constexpr int kSplitQuantum = 256; // split lengths are multiples of this
 constexpr int kChunkTokens = 2048;    // decode prologue chunk: fold operands in LDS
 
+// Launch arguments of the append (one new token per sequence, one layer).
+struct AppendArgs {
+  const uint16_t* k_new;   // bf16 [B][Hkv][D]
+  const uint16_t* v_new;
+  const int32_t* seq_lens; // tokens before the append
+  const int32_t* page_table;
+  int max_pages;
+  int batch;
+  int max_len;
+  int num_kv_heads;
+  int bits;
+  int k_axis;
+  int v_axis;
+  int paged;
+  int padded_len;
+  uint16_t* k_win;         // bf16 [B][Hkv][128][D]
+  uint16_t* v_win;
+  uint8_t* k_codes;
+  uint32_t* v_words;
+  uint16_t* k_sz;
+  uint16_t* v_sz;
+};
+
 // Launch arguments of the quantised decode (one layer).
 struct DecodeArgs {
   const uint16_t* q;       // bf16 [B][Hq][D]
@@ -33,10 +56,14 @@ struct DecodeArgs {
   int split_tokens;        // multiple of kSplitQuantum
   int num_splits;
   float scale_log2;        // softmax_scale * log2(e)
-  float* part_o;           // [B][Hq][num_splits][D]   (num_splits > 1)
-  float* part_ml;          // [B][Hq][num_splits][2]
-  void* out;               // final output when num_splits == 1
+  float* part_o;           // [B][Hq][part_stride][D]   (partials)
+  float* part_ml;          // [B][Hq][part_stride][2]
+  void* out;               // final output when direct_out
   int out_bf16;
+  int direct_out;          // 1: one split, write out; 0: write partial slot part_base + split
+  int part_stride;         // partial slots per (sequence, query head)
+  int part_base;
+  int len_mode;            // 0: L = seq_lens[b]; 1: L rounded down to whole 128-token groups
 };
 
 struct Bf16Args {
@@ -57,6 +84,10 @@ struct Bf16Args {
   float* part_ml;
   void* out;
   int out_bf16;
+  int direct_out;          // as DecodeArgs
+  int part_stride;
+  int part_base;
+  int len_mode;            // 0: L = seq_lens[b]; 2: L mod 128 (the tokens of a residual window)
 };
 
 struct PackArgs {
@@ -86,6 +117,7 @@ hipError_t launch_decode_bf16(const Bf16Args& a, hipStream_t s);
 hipError_t launch_combine(const float* part_o, const float* part_ml, int rows, int num_splits,
                           void* out, int out_bf16, hipStream_t s);
 
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 // Reads bytes (a multiple of 16) once; the HBM read reference for measurement.
 hipError_t launch_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t s);
 

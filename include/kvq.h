@@ -165,6 +165,55 @@ kvq_status decode_attention_bf16(const kvq_format* fmt, const void* q, const voi
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * kv_append -- decode-time quantise-on-write of one new token per sequence.
+ * A serving engine fills the cache as tokens are generated (grafy.ai "How can
+ * developers integrate FOSCAR into their LLM serving stacks?"); a channel-wise
+ * group needs all of its 128 tokens before its (s, z) exist (rag-lover.com
+ * "conditions of use": each group shares one s and z), so the tokens past the
+ * last whole group stay in a bf16 residual window and a group is quantised
+ * when its last token arrives. The pages do not describe this step; the
+ * residual window is this library's reading.
+ *   k_new, v_new  device bf16 [batch][Hkv][D]: the new token of every sequence.
+ *   seq_lens      device int32 [batch]: tokens BEFORE this append; the new token
+ *                 gets index seq_lens[b] (the caller then increments it).
+ *                 Sequences with seq_lens[b] >= max_len are left untouched.
+ *   k_window, v_window  device bf16 [batch][Hkv][128][D]: token t of a sequence
+ *                 lives in row t % 128 while t >= 128 * floor(len / 128).
+ *   cache         packed cache (fmt's layout, contiguous or paged): when index
+ *                 seq_lens[b] completes a 128-token group, that group's codes and
+ *                 (s, z) are written, bit-identical to kv_quantize_pack applied to
+ *                 the window's bf16 values; nothing else in the cache changes.
+ * Whole groups of a prompt may be written with kv_quantize_pack (lengths rounded
+ * down to a multiple of 128) and its remaining tokens appended one by one.
+ */
+kvq_status kv_append(const kvq_format* fmt, const void* k_new, const void* v_new,
+                     const int32_t* seq_lens, const int32_t* page_table,
+                     int32_t max_pages_per_seq, int32_t batch, int32_t max_len,
+                     const kvq_cache* cache, void* k_window, void* v_window, void* stream);
+
+/* Workspace bytes decode_attention_quant_window needs (its quantised splits
+ * plus one slot for the window). */
+kvq_status kvq_window_workspace_size(const kvq_format* fmt, int32_t batch, int32_t max_len,
+                                     int32_t num_splits, size_t* bytes);
+
+/*
+ * decode_attention_quant_window -- decode over a cache filled by kv_append:
+ * tokens [0, L - L % 128) from the packed cache with the affine folds (as
+ * decode_attention_quant), tokens [L - L % 128, L) from the bf16 window (as
+ * decode_attention_bf16), merged with the same log-sum-exp combine.
+ *   seq_lens      device int32 [batch]: total tokens L (cache + window).
+ *   workspace     at least kvq_window_workspace_size() bytes (always needed).
+ *   other arguments as decode_attention_quant.
+ */
+kvq_status decode_attention_quant_window(const kvq_format* fmt, const void* q,
+                                         const kvq_cache* cache, const void* k_window,
+                                         const void* v_window, const int32_t* seq_lens,
+                                         const int32_t* page_table, int32_t max_pages_per_seq,
+                                         int32_t batch, int32_t max_len, float softmax_scale,
+                                         void* out, int32_t out_dtype, int32_t num_splits,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * kvq_stream_read -- measurement reference, not part of the method: reads
  * `bytes` of device memory once with 128-bit loads (grid-stride over 256 CUs)
  * and nothing else, giving the practical HBM read rate that the decode

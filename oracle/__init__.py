@@ -249,3 +249,31 @@ def decode_attention_bf16(q_bf16, k_bf16, v_bf16, seq_lens, max_len, scale, num_
     if rc != 0:
         raise ValueError("oracle: bad arguments")
     return out
+
+
+def _bf16_to_f64(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def decode_attention_window(fmt, q_bf16, cache, k_win_bf16, v_win_bf16, seq_lens, max_len, scale,
+                            page_table=None):
+    """[B][Hq][D] fp64 attention over the tokens of a cache filled by appends:
+    tokens [0, Lq) dequantised from the packed cache (Lq = L rounded down to a
+    multiple of 128, whole groups only), then tokens [Lq, L) from the bf16
+    residual window (token t in row t % 128 of [B][Hkv][128][D]). A plain
+    composition of dequantize_unit and attention_f64."""
+    q = _bf16_to_f64(q_bf16)
+    B, Hq, D = q.shape
+    H = fmt.num_kv_heads
+    R = Hq // H
+    out = np.zeros((B, Hq, D), np.float64)
+    for b in range(B):
+        L = int(seq_lens[b])
+        Lq = L - L % 128
+        for h in range(H):
+            kh = np.concatenate([dequantize_unit(fmt, "k", cache, b, h, Lq, max_len, page_table),
+                                 _bf16_to_f64(k_win_bf16[b, h, :L - Lq])])
+            vh = np.concatenate([dequantize_unit(fmt, "v", cache, b, h, Lq, max_len, page_table),
+                                 _bf16_to_f64(v_win_bf16[b, h, :L - Lq])])
+            out[b, h * R:(h + 1) * R] = attention_f64(q[b, h * R:(h + 1) * R], kh, vh, scale)
+    return out

@@ -352,3 +352,40 @@ def test_bf16_attention_vs_torch(orc):
                            synth.bf16_bits_to_f32(k[b, h, :lens[b]]).astype(np.float64),
                            synth.bf16_bits_to_f32(v[b, h, :lens[b]]).astype(np.float64), 0.088)
             assert np.allclose(out[b, 4 * h:4 * h + 4], want, rtol=1e-11, atol=1e-13)
+
+
+def test_window_attention_vs_torch_and_special_cases(orc):
+    """The residual-window decode: whole groups dequantised from the cache, the
+    rest from the bf16 window. Pinned to torch's fp64 attention on the
+    concatenation, to the cache-only decode when the window is empty, and to
+    the bf16 decode when no group is complete."""
+    rng = np.random.default_rng(11)
+    B, H, D = 3, 2, 128
+    lens = [300, 256, 77]  # window 44, empty, everything in the window
+    Lmax = 300
+    w = _small_workload(2, "channel", "token", [Lmax] * B)
+    fmt = orc.fmt_of(w)
+    k, v = w.kv_all("k"), w.kv_all("v")
+    lq = [L - L % 128 for L in lens]
+    cache = orc.quantize_pack(fmt, k, v, lq)
+    kw = synth.f32_to_bf16_bits(rng.standard_normal((B, H, 128, D)).astype(np.float32))
+    vw = synth.f32_to_bf16_bits(rng.standard_normal((B, H, 128, D)).astype(np.float32))
+    q = synth.f32_to_bf16_bits(rng.standard_normal((B, 4 * H, D)).astype(np.float32))
+    scale = 1 / math.sqrt(128)
+    out = orc.decode_attention_window(fmt, q, cache, kw, vw, lens, Lmax, scale)
+    qf = synth.bf16_bits_to_f32(q).astype(np.float64)
+    for b, L in enumerate(lens):
+        r = L - lq[b]
+        for h in range(H):
+            kh = np.concatenate([orc.dequantize_unit(fmt, "k", cache, b, h, lq[b], Lmax),
+                                 synth.bf16_bits_to_f32(kw[b, h, :r]).astype(np.float64)])
+            vh = np.concatenate([orc.dequantize_unit(fmt, "v", cache, b, h, lq[b], Lmax),
+                                 synth.bf16_bits_to_f32(vw[b, h, :r]).astype(np.float64)])
+            want = _sdpa64(qf[b, 4 * h:4 * h + 4], kh, vh, scale)
+            assert np.allclose(out[b, 4 * h:4 * h + 4], want, rtol=1e-11, atol=1e-13)
+    # empty window: the cache-only decode
+    full = orc.decode_attention(fmt, q, cache, lq, Lmax, scale)
+    assert np.allclose(out[1], full[1], rtol=1e-12, atol=1e-14)
+    # no complete group: the bf16 decode of the window alone
+    bfo = orc.decode_attention_bf16(q, kw, vw, [0, 0, 77], 128, scale, H)
+    assert np.allclose(out[2], bfo[2], rtol=1e-12, atol=1e-14)
