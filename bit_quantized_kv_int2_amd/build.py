@@ -9,8 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvq.so")
-SOURCES = ["kvq_api.hip", "kvq_pack.hip", "kvq_decode.hip", "kvq_bf16.hip", "kvq_stream.hip",
-           "kvq_append.hip"]
+SOURCES = ["kvq_api.hip", "kvq_pack.hip", "kvq_decode.hip", "kvq_decode_tg.hip", "kvq_bf16.hip",
+           "kvq_stream.hip", "kvq_append.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fno-fast-math",
@@ -21,7 +21,8 @@ HIPCC_FLAGS = [
 # every exp2 argument is finite or -inf). Without NaN semantics the IEEE mode
 # bit can be cleared, so float max needs no operand canonicalisation and a
 # DPP row rotation folds into the max itself.
-EXTRA_FLAGS = {"kvq_decode.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+EXTRA_FLAGS = {"kvq_decode.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+               "kvq_decode_tg.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def _compile(hipcc, src, obj):

@@ -42,7 +42,14 @@ kvq_status kvq_check_format(const kvq_format* f) {
   if (f->bits != 2 && f->bits != 4) return KVQ_ERR_BAD_FORMAT;
   if (f->k_axis != KVQ_TOKEN_WISE && f->k_axis != KVQ_CHANNEL_WISE) return KVQ_ERR_BAD_FORMAT;
   if (f->v_axis != KVQ_TOKEN_WISE && f->v_axis != KVQ_CHANNEL_WISE) return KVQ_ERR_BAD_FORMAT;
-  if (f->group != kGroup || f->head_dim != kHeadDim) return KVQ_ERR_BAD_FORMAT;
+  if (f->head_dim != kHeadDim) return KVQ_ERR_BAD_FORMAT;
+  // 128 everywhere; 32 or 64 channels per group when both axes are token-wise
+  // (the one group size then counts channels for K and V) on a contiguous cache
+  if (f->group != kGroup) {
+    if (f->group != 32 && f->group != 64) return KVQ_ERR_BAD_FORMAT;
+    if (f->k_axis != KVQ_TOKEN_WISE || f->v_axis != KVQ_TOKEN_WISE || f->page_size != 0)
+      return KVQ_ERR_BAD_FORMAT;
+  }
   if (f->num_kv_heads < 1 || f->num_kv_heads > 65535) return KVQ_ERR_BAD_FORMAT;
   if (f->num_q_heads != kGqa * f->num_kv_heads) return KVQ_ERR_BAD_FORMAT;
   if (f->page_size != 0 && f->page_size != kPage) return KVQ_ERR_BAD_FORMAT;
@@ -70,8 +77,9 @@ kvq_status kvq_cache_sizes(const kvq_format* f, int32_t batch, int32_t max_len,
   }
   bytes[0] = tokens * D * b / 8;
   bytes[1] = tokens * D * b / 8;
-  bytes[2] = (f->k_axis == KVQ_TOKEN_WISE ? tokens * 4 : groups * D * 4);
-  bytes[3] = (f->v_axis == KVQ_TOKEN_WISE ? tokens * 4 : groups * D * 4);
+  const size_t ng = (size_t)(kHeadDim / f->group);  // token-wise groups per token
+  bytes[2] = (f->k_axis == KVQ_TOKEN_WISE ? tokens * ng * 4 : groups * D * 4);
+  bytes[3] = (f->v_axis == KVQ_TOKEN_WISE ? tokens * ng * 4 : groups * D * 4);
   return KVQ_OK;
 }
 
@@ -191,6 +199,7 @@ kvq_status kv_quantize_pack(const kvq_format* f, const float* k, const float* v,
   a.v_axis = f->v_axis;
   a.paged = f->page_size != 0;
   a.padded_len = padded_len(max_len);
+  a.ng = kHeadDim / f->group;
   a.k_codes = (uint8_t*)out->k_codes;
   a.v_words = (uint32_t*)out->v_codes;
   a.k_sz = (uint16_t*)out->k_scale_offset;
@@ -346,6 +355,7 @@ kvq_status kv_append(const kvq_format* f, const void* k_new, const void* v_new,
   a.v_axis = f->v_axis;
   a.paged = f->page_size != 0;
   a.padded_len = padded_len(max_len);
+  a.ng = kHeadDim / f->group;
   a.k_win = (uint16_t*)k_window;
   a.v_win = (uint16_t*)v_window;
   a.k_codes = (uint8_t*)cache->k_codes;

@@ -36,37 +36,43 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
   g.table = a.page_table;
   const int g0 = L + 1 - kGroup;  // first token of the completed group
   const int qmax = (1 << a.bits) - 1, per = 32 / a.bits;
-  __shared__ float S[kGroup], Z[kGroup];  // one (s, z) per token (token-wise) or per channel (channel-wise)
+  // one (s, z) per token and channel group (token-wise, ng groups of G
+  // channels) or per channel (channel-wise)
+  const int ng = a.ng, G = kHeadDim / ng;
+  __shared__ float S[kGroup * 4], Z[kGroup * 4];
 
   for (int is_k = 1; is_k >= 0; --is_k) {
     const uint16_t* w = is_k ? kw : vw;
     const int axis = is_k ? a.k_axis : a.v_axis;
     uint16_t* sz = is_k ? a.k_sz : a.v_sz;
-    // (s, z) of the window's 128 groups
-    if (tid < kGroup) {
+    const int ngroups = axis == KVQ_TOKEN_WISE ? kGroup * ng : kHeadDim;
+    for (int gi = tid; gi < ngroups; gi += kAppendThreads) {
       float mn, mx;
-      if (axis == KVQ_TOKEN_WISE) {  // group = token tid, over its channels
-        const uint16_t* row = w + tid * kHeadDim;
+      long p;
+      if (axis == KVQ_TOKEN_WISE) {  // group = channels [jG, jG + G) of token t
+        const int t = gi / ng, j = gi % ng;
+        const uint16_t* row = w + t * kHeadDim + j * G;
         mn = mx = bf16_f32(row[0]);
-        for (int d = 1; d < kHeadDim; ++d) {
+        for (int d = 1; d < G; ++d) {
           const float v = bf16_f32(row[d]);
           mn = fminf(mn, v);
           mx = fmaxf(mx, v);
         }
-      } else {  // group = channel tid, over the 128 tokens
-        mn = mx = bf16_f32(w[tid]);
+        p = pair_token(g, b, h, g0 + t, j, ng);
+      } else {  // group = channel gi over the 128 tokens
+        mn = mx = bf16_f32(w[gi]);
         for (int t = 1; t < kGroup; ++t) {
-          const float v = bf16_f32(w[t * kHeadDim + tid]);
+          const float v = bf16_f32(w[t * kHeadDim + gi]);
           mn = fminf(mn, v);
           mx = fmaxf(mx, v);
         }
+        p = pair_channel(g, b, h, g0, gi);
       }
       const uint16_t s16 = f16_bits(__fdiv_rn(mx - mn, (float)qmax)), z16 = f16_bits(mn);
-      const long p = axis == KVQ_TOKEN_WISE ? pair_token(g, b, h, g0 + tid) : pair_channel(g, b, h, g0, tid);
       sz[p] = s16;
       sz[p + 1] = z16;
-      S[tid] = f16_val(s16);
-      Z[tid] = f16_val(z16);
+      S[gi] = f16_val(s16);
+      Z[gi] = f16_val(z16);
     }
     __syncthreads();
     if (is_k) {  // K: one word = 32/b consecutive channels of a token row
@@ -76,7 +82,7 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
         uint32_t wd = 0;
         for (int e = 0; e < per; ++e) {
           const int d = j * per + e;
-          const int gi = axis == KVQ_TOKEN_WISE ? t : d;
+          const int gi = axis == KVQ_TOKEN_WISE ? t * ng + d / G : d;
           wd |= (uint32_t)encode(bf16_f32(w[t * kHeadDim + d]), S[gi], Z[gi], qmax) << (a.bits * e);
         }
         const int tt = g0 + t;
@@ -90,7 +96,7 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
         uint32_t wd = 0;
         for (int e = 0; e < per; ++e) {
           const int t = t0 + e;
-          const int gi = axis == KVQ_TOKEN_WISE ? t : d;
+          const int gi = axis == KVQ_TOKEN_WISE ? t * ng + d / G : d;
           wd |= (uint32_t)encode(bf16_f32(w[t * kHeadDim + d]), S[gi], Z[gi], qmax) << (a.bits * e);
         }
         const int tt = g0 + t0;

@@ -1,0 +1,232 @@
+// Device helpers shared by the quantised decode kernels (internal): MFMA
+// operand construction from packed codes, DPP / permlane reductions, the
+// token <-> tile maps and the LDS layout of one chunk's fold operands.
+// Included by the decode sources, which are built without NaN semantics.
+#pragma once
+
+#include <math.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kThr = 8;          // lazy-max threshold in log2 units: P <= 2^kThr
+constexpr int kMaxGroups = kChunkTokens / kGroup;
+
+__device__ inline h8 as_h8(u4 v) { return __builtin_bit_cast(h8, v); }
+__device__ inline f4 mfma(u4 a, u4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a), as_h8(b), c, 0, 0, 0);
+}
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack_f16x2(float lo, float hi) {
+  // v_cvt_pk_f16_f32: both halves rounded to nearest even in one instruction
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), h2));
+}
+// two binary16 products, each rounded once (v_pk_mul_f16); operands are
+// taken by value: bit-casting an ext-vector element in place reads element 0
+__device__ inline uint32_t mul_f16x2(uint32_t x, uint32_t y) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, x) * __builtin_bit_cast(h2, y));
+}
+__device__ inline float f16lo(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u & 0xFFFF)); }
+__device__ inline float f16hi(uint32_t u) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(u >> 16)); }
+__device__ inline float f16val(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
+__device__ inline float bf16val(uint16_t u) { return __builtin_bit_cast(float, (uint32_t)u << 16); }
+
+// Cross-lane reductions without LDS: DPP row rotations inside 16-lane rows,
+// v_permlane16/32_swap across rows.
+// Every lane of every row is a valid source for these rotations, so the
+// bound-control form is exact and lets the compiler fold the move into the
+// consuming max / add (one DPP instruction per step).
+template <int R>
+__device__ inline float ror(float x) {  // lane l of a 16-lane row reads lane (l - R) mod 16
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x120 + R, 0xF, 0xF, true));
+}
+template <int R>
+__device__ inline uint32_t ror_u(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x120 + R, 0xF, 0xF, true);
+}
+__device__ inline float swap32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ inline float swap16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+__device__ inline float swap32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+__device__ inline float swap16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x), false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
+}
+// max / sum over the 16 lanes that share (lane & 3): lanes n, n+4, n+8, n+12 of all 4 rows
+__device__ inline float head_max(float x) {
+  x = fmaxf(x, ror<4>(x));
+  x = fmaxf(x, ror<8>(x));
+  return swap16_max(swap32_max(x));
+}
+__device__ inline float head_sum(float x) {
+  x += ror<4>(x);
+  x += ror<8>(x);
+  return swap16_sum(swap32_sum(x));
+}
+// max / sum over one 16-lane row
+__device__ inline float row_max(float x) {
+  x = fmaxf(x, ror<1>(x));
+  x = fmaxf(x, ror<2>(x));
+  x = fmaxf(x, ror<4>(x));
+  return fmaxf(x, ror<8>(x));
+}
+__device__ inline float row_sum(float x) {
+  x += ror<1>(x);
+  x += ror<2>(x);
+  x += ror<4>(x);
+  return x + ror<8>(x);
+}
+__device__ inline uint32_t row_max_u(uint32_t x) {
+  x = max(x, ror_u<1>(x));
+  x = max(x, ror_u<2>(x));
+  x = max(x, ror_u<4>(x));
+  return max(x, ror_u<8>(x));
+}
+__device__ inline uint32_t swap32_max_u(uint32_t x) {
+  auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max((uint32_t)r[0], (uint32_t)r[1]);
+}
+__device__ inline uint32_t swap16_max_u(uint32_t x) {
+  auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return max((uint32_t)r[0], (uint32_t)r[1]);
+}
+// whole-wave reductions
+__device__ inline float wave_max_dpp(float x) { return swap16_max(swap32_max(row_max(x))); }
+__device__ inline float wave_sum_dpp(float x) { return swap16_sum(swap32_sum(row_sum(x))); }
+__device__ inline uint32_t wave_max_u(uint32_t x) { return swap16_max_u(swap32_max_u(row_max_u(x))); }
+// largest binary16 bit pattern (sign cleared) among the low halves of 8 words
+__device__ inline uint32_t max_lo16(const u4& a, const u4& b) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) m = max(m, max(a[e] & 0x7FFFu, b[e] & 0x7FFFu));
+  return m;
+}
+
+// exponent e with x < 2^e (x > 0), 0 for x == 0: the frexp exponent
+// (x = f * 2^e with 0.5 <= f < 1), one v_frexp_exp_i32_f32
+__device__ inline int exp_above(float x) { return __builtin_amdgcn_frexp_expf(x); }
+
+// Unpack one 32-bit word of INT4 codes into one k-step of fp16 subnormals:
+// VGPR m holds codes (m, m+4), weight 16^(m&1).
+__device__ inline u4 unpack4(uint32_t w) {
+  uint32_t t = w >> 8;
+  return u4{w & 0x000F000Fu, w & 0x00F000F0u, t & 0x000F000Fu, t & 0x00F000F0u};
+}
+// Unpack one 32-bit word of INT2 codes into two k-steps: sel 0 from w, sel 1
+// from w >> 8; VGPR m of sel holds codes (4 sel + m, 8 + 4 sel + m), weight 4^m.
+__device__ inline u4 unpack2(uint32_t w, int sel) {
+  uint32_t t = sel ? (w >> 8) : w;
+  return u4{t & 0x00030003u, t & 0x000C000Cu, t & 0x00300030u, t & 0x00C000C0u};
+}
+
+template <int BITS>
+struct Cfg {
+  static constexpr int TPW = 32 / BITS;             // tokens per V word
+  static constexpr int TIT = 64;                    // tokens per wave iteration
+  static constexpr int NK = 2;                      // PV k-steps per iteration
+  static constexpr int KROW = kHeadDim * BITS / 8;  // bytes per K token row
+  static constexpr int KDW = KROW / 4;              // dwords per K token row
+  static constexpr int NVW = BITS == 4 ? 4 : 2;     // 16-byte V loads per lane
+  static constexpr int SLOTS = 8 / BITS;            // codes per byte
+  static constexpr int D2 = TPW / 2;                // token distance of a packed pair
+  // weight 2^(BITS*(m % SLOTS)) of VGPR m of an unpacked word (its codes' bit
+  // offset within their bytes); the other operand is divided by it
+  __device__ static inline float inv_w(int m) { return 1.0f / (float)(1 << (BITS * (m % SLOTS))); }
+  __device__ static inline float w(int m) { return (float)(1 << (BITS * (m % SLOTS))); }
+  // first of the 4 consecutive channels fed by half hf of QK k-step s
+  __device__ static inline int k_run(int s, int hf) {
+    return BITS == 4 ? 8 * s + 4 * hf : 16 * (s >> 1) + 4 * (s & 1) + 8 * hf;
+  }
+  // token (within an iteration) of QK row i = 4 gi + j in k-group q; chosen so
+  // that a lane's pairs (j = 2a, 2a + 1) are the two tokens of one packed V
+  // VGPR, which makes the P -> B-operand move one permute per VGPR
+  __device__ static inline int tok(int q, int gi, int j) {
+    const int base = BITS == 4 ? 8 * (gi >> 1) + 2 * (gi & 1) : 2 * gi;
+    return 16 * q + base + (j >> 1) + D2 * (j & 1);
+  }
+  // QK^T B-operand position of channel d: half hf of VGPR m of k-step s, as
+  // a binary16 index ((s * 4 + m) * 2 + hf); inverse of k_run
+  __device__ static inline int qpos(int d) {
+    const int m = d & 3;
+    const int s = BITS == 4 ? d >> 3 : 2 * (d >> 4) + ((d >> 2) & 1);
+    const int hf = BITS == 4 ? (d >> 2) & 1 : (d >> 3) & 1;
+    return (s * 4 + m) * 2 + hf;
+  }
+  // 1 / weight of channel d's code slot (its bit offset within its byte)
+  __device__ static inline float inv_wd(int d) { return 1.0f / (float)(1 << (BITS * (d % SLOTS))); }
+};
+
+// LDS layout (bytes) for one chunk. LDS serves 128 bytes per clock in 32
+// four-byte banks; the q'' rows of the four heads are 288 bytes apart (16 k-steps
+// of 16 bytes plus 32 bytes of padding) and the block of zeros starts 16 bytes
+// into a 128-byte line, so the five distinct 16-byte addresses of one
+// B-operand read (four heads, zeros) fall in five different bank groups.
+template <int KAX, int VAX>
+struct Lds {
+  static constexpr int HEAD_STRIDE = 288;                       // bytes per head's 16 k-steps of q''
+  static constexpr int GROUP_STRIDE = 4 * HEAD_STRIDE;           // 9 x 128 bytes
+  static constexpr int QS = 0;                                   // float [4][128] / binary16 q
+  static constexpr int QB = QS + 4 * 128 * 4;                    // u4 [groups][4 heads][18] (16 used)
+  static constexpr int QB_BYTES = (KAX == KVQ_CHANNEL_WISE ? kMaxGroups : 1) * GROUP_STRIDE;
+  static constexpr int QZ = QB + QB_BYTES + 16;                  // 256 B of zeros (off-diagonal B)
+  static constexpr int KB = QZ + 256 + 112;                      // chan-K (scale, bias) [groups][4] / tok-K (s',z'') [tokens]
+  static constexpr int KB_BYTES = KAX == KVQ_CHANNEL_WISE ? kMaxGroups * 4 * 8 : kChunkTokens * 8;
+  static constexpr int VA = KB + KB_BYTES;                       // tok-V coef [tokens] / chan-V (sigma,rho) [groups][128]
+  static constexpr int VG_BLOCK = 32 * 8 + 16;                   // chan-V: 32 channels' (sigma, rho) + 16 B padding
+  static constexpr int VG_GROUP = 4 * VG_BLOCK;                  // chan-V: one 128-token group
+  static constexpr int VA_BYTES = VAX == KVQ_TOKEN_WISE ? kChunkTokens * 4 : kMaxGroups * VG_GROUP;
+  static constexpr int VR = VA + VA_BYTES;                       // tok-V rho hi, lo rows, fp16, A-operand order
+  static constexpr int VR_LO = kChunkTokens + 32;                // lo row offset in halfwords (64 B off the hi row's banks)
+  static constexpr int VR_BYTES = VAX == KVQ_TOKEN_WISE ? 2 * VR_LO * 2 : 0;
+  static constexpr int RED = VR + VR_BYTES;                      // float [32] reductions
+  static constexpr int TOTAL = RED + 32 * 4;
+  // merge area reuses the front of LDS after the main loop
+  static constexpr int MO = 0;                                   // float [4 waves][4 heads][128]
+  static constexpr int ML = MO + 4 * 4 * 128 * 4;                // float [4 waves][4 heads][2]
+  static_assert(ML + 4 * 4 * 2 * 4 <= RED, "merge area overlaps reductions");
+  static_assert(QB % 128 == 0 && GROUP_STRIDE % 128 == 0 && (QZ - QB) % 128 == 16, "bank layout");
+  static_assert(KB % 16 == 0 && VA % 16 == 0 && VR % 16 == 0, "alignment");
+};
+
+// Token-wise V: byte offset of the coefficient pair p (tokens 2p, 2p + 1).
+// Within every odd 128-byte block of 16 pairs the offset is XORed with 32 B
+// (INT2) or 16 B (INT4), a permutation inside the block, so that the 16
+// pairs one read instruction gathers (lanes of different token quarters,
+// spread over two adjacent blocks) land in distinct banks. Pairs 2i, 2i + 1
+// stay adjacent (a 16-byte write covers both).
+template <int BITS>
+__device__ inline int coef_off(int p) { return (8 * p) ^ ((BITS == 2 ? 32 : 16) * ((p >> 4) & 1)); }
+// Channel-wise V: byte offset of channel d's (sigma, rho) in group gi; each
+// 32-channel block is padded by 16 B so the four lane groups' reads (one
+// block each) fall in different banks.
+template <int KAX, int VAX>
+__device__ inline int vg_off(int gi, int d) {
+  return gi * Lds<KAX, VAX>::VG_GROUP + (d >> 5) * Lds<KAX, VAX>::VG_BLOCK + (d & 31) * 8;
+}
+
+// Work-groups per CU the register allocation targets (4 waves of 256 threads
+// per SIMD leave 128 VGPRs, 3 leave 168): INT2 with token-wise V fits in 128;
+// channel-wise V keeps a second 8-tile accumulator and INT4 twice the codes.
+constexpr int groups_per_cu(int bits, int vax) { return (bits == 2 && vax == KVQ_TOKEN_WISE) ? 4 : 3; }
+
+}  // namespace
+}  // namespace kvq

@@ -1,0 +1,452 @@
+// Decode attention over INT2/INT4 caches whose K and V groups are both
+// token-wise with G = 128 / NG channels per group (NG = 2: G = 64, NG = 4:
+// G = 32), gfx950. A token has NG (s, z) pairs per tensor.
+//
+// Folds (rag-lover.com explainer; limits section: an acc-fold partial is
+// scaled per quantisation group and never accumulated across groups):
+//   q.K^T, acc-fold per channel group j:
+//     S_t = sum_j [ s_{t,j} (q_j . c_{t,j}) + z_{t,j} sum_{d in j} q_d ]
+//     one MFMA accumulator per group; the 16 k-steps fall into NG blocks of
+//     16 / NG consecutive k-steps, one per group.
+//   P.V, operand-fold per channel group:
+//     O_d = sum_t (P_t s_{t,j(d)}) c_{t,d} + sum_t P_t z_{t,j(d)}
+//     every 16-channel tile lies in one group (tile c = channels 16c..16c+15)
+//     and takes that group's P'' operand; one offset tile per group.
+// Everything else (block-diagonal QK^T, token maps, subnormal operands,
+// consistent offsets, lazy softmax, wave-local chunks) is as in the G = 128
+// kernel; a chunk holds 2048 / NG tokens so its fold operands fit the same LDS.
+#include "kvq_internal.h"
+#include "kvq_decode_common.h"
+
+namespace kvq {
+namespace {
+
+template <int BITS, int NG>
+struct TgLds {
+  static constexpr int CHUNK = kChunkTokens / NG;           // tokens per chunk
+  static constexpr int HEAD_STRIDE = 288;                    // q'' of one head: 16 k-steps + padding
+  static constexpr int QS = 0;                               // float q [4][128]
+  static constexpr int QB = QS + 4 * 128 * 4;                // u4 q'' [4 heads][18]
+  static constexpr int QZ = QB + 4 * HEAD_STRIDE + 16;       // 256 B of zeros, 16 B into a 128-byte line
+  static constexpr int KB = QZ + 256 + 112;                  // float2 (s', z'') [CHUNK tokens][NG]
+  static constexpr int VA = KB + CHUNK * NG * 8;             // float coef [NG][CHUNK], pairs XOR-permuted
+  static constexpr int VA_GROUP = CHUNK * 4;
+  static constexpr int VR = VA + NG * VA_GROUP;              // fp16 offset-tile rows [NG][hi, lo][VR_LO]
+  static constexpr int VR_LO = CHUNK + 32;                   // halfwords (lo row 64 B off the hi row's banks)
+  static constexpr int VR_GROUP = 2 * VR_LO;                 // halfwords per group
+  static constexpr int RED = VR + NG * VR_GROUP * 2;         // float [32]: q max per head, q sums per (head, group)
+  static constexpr int TOTAL = RED + 32 * 4;
+  static constexpr int MO = 0;                               // merge area (after the main loop)
+  static constexpr int ML = MO + 4 * 4 * 128 * 4;
+  static_assert(ML + 4 * 4 * 2 * 4 <= RED, "merge area overlaps reductions");
+  static_assert(QB % 128 == 0 && (QZ - QB) % 128 == 16, "bank layout");
+  static_assert(KB % 16 == 0 && VA % 16 == 0 && VR % 16 == 0, "alignment");
+};
+
+template <int BITS, int NG>
+__global__ void __launch_bounds__(kThreads, 3) decode_tg_kernel(DecodeArgs a) {
+  using C = Cfg<BITS>;
+  using M = TgLds<BITS, NG>;
+  constexpr int G = kHeadDim / NG;   // channels per group
+  constexpr int TPG = 8 / NG;        // 16-channel PV tiles per group
+  constexpr int NV = BITS == 2 ? 8 : 16;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[M::TOTAL];
+  float* qs = (float*)(lds + M::QS);
+  float* red = (float*)(lds + M::RED);
+
+  const int sp = __builtin_amdgcn_workgroup_id_x(), h = __builtin_amdgcn_workgroup_id_y(),
+            b = __builtin_amdgcn_workgroup_id_z();
+  const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = a.num_kv_heads, Hq = H * kGqa;
+  int L = min(max(a.seq_lens[b], 0), a.max_len);
+  if (a.len_mode == 1) L -= L % kGroup;
+  const int tb = sp * a.split_tokens;
+  const int te = min(tb + a.split_tokens, L);
+  const long row0 = (long)b * Hq + (long)h * kGqa;
+
+  if (te <= tb) {  // nothing in this split (or an empty sequence)
+    for (int e = tid; e < kGqa * kHeadDim; e += kThreads) {
+      int hh = e / kHeadDim, d = e % kHeadDim;
+      if (a.direct_out) {
+        if (a.out_bf16) ((uint16_t*)a.out)[(row0 + hh) * kHeadDim + d] = 0;
+        else ((float*)a.out)[(row0 + hh) * kHeadDim + d] = 0.f;
+      } else {
+        const long pr = (row0 + hh) * a.part_stride + a.part_base + sp;
+        a.part_o[pr * kHeadDim + d] = 0.f;
+        if (d == 0) {
+          a.part_ml[pr * 2] = -INFINITY;
+          a.part_ml[pr * 2 + 1] = 0.f;
+        }
+      }
+    }
+    return;
+  }
+  const float alpha = a.scale_log2;
+
+  // ---- cache addressing (contiguous caches) -----------------------------
+  const long unit = (long)b * H + h;
+  auto chunk_of = [&](int t) -> long { return unit * (a.padded_len / kPage) + t / kPage; };
+  auto pair_at = [&](const uint16_t* sz, int t, int j) -> const uint32_t* {
+    return (const uint32_t*)(sz + ((chunk_of(t) * kPage + t % kPage) * NG + j) * 2);
+  };
+
+  const int n = lane & 15, g = lane >> 4, hh = n & 3;
+  const int ri = lane & 15;
+
+  // ---- code loads for one 64-token iteration ---------------------------
+  // K as in the G = 128 kernel (each lane one token's whole row). V: lane
+  // (ri, g) loads, for each 16-channel tile c, the word of channel 16c + ri
+  // in word row g (INT2) or rows g and g + 4 (INT4; k-step k = row g + 4k).
+  struct Codes {
+    u4 k[C::KDW / 4];
+    uint32_t v[NV];
+  };
+  auto lane_koff = [](int lg, int lr) { return (uint32_t)(C::tok(lg, lr >> 2, lr & 3) * C::KROW); };
+  auto load_codes = [&](int t0, Codes& cd, uint32_t koff, int lg, int lr) {
+    const long ch = chunk_of(t0);
+    const unsigned char* kb = a.k_codes + (ch * kPage + t0 % kPage) * C::KROW + koff;
+#pragma unroll
+    for (int e = 0; e < C::KDW / 4; ++e) cd.k[e] = *(const u4*)(kb + 16 * e);
+    const uint32_t* vb = a.v_words + (ch * (kPage / C::TPW) + (t0 % kPage) / C::TPW + lg) * kHeadDim + lr;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) cd.v[e] = vb[(e >> 3) * 4 * kHeadDim + 16 * (e & 7)];
+  };
+
+  // wave wv owns the 128-token groups wv, wv + 4, ... (iterations 2G, 2G + 1)
+  Codes cur;
+  {
+    const int t0 = tb + 2 * wv * C::TIT;
+    if (t0 < te) load_codes(t0, cur, lane_koff(g, ri), g, ri);
+  }
+
+  // ---- query: once per split -------------------------------------------------
+  {
+    const int d = lane * 2;  // wave wv loads query head wv
+    const uint32_t qq = *(const uint32_t*)(a.q + (row0 + wv) * kHeadDim + d);
+    const float q0 = bf16val((uint16_t)(qq & 0xFFFF)), q1 = bf16val((uint16_t)(qq >> 16));
+    const float m = wave_max_dpp(fmaxf(fabsf(q0), fabsf(q1)));
+    qs[wv * 128 + d] = q0;
+    qs[wv * 128 + d + 1] = q1;
+    // sum of q over each channel group: G / 2 lanes (one DPP row for G = 32,
+    // two rows for G = 64)
+    float gs = row_sum(q0 + q1);
+    if (NG == 2) gs = swap16_sum(gs);
+    if ((lane % (G / 2)) == 0) red[16 + wv * 4 + lane / (G / 2)] = gs;
+    if (lane == 0) red[wv] = m;
+  }
+  if (tid < 16) ((u4*)(lds + M::QZ))[tid] = u4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  // q'' = q * 2^-E / w (max |q''| < 2^14), shared by all waves and groups
+  const float qmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int E = exp_above(qmax) - 14;
+  if (tid < 64) {
+    const float two_mE = ldexpf(1.f, -E);
+    const int s = tid & 15, qh = tid >> 4;
+    uint32_t wds[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      float v0 = qs[qh * 128 + C::k_run(s, 0) + m] * two_mE * C::inv_w(m);
+      float v1 = qs[qh * 128 + C::k_run(s, 1) + m] * two_mE * C::inv_w(m);
+      wds[m] = pack_f16x2(v0, v1);
+    }
+    ((u4*)(lds + M::QB + qh * M::HEAD_STRIDE))[s] = u4{wds[0], wds[1], wds[2], wds[3]};
+  }
+  __syncthreads();
+  const float ktok_sc = alpha * ldexpf(1.f, E + 24);
+
+  f4 O[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) O[c] = f4{0.f, 0.f, 0.f, 0.f};
+  f4 X[NG];  // offset tile per group
+#pragma unroll
+  for (int j = 0; j < NG; ++j) X[j] = f4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float lsum = 0.f;
+  int F = 0;  // P'' = P * s * 2^-F / w, running per wave
+
+  for (int cb = tb; cb < te; cb += M::CHUNK) {
+    const int ce = min(cb + M::CHUNK, te);
+    const int ntok = ce - cb;
+
+    // ---- prologue: lane l builds group pj = l / (64/NG) of the 8-token
+    // A-operand block lb = l % (64/NG) of this wave's tokens ----------------
+    int pl = lane;
+    asm volatile("" : "+v"(pl));
+    const int lb = pl % (64 / NG), pj = pl / (64 / NG);
+    const int bu = lb & 15;
+    const int pit = 2 * (wv + 4 * (lb >> 4)) + (bu >> 3);
+    const int pblk = pit * 8 + (bu & 7);
+    int tb_run[2];
+    {
+      const int ks = (bu >> 2) & 1, gg = bu & 3;
+      if (BITS == 2) {
+        tb_run[0] = pit * C::TIT + 16 * gg + 4 * ks;
+        tb_run[1] = tb_run[0] + 8;
+      } else {
+        tb_run[0] = pit * C::TIT + 32 * ks + 8 * gg;
+        tb_run[1] = tb_run[0] + 4;
+      }
+    }
+    uint32_t kz[2][4], vz[2][4];
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = tb_run[rr] + e;
+        const bool ok = t < ntok;
+        kz[rr][e] = ok ? *pair_at(a.k_sz, cb + t, pj) : 0u;
+        vz[rr][e] = ok ? *pair_at(a.v_sz, cb + t, pj) : 0u;
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    {
+      // every scale of this wave's tokens < 2^Fs (scales of 0 count as 1)
+      uint32_t mb = 0;
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mb = max(mb, vz[rr][e] & 0x7FFFu);
+      mb = wave_max_u(mb);
+      const int Fc = max((int)(mb >> 10) - 14, 1) + kThr - 14;
+      if (cb == tb) {
+        F = Fc;
+      } else if (Fc > F) {
+        const float sc = ldexpf(1.f, F - Fc);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) O[c] *= sc;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) X[j] *= sc;
+        F = Fc;
+      }
+      const float two_mF = ldexpf(1.f, -F);
+      unsigned char* coef = lds + M::VA + pj * M::VA_GROUP;
+      _Float16* rh = (_Float16*)(lds + M::VR) + pj * M::VR_GROUP;
+      float rw[2][4];
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        float cf[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float wt = (float)(1 << (BITS * (e % C::SLOTS)));
+          const float sv = f16lo(vz[rr][e]), zv = f16hi(vz[rr][e]);
+          const float sg = sv != 0.f ? sv : 1.f;
+          cf[e] = sg * (two_mF / wt);
+          rw[rr][e] = zv * (__builtin_amdgcn_rcpf(sg) * wt);
+        }
+        *(float4*)(coef + coef_off<BITS>(tb_run[rr] / 2)) = make_float4(cf[0], cf[1], cf[2], cf[3]);
+      }
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float a0 = rw[0][m], a1 = rw[1][m];
+        hi[m] = pack_f16x2(a0, a1);
+        lo[m] = pack_f16x2(a0 - f16lo(hi[m]), a1 - f16hi(hi[m]));
+      }
+      ((u4*)rh)[pblk] = u4{hi[0], hi[1], hi[2], hi[3]};
+      ((u4*)(rh + M::VR_LO))[pblk] = u4{lo[0], lo[1], lo[2], lo[3]};
+      // token-wise K: (s', z'') of (token, group pj)
+      float2* ktok = (float2*)(lds + M::KB);
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          ktok[(tb_run[rr] + e) * NG + pj] = make_float2(f16lo(kz[rr][e]) * ktok_sc, f16hi(kz[rr][e]) * alpha);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+    // ---- per-lane constants of the main loop (laundered lane id) ---------
+    int mlane = lane;
+    asm volatile("" : "+v"(mlane));
+    const int mn_ = mlane & 15, mg = mlane >> 4, mhh = mn_ & 3, mnq = mn_ >> 2;
+    const uint32_t koff = lane_koff(mg, mn_);
+    const int tk0 = C::tok(mnq, mg, 0);
+    const bool qlive = mg == mnq;
+    int src[2][2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) {
+        const int sq = BITS == 2 ? mg : 2 * k + (mg >> 1);
+        const int sg = BITS == 2 ? 2 * k + m2 : 2 * (mg & 1) + m2;
+        src[k][m2] = 4 * (mhh + 4 * sq + 16 * sg);
+      }
+    const int rrow = (mn_ & 1) * M::VR_LO + 8 * mg;
+    float Qs[NG];
+#pragma unroll
+    for (int j = 0; j < NG; ++j) Qs[j] = red[16 + mhh * 4 + j];
+
+    for (int jj = 0;; ++jj) {
+      const int it = 2 * (wv + 4 * (jj >> 1)) + (jj & 1);
+      const int t0 = cb + it * C::TIT;
+      if (t0 >= ce) break;
+      Codes nxt;
+      const int t1 = t0 + ((jj & 1) ? 7 : 1) * C::TIT;
+      if (t1 < te) load_codes(t1, nxt, koff, mg, mn_);
+      const int rel = t0 - cb;
+
+      // QK^T: k-step s belongs to channel group s * NG / 16; consecutive
+      // MFMAs go to different groups' accumulators
+      float S[4];
+      {
+        const u4* qb = (const u4*)(lds + (qlive ? M::QB + mhh * M::HEAD_STRIDE : M::QZ));
+        f4 acc[NG];
+#pragma unroll
+        for (int j = 0; j < NG; ++j) acc[j] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ss = 0; ss < 16; ++ss) {
+          const int j = ss % NG, s = j * (16 / NG) + ss / NG;
+          const uint32_t w = BITS == 4 ? cur.k[s >> 2][s & 3] : cur.k[s >> 3][(s >> 1) & 3];
+          const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, s & 1);
+          acc[j] = mfma(av, qb[s], acc[j]);
+        }
+        const float2* kt = (const float2*)(lds + M::KB);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int t = rel + tk0 + (q4 >> 1) + C::D2 * (q4 & 1);  // S[q4]'s token
+          float sv = 0.f;
+#pragma unroll
+          for (int j = 0; j < NG; ++j) {
+            const float2 p = kt[t * NG + j];
+            sv = fmaf(acc[j][q4], p.x, fmaf(p.y, Qs[j], sv));
+          }
+          S[q4] = sv;
+        }
+      }
+      if (t0 + C::TIT > te) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (t0 + tk0 + (j >> 1) + C::D2 * (j & 1) >= te) S[j] = -INFINITY;
+      }
+      const float mx = head_max(fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3])));
+      if (__any(mx > m_run + (float)kThr)) {
+        const float mn = fmaxf(m_run, mx);
+        const float sc = exp2_fast(m_run - mn);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) O[c] *= sc;
+#pragma unroll
+        for (int j = 0; j < NG; ++j) X[j] *= sc;
+        lsum *= sc;
+        m_run = mn;
+      }
+      float P[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) P[j] = exp2_fast(S[j] - m_run);
+      lsum += (P[0] + P[1]) + (P[2] + P[3]);
+
+      // PV, one channel group at a time: its P'' operand, its tiles, its offset tile
+#pragma unroll
+      for (int j = 0; j < NG; ++j) {
+        const unsigned char* cf = lds + M::VA + j * M::VA_GROUP;
+        const float2 c0 = *(const float2*)(cf + coef_off<BITS>((rel + tk0) / 2));
+        const float2 c1 = *(const float2*)(cf + coef_off<BITS>((rel + tk0 + C::D2) / 2));
+        uint32_t pk[2];
+        pk[0] = pack_f16x2(P[0] * c0.x, P[1] * c1.x);
+        pk[1] = pack_f16x2(P[2] * c0.y, P[3] * c1.y);
+        u4 bp[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            bp[k][m] = (uint32_t)__builtin_amdgcn_ds_bpermute(src[k][m >> 1], (int)pk[m & 1]);
+        const _Float16* rbase = (const _Float16*)(lds + M::VR) + j * M::VR_GROUP;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+#pragma unroll
+          for (int ct = 0; ct < TPG; ++ct) {
+            const int c = j * TPG + ct;
+            const uint32_t w = BITS == 4 ? cur.v[8 * k + c] : cur.v[c];
+            const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
+            O[c] = mfma(av, bp[k], O[c]);
+          }
+          const int pos = ((rel / C::TIT) * C::NK + k) * 32;
+          X[j] = mfma(*(const u4*)(rbase + rrow + pos), bp[k], X[j]);
+        }
+      }
+      cur = nxt;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  }
+
+  // ---- per-wave result ----------------------------------------------------
+  lsum = head_sum(lsum);
+  {
+    const float s24 = ldexpf(1.f, F + 24), sF = ldexpf(1.f, F);
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const float off = __shfl(X[j][0] + X[j][1], n);  // rows 0, 1 live in lane group 0
+#pragma unroll
+      for (int ct = 0; ct < TPG; ++ct)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) O[j * TPG + ct][q4] = fmaf(O[j * TPG + ct][q4], s24, off * sF);
+    }
+  }
+
+  // ---- merge the four waves --------------------------------------------
+  __syncthreads();
+  float* mo = (float*)(lds + M::MO);
+  float* ml = (float*)(lds + M::ML);
+  if (n < 4 && g == 0) ml[(wv * 4 + n) * 2] = m_run;
+  __syncthreads();
+  float mall = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) mall = fmaxf(mall, ml[(w * 4 + hh) * 2]);
+  const float f = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - mall);
+  __syncthreads();
+  if (n < 4) {
+    // lane (n, g) holds rows 4g .. 4g + 3 of every tile: channels 16c + 4g + q4
+    float* dst = mo + (wv * 4 + n) * kHeadDim + 4 * g;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) dst[16 * c + q4] = O[c][q4] * f;
+    if (g == 0) ml[(wv * 4 + n) * 2 + 1] = lsum * f;
+  }
+  if (n < 4 && g == 0) ml[(wv * 4 + n) * 2] = mall;
+  __syncthreads();
+  {
+    const int qh = tid >> 6, d = (tid & 63) * 2;
+    float n0 = 0.f, n1 = 0.f, lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      n0 += mo[(w * 4 + qh) * kHeadDim + d];
+      n1 += mo[(w * 4 + qh) * kHeadDim + d + 1];
+      lt += ml[(w * 4 + qh) * 2 + 1];
+    }
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float o0 = n0 * inv, o1 = n1 * inv;
+    const long row = row0 + qh;
+    if (a.direct_out) {
+      if (a.out_bf16) {
+        __bf16 b0 = (__bf16)o0, b1 = (__bf16)o1;
+        uint32_t pk = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+                      ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+        *(uint32_t*)((uint16_t*)a.out + row * kHeadDim + d) = pk;
+      } else {
+        *(float2*)((float*)a.out + row * kHeadDim + d) = make_float2(o0, o1);
+      }
+    } else {
+      const long pr = row * a.part_stride + a.part_base + sp;
+      *(float2*)(a.part_o + pr * kHeadDim + d) = make_float2(o0, o1);
+      if (d == 0) {
+        a.part_ml[pr * 2] = ml[(0 * 4 + qh) * 2];
+        a.part_ml[pr * 2 + 1] = lt;
+      }
+    }
+  }
+}
+
+template <int BITS, int NG>
+hipError_t launch_tg(const DecodeArgs& a, hipStream_t s) {
+  dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
+  decode_tg_kernel<BITS, NG><<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_quant_tg(const kvq_format& f, const DecodeArgs& a, hipStream_t s) {
+  if (f.group == 64) return f.bits == 4 ? launch_tg<4, 2>(a, s) : launch_tg<2, 2>(a, s);
+  return f.bits == 4 ? launch_tg<4, 4>(a, s) : launch_tg<2, 4>(a, s);
+}
+
+}  // namespace kvq

@@ -31,6 +31,7 @@ struct AppendArgs {
   int v_axis;
   int paged;
   int padded_len;
+  int ng;                  // token-wise (s, z) pairs per token: 128 / group
   uint16_t* k_win;         // bf16 [B][Hkv][128][D]
   uint16_t* v_win;
   uint8_t* k_codes;
@@ -104,6 +105,7 @@ struct PackArgs {
   int v_axis;
   int paged;
   int padded_len;
+  int ng;                  // token-wise (s, z) pairs per token: 128 / group
   uint8_t* k_codes;
   uint32_t* v_words;
   uint16_t* k_sz;
@@ -113,6 +115,8 @@ struct PackArgs {
 // Kernel launchers (return the hipError_t of the launch).
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_decode_quant(const kvq_format& f, const DecodeArgs& a, hipStream_t s);
+// token-wise K and V with 32 or 64 channels per group (contiguous caches)
+hipError_t launch_decode_quant_tg(const kvq_format& f, const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const Bf16Args& a, hipStream_t s);
 hipError_t launch_combine(const float* part_o, const float* part_ml, int rows, int num_splits,
                           void* out, int out_bf16, hipStream_t s);

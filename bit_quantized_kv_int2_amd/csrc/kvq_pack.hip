@@ -24,29 +24,32 @@ __global__ void __launch_bounds__(256) sz_token_kernel(PackArgs a, Geo g, int is
   const float* x = is_k ? a.k : a.v;
   uint16_t* sz = is_k ? a.k_sz : a.v_sz;
   const int qmax = (1 << a.bits) - 1;
-  const long total = (long)a.batch * a.num_kv_heads * a.padded_len;
+  const int ng = a.ng, G = kHeadDim / ng;  // one pair per G consecutive channels of a token
+  const long total = (long)a.batch * a.num_kv_heads * a.padded_len * ng;
   for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < total;
        i += (long)gridDim.x * blockDim.x) {
-    int t = (int)(i % a.padded_len);
-    long bh = i / a.padded_len;
+    const int j = (int)(i % ng);
+    const long r = i / ng;
+    int t = (int)(r % a.padded_len);
+    long bh = r / a.padded_len;
     int h = (int)(bh % a.num_kv_heads), b = (int)(bh / a.num_kv_heads);
     int L = min(max(a.seq_lens[b], 0), a.max_len);
     if (t >= g.extent(L)) continue;
     uint16_t s16 = 0, z16 = 0;
     if (t < L) {
-      const float4* row = (const float4*)(x + ((bh * a.max_len) + t) * (long)kHeadDim);
+      const float4* row = (const float4*)(x + ((bh * a.max_len) + t) * (long)kHeadDim + j * G);
       float4 v0 = row[0];
       float mn = fminf(fminf(v0.x, v0.y), fminf(v0.z, v0.w));
       float mx = fmaxf(fmaxf(v0.x, v0.y), fmaxf(v0.z, v0.w));
-      for (int j = 1; j < kHeadDim / 4; ++j) {
-        float4 v = row[j];
+      for (int c = 1; c < G / 4; ++c) {
+        float4 v = row[c];
         mn = fminf(mn, fminf(fminf(v.x, v.y), fminf(v.z, v.w)));
         mx = fmaxf(mx, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
       }
       s16 = f16_bits(__fdiv_rn(mx - mn, (float)qmax));
       z16 = f16_bits(mn);
     }
-    long p = pair_token(g, b, h, t);
+    long p = pair_token(g, b, h, t, j, ng);
     sz[p] = s16;
     sz[p + 1] = z16;
   }
@@ -107,8 +110,8 @@ __global__ void __launch_bounds__(256) k_codes_kernel(PackArgs a, Geo g) {
     if (t < L) {
       const float* xr = a.k + (bh * a.max_len + t) * (long)kHeadDim + j * per;
       float S = 0.f, Z = 0.f;
-      if (a.k_axis == KVQ_TOKEN_WISE) {
-        long p = pair_token(g, b, h, t);
+      if (a.k_axis == KVQ_TOKEN_WISE) {  // a word's channels lie in one group (32/b <= 16 <= G)
+        long p = pair_token(g, b, h, t, (j * per) / (kHeadDim / a.ng), a.ng);
         S = f16_val(a.k_sz[p]);
         Z = f16_val(a.k_sz[p + 1]);
       }
@@ -146,7 +149,8 @@ __global__ void __launch_bounds__(256) v_codes_kernel(PackArgs a, Geo g) {
     for (int e = 0; e < per; ++e) {
       int t = t0 + e;
       if (t >= L) break;
-      long p = (a.v_axis == KVQ_TOKEN_WISE) ? pair_token(g, b, h, t) : pair_channel(g, b, h, t, d);
+      long p = (a.v_axis == KVQ_TOKEN_WISE) ? pair_token(g, b, h, t, d / (kHeadDim / a.ng), a.ng)
+                                            : pair_channel(g, b, h, t, d);
       float S = f16_val(a.v_sz[p]), Z = f16_val(a.v_sz[p + 1]);
       float xv = a.v[(bh * a.max_len + t) * (long)kHeadDim + d];
       w |= (uint32_t)encode(xv, S, Z, qmax) << (bits * e);
@@ -172,7 +176,7 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
   for (int is_k = 1; is_k >= 0; --is_k) {
     int axis = is_k ? a.k_axis : a.v_axis;
     if (axis == KVQ_TOKEN_WISE)
-      sz_token_kernel<<<grid_for(tok), 256, 0, s>>>(a, g, is_k);
+      sz_token_kernel<<<grid_for(tok * a.ng), 256, 0, s>>>(a, g, is_k);
     else
       sz_channel_kernel<<<grid_for(grp), 256, 0, s>>>(a, g, is_k);
     hipError_t e = hipGetLastError();

@@ -28,8 +28,9 @@ __device__ inline uint16_t f16_bits(float x) {
 }
 __device__ inline float f16_val(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
 
-__device__ inline long pair_token(const Geo& g, int b, int h, int t) {
-  return (g.chunk(b, h, t) * kPage + t % kPage) * 2;
+// token-wise pair of token t, channel group j (ng groups per token)
+__device__ inline long pair_token(const Geo& g, int b, int h, int t, int j, int ng) {
+  return ((g.chunk(b, h, t) * kPage + t % kPage) * ng + j) * 2;
 }
 __device__ inline long pair_channel(const Geo& g, int b, int h, int t, int d) {
   if (!g.paged) return (((long)b * g.H + h) * (g.Lp / kGroup) + t / kGroup) * (long)kHeadDim * 2 + d * 2;

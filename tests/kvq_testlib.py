@@ -31,9 +31,15 @@ def max_abs(a, b):
     return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)))) if np.size(a) else 0.0
 
 
+def group_of(w):
+    """Group size of a workload (128 unless the workload sets extra['group'])."""
+    return int(w.extra.get("group", 128))
+
+
 def gpu_format(w):
     import bit_quantized_kv_int2_amd as kvq
-    return kvq.make_format(w.bits, w.k_axis, w.v_axis, w.num_kv_heads, page_size=w.page_size)
+    return kvq.make_format(w.bits, w.k_axis, w.v_axis, w.num_kv_heads, page_size=w.page_size,
+                           group=group_of(w))
 
 
 class Inputs:
@@ -52,13 +58,14 @@ class Inputs:
 
 def oracle_pack(inp: Inputs):
     w = inp.w
-    return oracle.quantize_pack(oracle.fmt_of(w), inp.k, inp.v, inp.lens, page_table=inp.table,
+    return oracle.quantize_pack(oracle.fmt_of(w, group_of(w)), inp.k, inp.v, inp.lens,
+                                page_table=inp.table,
                                 num_pages=inp.num_pages)
 
 
 def oracle_attention(inp: Inputs, cache, units=None):
     w = inp.w
-    return oracle.decode_attention(oracle.fmt_of(w), inp.q, cache, inp.lens, w.max_len, SCALE,
+    return oracle.decode_attention(oracle.fmt_of(w, group_of(w)), inp.q, cache, inp.lens, w.max_len, SCALE,
                                    page_table=inp.table, units=units)
 
 

@@ -79,6 +79,21 @@ def test_cache_sizes(L):
     assert kc == 100 * 8 * 64 * 64 and ks == 100 * 8 * 128 * 4 and vs == 100 * 8 * 64 * 4
 
 
+def test_small_token_wise_groups(L):
+    # 32 or 64 channels per group only when K and V are both token-wise, contiguous
+    for gsz in (32, 64):
+        assert kvq.kvq_check_format(kvq.make_format(2, "token", "token", 2, group=gsz)) == OK
+        assert kvq.kvq_check_format(kvq.make_format(4, "channel", "token", 2, group=gsz)) == BADFMT
+        assert kvq.kvq_check_format(kvq.make_format(4, "token", "channel", 2, group=gsz)) == BADFMT
+        assert kvq.kvq_check_format(kvq.make_format(2, "token", "token", 2, group=gsz,
+                                                    page_size=64)) == BADFMT
+        kc, vc, ks, vs = kvq.kvq_cache_sizes(kvq.make_format(4, "token", "token", 2, group=gsz), 3, 1000)
+        assert kc == vc == 3 * 2 * 1024 * 64
+        assert ks == vs == 3 * 2 * 1024 * (128 // gsz) * 4
+    for bad in (16, 96, 256):
+        assert kvq.kvq_check_format(kvq.make_format(2, "token", "token", 2, group=bad)) == BADFMT
+
+
 def test_split_plan_and_workspace(L):
     f = kvq.make_format(2, "channel", "token", 8)
     ns = kvq.kvq_plan_splits(f, 128, 32768)

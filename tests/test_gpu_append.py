@@ -18,19 +18,20 @@ from kvq_testlib import (MAX_ABS_TOL, REL_L2_TOL, SCALE, cache_bytes_equal, gpu_
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("bits,k_axis,v_axis,paged", [(2, "channel", "token", False),
-                                                      (4, "channel", "token", True),
-                                                      (2, "token", "channel", False),
-                                                      (4, "channel", "channel", False),
-                                                      (2, "token", "token", True)])
-def test_append_then_window_decode(bits, k_axis, v_axis, paged):
+@pytest.mark.parametrize("bits,k_axis,v_axis,paged,group", [(2, "channel", "token", False, 128),
+                                                            (4, "channel", "token", True, 128),
+                                                            (2, "token", "channel", False, 128),
+                                                            (4, "channel", "channel", False, 128),
+                                                            (2, "token", "token", True, 128),
+                                                            (4, "token", "token", False, 32)])
+def test_append_then_window_decode(bits, k_axis, v_axis, paged, group):
     import torch
     import bit_quantized_kv_int2_amd as kvq
     B, H, Lmax = 3, 2, 400
     start = [128, 0, 256]   # whole groups packed in bulk first
     total = [300, 130, 383]  # final lengths (window 44, 2, 127 tokens)
     w = synth.Workload("append", B, H, 4 * H, 128, [Lmax] * B, bits, k_axis, v_axis, seed=81,
-                       outliers=True, page_size=64 if paged else 0)
+                       outliers=True, page_size=64 if paged else 0, extra={"group": group})
     kb = synth.f32_to_bf16_bits(w.kv_all("k"))  # the appended tokens are bf16
     vb = synth.f32_to_bf16_bits(w.kv_all("v"))
     kr = synth.bf16_bits_to_f32(kb)
@@ -61,7 +62,7 @@ def test_append_then_window_decode(bits, k_axis, v_axis, paged):
 
     # the cache holds exactly the whole groups, as the bulk rule packs them
     lq = [L - L % 128 for L in total]
-    fo = oracle.fmt_of(w)
+    fo = oracle.fmt_of(w, group)
     orc_cache = oracle.quantize_pack(fo, kr, vr, np.asarray(lq, np.int32), page_table=table,
                                      num_pages=num_pages)
     ok, msg = cache_bytes_equal([c.cpu().numpy() for c in cache], orc_cache)
@@ -86,7 +87,7 @@ def test_append_then_window_decode(bits, k_axis, v_axis, paged):
         torch.cuda.synchronize()
         o = out.cpu().numpy().astype(np.float64)
         e2, ea = rel_l2(o, ref), max_abs(o, ref)
-        print(f"append int{bits} {k_axis[0]}{v_axis[0]} paged={paged} splits {ns}: "
+        print(f"append int{bits} {k_axis[0]}{v_axis[0]} G{group} paged={paged} splits {ns}: "
               f"rel_l2={e2:.3e} max_abs={ea:.3e}")
         assert np.isfinite(o).all()
         assert e2 <= REL_L2_TOL and ea <= MAX_ABS_TOL, (ns, e2, ea)

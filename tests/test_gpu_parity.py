@@ -143,3 +143,24 @@ def test_bf16_output():
     ref = oracle_attention(inp, oracle_pack(inp))
     o = run.decode(out_dtype=torch.bfloat16)
     assert rel_l2(o, ref) <= REL_L2_TOL and max_abs(o, ref) <= MAX_ABS_TOL
+
+
+@pytest.mark.parametrize("bits,group", [(2, 32), (2, 64), (4, 32), (4, 64)])
+def test_token_wise_groups_smaller_than_head_dim(bits, group):
+    """K and V token-wise with 32 or 64 channels per group: each token has
+    128 / G (s, z) pairs per tensor, acc-fold partials are scaled per group,
+    and a split walks several chunks of 2048 * G / 128 tokens."""
+    lens = [3000, 1, 700, 2112, 129]
+    w = synth.Workload("tg", len(lens), 2, 8, 128, lens, bits, "token", "token", seed=91,
+                       outliers=True, extra={"group": group})
+    inp = Inputs(w)
+    inp.k[0, 0, 5, :] = 0.25           # a constant token: every group of it has s = 0
+    inp.v[1, 1, 0, 32:64] = 1.5        # one constant channel group of a token
+    inp.v[0, 1, 2000:2100, 64:] *= 30  # large V scales in some groups of a later chunk
+    run = GpuRun(inp)
+    out, ref = _check(inp, run, label=f"tg_int{bits}_G{group}")
+    for ns in (1, 2):
+        o = run.decode(num_splits=ns)
+        e2, ea = rel_l2(o, ref), max_abs(o, ref)
+        print(f"tg_int{bits}_G{group} splits {ns}: rel_l2={e2:.3e} max_abs={ea:.3e}")
+        assert e2 <= REL_L2_TOL and ea <= MAX_ABS_TOL, (ns, e2, ea)
