@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     p.add_argument("--no-bf16", action="store_true")
     p.add_argument("--no-append", action="store_true", help="skip the append / window timings")
+    p.add_argument("--no-groups", action="store_true",
+                   help="skip the token-wise G = 128 / 64 / 32 timings")
     p.add_argument("--only", choices=["int2", "int4"], default=None,
                    help="time one bit width only (profiling runs)")
     return p.parse_args()
@@ -97,9 +99,11 @@ def time_calls(fn, steps, warmup, stream):
     return per, total_ms
 
 
-def make_inputs(B, L, widths, need_bf16, dev, log=log):
+def make_inputs(B, L, widths, need_bf16, dev, log=log, extra_formats=()):
     """Headline inputs: fp32 K/V drawn per batch row on the host, packed on the
-    GPU into one cache per bit width (and copied to bf16 for the baseline)."""
+    GPU into one cache per bit width (and copied to bf16 for the baseline).
+    extra_formats: (name, bits, k_axis, v_axis, group) caches packed from the
+    same rows."""
     import torch
     import synth
     import bit_quantized_kv_int2_amd as kvq
@@ -109,6 +113,9 @@ def make_inputs(B, L, widths, need_bf16, dev, log=log):
     fmts = {bits: kvq.make_format(bits, "channel", "token", H) for bits in (2, 4)}
     caches = {bits: kvq.cache_tensors(fmts[bits], B, L, device=dev) for bits in widths}
     row_bytes = {bits: kvq.kvq_cache_sizes(fmts[bits], 1, L) for bits in widths}
+    xfmts = {name: kvq.make_format(bits, ka, va, H, group=gsz) for name, bits, ka, va, gsz in extra_formats}
+    xcaches = {name: kvq.cache_tensors(f, B, L, device=dev) for name, f in xfmts.items()}
+    xrow = {name: kvq.kvq_cache_sizes(f, 1, L) for name, f in xfmts.items()}
     if need_bf16:
         kb = torch.empty((B, H, L, D), dtype=torch.bfloat16, device=dev)
         vb = torch.empty((B, H, L, D), dtype=torch.bfloat16, device=dev)
@@ -129,6 +136,9 @@ def make_inputs(B, L, widths, need_bf16, dev, log=log):
         for bits in widths:
             rc = [c[b * n:(b + 1) * n] for c, n in zip(caches[bits], row_bytes[bits])]
             kvq.kv_quantize_pack(fmts[bits], kst, vst, len1, rc, max_len=L)
+        for name, f in xfmts.items():
+            rc = [c[b * n:(b + 1) * n] for c, n in zip(xcaches[name], xrow[name])]
+            kvq.kv_quantize_pack(f, kst, vst, len1, rc, max_len=L)
         if need_bf16:
             kb[b].copy_(kst[0])
             vb[b].copy_(vst[0])
@@ -143,7 +153,7 @@ def make_inputs(B, L, widths, need_bf16, dev, log=log):
 
     kb_vb = (kb, vb) if need_bf16 else None
     return dict(w=w, fmts=fmts, caches=caches, row_bytes=row_bytes, q=q, lens=lens, out=out,
-                bf16=kb_vb)
+                bf16=kb_vb, xfmts=xfmts, xcaches=xcaches)
 
 
 def main():
@@ -166,7 +176,12 @@ def main():
     scale = 1.0 / math.sqrt(D)
     widths = [int(args.only[-1])] if args.only else [2, 4]
     need_bf16 = not args.no_bf16 and args.only is None
-    inp = make_inputs(B, L, widths, need_bf16, dev)
+    extra = []
+    if not args.no_groups and args.only is None:
+        for bits in (2, 4):
+            for gsz in (128, 64, 32):
+                extra.append((f"int{bits}_tt_g{gsz}", bits, "token", "token", gsz))
+    inp = make_inputs(B, L, widths, need_bf16, dev, extra_formats=extra)
     w, fmts, caches, row_bytes = inp["w"], inp["fmts"], inp["caches"], inp["row_bytes"]
     q, lens, out = inp["q"], inp["lens"], inp["out"]
     if need_bf16:
@@ -198,6 +213,24 @@ def main():
             out2 = out.clone()
         else:
             out4 = out.clone()
+
+    # ---- token-wise K and V with 128, 64 or 32 channels per group ------------
+    groups = {}
+    for name, f in inp["xfmts"].items():
+        cache = inp["xcaches"][name]
+        eff = sum(kvq.kvq_cache_sizes(f, B, L))
+
+        def callg():
+            kvq.decode_attention_quant(f, q, cache, lens, L, scale, out)
+
+        per, total_ms = time_calls(callg, args.steps, args.warmup, stream)
+        us = total_ms * 1e3 / args.steps
+        groups[name] = dict(us_per_call=round(us, 2), us_median=round(float(np.median(per)), 2),
+                            effective_bytes=eff, gbs=round(eff / (us * 1e-6) / 1e9, 1),
+                            pct_peak=round(100.0 * eff / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2))
+        log(f"{name}: {us:.1f} us/call, {groups[name]['gbs']:.0f} GB/s effective "
+            f"({groups[name]['pct_peak']:.1f}%)")
+    del inp["xcaches"]
 
     # ---- streaming-read reference over the same byte count (context) --------
     stream_ref = {}
@@ -361,6 +394,7 @@ def main():
         "bf16": bf16,
         "stream_read_reference": {f"int{b}_bytes": v for b, v in stream_ref.items()},
         "append": append,
+        "token_wise_groups": groups or None,
     }
     for b, v in stream_ref.items():
         line[f"int{b}_vs_stream_read"] = round(v["us"] / results[b]["us_per_call"], 4)
