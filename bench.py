@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     p.add_argument("--no-bf16", action="store_true")
     p.add_argument("--no-append", action="store_true", help="skip the append / window timings")
+    p.add_argument("--no-share", action="store_true",
+                   help="skip the one-KV-head (8-way tensor-parallel share) timings")
     p.add_argument("--no-groups", action="store_true",
                    help="skip the token-wise G = 128 / 64 / 32 timings")
     p.add_argument("--only", choices=["int2", "int4"], default=None,
@@ -56,10 +58,10 @@ def parse():
 
 
 def measured_traffic(bits):
-    """HBM bytes per decode call (decode + combine kernels) from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE counters, scaled by what the same
-    counters read for a plain copy; None when the kernel source has changed
-    since the counters were taken."""
+    """HBM bytes per headline decode call (one decode kernel, one split) from
+    the committed rocprofv3 FETCH_SIZE / WRITE_SIZE counters, scaled by what
+    the same counters read for a plain copy; None when the kernel source has
+    changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "decode_headline_hbm_traffic.json")
     try:
@@ -156,6 +158,56 @@ def make_inputs(B, L, widths, need_bf16, dev, log=log, extra_formats=()):
                 bf16=kb_vb, xfmts=xfmts, xcaches=xcaches)
 
 
+def share_timings(B, L, widths, args, dev, stream):
+    """The headline's 8-way tensor-parallel share on this GPU: B sequences x L
+    tokens of ONE KV head and its 4 query heads. With only B units the plan
+    splits each sequence, so this times decode + combine at that shape."""
+    import torch
+    import synth
+    import bit_quantized_kv_int2_amd as kvq
+    w = synth.tp8_share(widths[0])
+    w.batch, w.seq_lens = B, [L] * B
+    fmts = {bits: kvq.make_format(bits, "channel", "token", 1) for bits in widths}
+    caches = {bits: kvq.cache_tensors(fmts[bits], B, L, device=dev) for bits in widths}
+    row = {bits: kvq.kvq_cache_sizes(fmts[bits], 1, L) for bits in widths}
+    offs = w.outlier_offsets()
+    kh = np.empty((1, L, 128), np.float32)
+    vh = np.empty((1, L, 128), np.float32)
+    len1 = torch.tensor([L], dtype=torch.int32, device=dev)
+    for b in range(B):
+        w.kv_row("k", b, offsets=offs, out=kh)
+        w.kv_row("v", b, out=vh)
+        kd = torch.from_numpy(kh)[None].to(dev)
+        vd = torch.from_numpy(vh)[None].to(dev)
+        for bits in widths:
+            rc = [c[b * n:(b + 1) * n] for c, n in zip(caches[bits], row[bits])]
+            kvq.kv_quantize_pack(fmts[bits], kd, vd, len1, rc, max_len=L)
+    q = torch.from_numpy(w.q_bf16().view(np.int16)).to(dev).view(torch.bfloat16)
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    out = torch.empty((B, 4, 128), dtype=torch.float32, device=dev)
+    res = {}
+    for bits in widths:
+        fmt, cache = fmts[bits], caches[bits]
+        ws = kvq.workspace_tensor(fmt, B, L, device=dev)
+        eff = sum(kvq.kvq_cache_sizes(fmt, B, L))
+
+        def call():
+            kvq.decode_attention_quant(fmt, q, cache, lens, L, 1.0 / math.sqrt(128), out,
+                                       workspace=ws)
+
+        per, total_ms = time_calls(call, args.steps, args.warmup, stream)
+        us = total_ms * 1e3 / args.steps
+        gbs = eff / (us * 1e-6) / 1e9
+        res[f"int{bits}"] = dict(us_per_call=round(us, 2), us_median=round(float(np.median(per)), 2),
+                                 effective_bytes=eff, gbs=round(gbs, 1),
+                                 pct_peak=round(100.0 * gbs / PEAK_HBM_GBS, 2),
+                                 num_splits=kvq.kvq_plan_splits(fmt, B, L))
+        log(f"TP-8 share INT{bits}: {us:.1f} us/call, {gbs:.0f} GB/s "
+            f"({100 * gbs / PEAK_HBM_GBS:.1f}%), splits {res[f'int{bits}']['num_splits']}")
+    res["shape"] = f"B={B} x {L} tokens, 1 KV head x 4 query heads (decode + combine)"
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -219,9 +271,10 @@ def main():
     for name, f in inp["xfmts"].items():
         cache = inp["xcaches"][name]
         eff = sum(kvq.kvq_cache_sizes(f, B, L))
+        wsg = kvq.workspace_tensor(f, B, L, device=dev)
 
         def callg():
-            kvq.decode_attention_quant(f, q, cache, lens, L, scale, out)
+            kvq.decode_attention_quant(f, q, cache, lens, L, scale, out, workspace=wsg)
 
         per, total_ms = time_calls(callg, args.steps, args.warmup, stream)
         us = total_ms * 1e3 / args.steps
@@ -231,6 +284,8 @@ def main():
         log(f"{name}: {us:.1f} us/call, {groups[name]['gbs']:.0f} GB/s effective "
             f"({groups[name]['pct_peak']:.1f}%)")
     del inp["xcaches"]
+
+    share = None if args.no_share or args.only else share_timings(B, L, widths, args, dev, stream)
 
     # ---- streaming-read reference over the same byte count (context) --------
     stream_ref = {}
@@ -395,6 +450,7 @@ def main():
         "stream_read_reference": {f"int{b}_bytes": v for b, v in stream_ref.items()},
         "append": append,
         "token_wise_groups": groups or None,
+        "tp8_share": share,
     }
     for b, v in stream_ref.items():
         line[f"int{b}_vs_stream_read"] = round(v["us"] / results[b]["us_per_call"], 4)

@@ -162,8 +162,8 @@ def cache_tensors(fmt: Format, batch: int, max_len: int, num_pages: int = 0, dev
 
 
 def workspace_tensor(fmt: Format, batch: int, max_len: int, num_splits: int = 0, device="cuda"):
-    """Zero-filled workspace for decode calls (its arrival counters must start
-    at zero; each call leaves them zero again)."""
+    """Zero-filled workspace for decode calls: the per-split partials (m, l, O)
+    that the combine kernel merges."""
     import torch
     ws = kvq_workspace_size(fmt, batch, max_len, num_splits)
     return torch.zeros(max(ws, 16), dtype=torch.uint8, device=device)

@@ -15,6 +15,12 @@ static kvq_status hip_status(hipError_t e) {
   return KVQ_ERR_HIP;
 }
 
+// The launches below report hipGetLastError() after each kernel. That state is
+// per thread and shared with every other HIP user in the process, so a
+// failure another library left unread (a device query, say) would be blamed
+// on this call's launch. Each entry point clears it right before launching.
+static void clear_stale_error() { (void)hipGetLastError(); }
+
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 extern "C" {
@@ -204,6 +210,7 @@ kvq_status kv_quantize_pack(const kvq_format* f, const float* k, const float* v,
   a.v_words = (uint32_t*)out->v_codes;
   a.k_sz = (uint16_t*)out->k_scale_offset;
   a.v_sz = (uint16_t*)out->v_scale_offset;
+  clear_stale_error();
   return hip_status(launch_pack(a, (hipStream_t)stream));
 }
 
@@ -265,6 +272,7 @@ kvq_status decode_attention_quant(const kvq_format* f, const void* q, const kvq_
     a.part_ml = a.part_o + rows * nsplit * kHeadDim;
   }
   hipStream_t s = (hipStream_t)stream;
+  clear_stale_error();
   st = hip_status(launch_decode_quant(*f, a, s));
   if (st != KVQ_OK || nsplit == 1) return st;
   return hip_status(launch_combine(a.part_o, a.part_ml, batch * f->num_q_heads, nsplit, out,
@@ -320,6 +328,7 @@ kvq_status decode_attention_bf16(const kvq_format* f, const void* q, const void*
     a.part_ml = a.part_o + rows * nsplit * kHeadDim;
   }
   hipStream_t s = (hipStream_t)stream;
+  clear_stale_error();
   st = hip_status(launch_decode_bf16(a, s));
   if (st != KVQ_OK || nsplit == 1) return st;
   return hip_status(launch_combine(a.part_o, a.part_ml, batch * f->num_q_heads, nsplit, out,
@@ -362,6 +371,7 @@ kvq_status kv_append(const kvq_format* f, const void* k_new, const void* v_new,
   a.v_words = (uint32_t*)cache->v_codes;
   a.k_sz = (uint16_t*)cache->k_scale_offset;
   a.v_sz = (uint16_t*)cache->v_scale_offset;
+  clear_stale_error();
   return hip_status(launch_append(a, (hipStream_t)stream));
 }
 
@@ -435,6 +445,7 @@ kvq_status decode_attention_quant_window(const kvq_format* f, const void* q,
   a.part_ml = part_ml;
   a.part_stride = slots;
   a.len_mode = 1;  // whole groups from the cache
+  clear_stale_error();
   st = hip_status(launch_decode_quant(*f, a, s));
   if (st != KVQ_OK) return st;
 
@@ -467,6 +478,7 @@ kvq_status kvq_stream_read(const void* data, size_t bytes, uint32_t* sink, void*
   if (!aligned16(data) || ((uintptr_t)sink & 3u)) return KVQ_ERR_MISALIGNED;
   if (bytes % 16 != 0) return KVQ_ERR_BAD_SHAPE;
   if (bytes == 0) return KVQ_OK;
+  clear_stale_error();
   return hip_status(launch_stream_read(data, bytes, sink, (hipStream_t)stream));
 }
 

@@ -192,6 +192,14 @@ def headline(bits: int, k_axis="channel", v_axis="token") -> Workload:
                     bits, k_axis, v_axis, seed=3, outliers=True)
 
 
+def tp8_share(bits: int) -> Workload:
+    """One GPU's share of the headline under 8-way tensor parallelism: the same
+    128 sequences x 32768 tokens, but one KV head and its 4 query heads.
+    Own seed (6), same distribution as the headline."""
+    return Workload(f"tp8_share_int{bits}", 128, 1, 4, 128, [32768] * 128, bits, "channel", "token",
+                    seed=6, outliers=True)
+
+
 def paged_long(layer: int, n_seq: int = 64, lo: int = 1024, hi: int = 131072) -> Workload:
     """64 sequences, lengths log-uniform in [1K, 128K], 64-token pages in one pool,
     layers alternate INT4, INT2, INT4, INT2; K channel-wise / V token-wise."""

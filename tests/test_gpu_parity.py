@@ -8,8 +8,8 @@ import numpy as np
 import pytest
 
 import synth
-from kvq_testlib import (MAX_ABS_TOL, REL_L2_TOL, GpuRun, Inputs, cache_bytes_equal, max_abs,
-                         oracle_attention, oracle_pack, rel_l2)
+from kvq_testlib import (MAX_ABS_TOL, REL_L2_TOL, SCALE, GpuRun, Inputs, cache_bytes_equal,
+                         max_abs, oracle_attention, oracle_pack, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -164,3 +164,38 @@ def test_token_wise_groups_smaller_than_head_dim(bits, group):
         e2, ea = rel_l2(o, ref), max_abs(o, ref)
         print(f"tg_int{bits}_G{group} splits {ns}: rel_l2={e2:.3e} max_abs={ea:.3e}")
         assert e2 <= REL_L2_TOL and ea <= MAX_ABS_TOL, (ns, e2, ea)
+
+
+def test_unread_hip_error_from_elsewhere_is_not_blamed():
+    """A failed HIP call made by someone else in this thread (here an invalid
+    device ordinal, which changes nothing) leaves the runtime's last-error state
+    set; the library's pack and decode must still launch and report success.
+    The error is planted right before each library call, after every torch
+    operation (torch checks that state after its own launches too)."""
+    import ctypes
+    import torch
+    hip = ctypes.CDLL("libamdhip64.so")
+    w = synth.tiny_int4()
+    inp = Inputs(w)
+    run = GpuRun(inp)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    ws = run.kvq.workspace_tensor(run.fmt, w.batch, w.max_len)
+    torch.cuda.synchronize()
+
+    def plant():
+        assert hip.hipSetDevice(ctypes.c_int(1 << 20)) != 0
+        if hip.hipPeekAtLastError() == 0:
+            pytest.skip("this runtime keeps no last error for a failed hipSetDevice")
+
+    plant()
+    run.kvq.kv_quantize_pack(run.fmt, run.k, run.v, run.lens, run.cache, max_len=w.max_len)
+    plant()
+    run.kvq.decode_attention_quant(run.fmt, run.q, run.cache, run.lens, w.max_len, SCALE, out,
+                                    workspace=ws)
+    torch.cuda.synchronize()
+    orc_cache = oracle_pack(inp)
+    ok, msg = cache_bytes_equal(run.cache_host(), orc_cache)
+    assert ok, msg
+    ref = oracle_attention(inp, orc_cache)
+    got = out.double().cpu().numpy()
+    assert rel_l2(got, ref) <= REL_L2_TOL and max_abs(got, ref) <= MAX_ABS_TOL

@@ -2,6 +2,7 @@
 oracle recomputes one by one, plus the bf16 baseline kernel.
 
 - headline: B=128 x 32768 tokens, INT4 and INT2 (both fold pairings for INT2);
+- the headline's 8-way tensor-parallel share: one KV head, 4 query heads;
 - paged long context: 64 sequences, log-uniform lengths in [1K, 128K], 64-token
   pages scattered over one pool, four layers INT4, INT2, INT4, INT2 run back to
   back on one stream;
@@ -74,6 +75,20 @@ def test_headline_sampled(bits, k_axis, v_axis):
     got = unit_host_cache(w, oracle.fmt_of(w), cache, b)
     for g, o in zip(got, ref):
         assert np.array_equal(np.ascontiguousarray(g).view(np.uint8), np.ascontiguousarray(o).view(np.uint8))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_tp8_share_sampled(bits):
+    """One KV head per sequence (an 8-way tensor-parallel share of the headline):
+    128 units only, so the automatic plan splits every sequence and the
+    log-sum-exp combine runs at this real shape."""
+    import bit_quantized_kv_int2_amd as kvq
+    w = synth.tp8_share(bits)
+    fmt = gpu_format(w)
+    assert kvq.kvq_plan_splits(fmt, w.batch, w.max_len) > 1
+    cache = pack_rowwise(w, fmt)
+    out = _decode(w, fmt, cache)
+    _check_units(w, cache, out, [(0, 0), (45, 0), (90, 0), (127, 0)], label=w.name)
 
 
 def test_paged_long_context_four_layers():
