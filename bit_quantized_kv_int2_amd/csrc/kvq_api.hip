@@ -91,17 +91,24 @@ kvq_status kvq_cache_sizes(const kvq_format* f, int32_t batch, int32_t max_len,
 
 // Token split per (sequence, KV head): a multiple of kSplitQuantum tokens.
 // A decode work-group walks its split in chunks of kChunkTokens (the fold
-// operands of one chunk sit in LDS), so a split may span the whole sequence;
-// the automatic plan splits only as far as needed for kTargetGroups
-// work-groups over the chip.
-static constexpr long kTargetGroups = 1024;
+// operands of one chunk sit in LDS), so a split may span the whole sequence.
+// The automatic plan splits only as far as needed to give the chip one full
+// round of resident work-groups (`slots`): a second, partial round of short
+// splits costs more than it balances.
+static constexpr long kBf16Slots = 1024;
 
-static int plan_split_tokens(int batch, int num_kv_heads, int max_len, int num_splits) {
+static long quant_slots(const kvq_format* f) {
+  const int per_cu = f->group == kGroup ? groups_per_cu(f->bits, f->v_axis) : kTgGroupsPerCu;
+  return (long)kComputeUnits * per_cu;
+}
+
+static int plan_split_tokens(long slots, int batch, int num_kv_heads, int max_len,
+                             int num_splits) {
   if (max_len <= 0) return kSplitQuantum;
   const int quanta = (max_len + kSplitQuantum - 1) / kSplitQuantum;
   if (num_splits <= 0) {
     const long units = (long)batch * num_kv_heads;
-    long ns = units > 0 ? (kTargetGroups + units - 1) / units : 1;
+    long ns = units > 0 ? (slots + units - 1) / units : 1;
     if (ns > quanta) ns = quanta;
     num_splits = (int)ns;
   }
@@ -120,16 +127,17 @@ kvq_status kvq_plan_splits(const kvq_format* f, int32_t batch, int32_t max_len,
   if (st != KVQ_OK) return st;
   if (!num_splits) return KVQ_ERR_NULL_POINTER;
   if (batch < 0 || max_len < 0) return KVQ_ERR_BAD_SHAPE;
-  *num_splits = splits_for(max_len, plan_split_tokens(batch, f->num_kv_heads, max_len, 0));
+  *num_splits = splits_for(max_len, plan_split_tokens(quant_slots(f), batch, f->num_kv_heads,
+                                                       max_len, 0));
   return KVQ_OK;
 }
 
-static kvq_status resolve_splits(const kvq_format* f, int batch, int max_len, int req,
+static kvq_status resolve_splits(const kvq_format* f, long slots, int batch, int max_len, int req,
                                  int* split_tokens, int* nsplit) {
   if (req < 0) return KVQ_ERR_BAD_SHAPE;
   int quanta = max_len > 0 ? (max_len + kSplitQuantum - 1) / kSplitQuantum : 1;
   if (req > quanta) return KVQ_ERR_BAD_SHAPE;
-  *split_tokens = plan_split_tokens(batch, f->num_kv_heads, max_len, req);
+  *split_tokens = plan_split_tokens(slots, batch, f->num_kv_heads, max_len, req);
   *nsplit = splits_for(max_len, *split_tokens);
   return KVQ_OK;
 }
@@ -146,10 +154,13 @@ kvq_status kvq_workspace_size(const kvq_format* f, int32_t batch, int32_t max_le
   if (st != KVQ_OK) return st;
   if (!bytes) return KVQ_ERR_NULL_POINTER;
   if (batch < 0 || max_len < 0) return KVQ_ERR_BAD_SHAPE;
-  int split_tokens, nsplit;
-  st = resolve_splits(f, batch, max_len, num_splits, &split_tokens, &nsplit);
+  // enough for either decode: the quantised and the bf16 plans may differ
+  int split_tokens, nq, nb;
+  st = resolve_splits(f, quant_slots(f), batch, max_len, num_splits, &split_tokens, &nq);
   if (st != KVQ_OK) return st;
-  *bytes = workspace_bytes_for(f, batch, nsplit);
+  st = resolve_splits(f, kBf16Slots, batch, max_len, num_splits, &split_tokens, &nb);
+  if (st != KVQ_OK) return st;
+  *bytes = workspace_bytes_for(f, batch, nq > nb ? nq : nb);
   return KVQ_OK;
 }
 
@@ -237,7 +248,7 @@ kvq_status decode_attention_quant(const kvq_format* f, const void* q, const kvq_
   if (st != KVQ_OK) return st;
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVQ_ERR_BAD_SHAPE;
   int split_tokens, nsplit;
-  st = resolve_splits(f, batch, max_len, num_splits, &split_tokens, &nsplit);
+  st = resolve_splits(f, quant_slots(f), batch, max_len, num_splits, &split_tokens, &nsplit);
   if (st != KVQ_OK) return st;
   size_t need = workspace_bytes_for(f, batch, nsplit);
   if (need > 0) {
@@ -295,7 +306,7 @@ kvq_status decode_attention_bf16(const kvq_format* f, const void* q, const void*
   if (st != KVQ_OK) return st;
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVQ_ERR_BAD_SHAPE;
   int split_tokens, nsplit;
-  st = resolve_splits(f, batch, max_len, num_splits, &split_tokens, &nsplit);
+  st = resolve_splits(f, kBf16Slots, batch, max_len, num_splits, &split_tokens, &nsplit);
   if (st != KVQ_OK) return st;
   size_t need = workspace_bytes_for(f, batch, nsplit);
   if (need > 0) {
@@ -386,7 +397,7 @@ kvq_status kvq_window_workspace_size(const kvq_format* f, int32_t batch, int32_t
   if (!bytes) return KVQ_ERR_NULL_POINTER;
   if (batch < 0 || max_len < 0) return KVQ_ERR_BAD_SHAPE;
   int split_tokens, nsplit;
-  st = resolve_splits(f, batch, max_len, num_splits, &split_tokens, &nsplit);
+  st = resolve_splits(f, quant_slots(f), batch, max_len, num_splits, &split_tokens, &nsplit);
   if (st != KVQ_OK) return st;
   *bytes = window_workspace_bytes(f, batch, nsplit);
   return KVQ_OK;
@@ -411,7 +422,7 @@ kvq_status decode_attention_quant_window(const kvq_format* f, const void* q,
   if (st != KVQ_OK) return st;
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale)) return KVQ_ERR_BAD_SHAPE;
   int split_tokens, nsplit;
-  st = resolve_splits(f, batch, max_len, num_splits, &split_tokens, &nsplit);
+  st = resolve_splits(f, quant_slots(f), batch, max_len, num_splits, &split_tokens, &nsplit);
   if (st != KVQ_OK) return st;
   const size_t need = window_workspace_bytes(f, batch, nsplit);
   if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;

@@ -223,10 +223,5 @@ __device__ inline int vg_off(int gi, int d) {
   return gi * Lds<KAX, VAX>::VG_GROUP + (d >> 5) * Lds<KAX, VAX>::VG_BLOCK + (d & 31) * 8;
 }
 
-// Work-groups per CU the register allocation targets (4 waves of 256 threads
-// per SIMD leave 128 VGPRs, 3 leave 168): INT2 with token-wise V fits in 128;
-// channel-wise V keeps a second 8-tile accumulator and INT4 twice the codes.
-constexpr int groups_per_cu(int bits, int vax) { return (bits == 2 && vax == KVQ_TOKEN_WISE) ? 4 : 3; }
-
 }  // namespace
 }  // namespace kvq

@@ -15,6 +15,15 @@ constexpr int kGqa = 4;            // query heads per KV head
 constexpr int kPage = 64;          // tokens per page
 constexpr int kSplitQuantum = 256; // split lengths are multiples of this
 constexpr int kChunkTokens = 2048;    // decode prologue chunk: fold operands in LDS
+constexpr int kComputeUnits = 256;    // MI355X
+
+// Resident 256-thread decode work-groups per CU that the register allocation
+// targets (the kernels' launch bounds; 4 leave 128 VGPRs per lane, 3 leave
+// 168): INT2 with token-wise V fits in 128; channel-wise V keeps a second
+// accumulator tile and INT4 twice the codes. The split planner sizes grids
+// by the same numbers.
+constexpr int groups_per_cu(int bits, int vax) { return (bits == 2 && vax == KVQ_TOKEN_WISE) ? 4 : 3; }
+constexpr int kTgGroupsPerCu = 3;     // token-wise groups of 32 / 64 channels
 
 // Launch arguments of the append (one new token per sequence, one layer).
 struct AppendArgs {
