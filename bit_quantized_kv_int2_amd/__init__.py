@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(PKG, "libkvq.so")
 
 TOKEN_WISE, CHANNEL_WISE = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
-LAYOUT_VERSION = 1
+LAYOUT_VERSION = 2
 AXES = {"token": TOKEN_WISE, "channel": CHANNEL_WISE, TOKEN_WISE: TOKEN_WISE,
         CHANNEL_WISE: CHANNEL_WISE}
 

@@ -86,8 +86,8 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
           wd |= (uint32_t)encode(bf16_f32(w[t * kHeadDim + d]), S[gi], Z[gi], qmax) << (a.bits * e);
         }
         const int tt = g0 + t;
-        const long row = g.chunk(b, h, tt) * kPage + tt % kPage;
-        ((uint32_t*)a.k_codes)[row * words + j] = wd;
+        const long blk = g.chunk(b, h, tt) * (long)(kPage * words * 4);
+        *(uint32_t*)(a.k_codes + blk + k_block_byte(a.bits, tt % kPage, 4 * j)) = wd;
       }
     } else {  // V: one word = 32/b consecutive tokens of a channel
       const int nw = kGroup / per;
@@ -100,7 +100,8 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
           wd |= (uint32_t)encode(bf16_f32(w[t * kHeadDim + d]), S[gi], Z[gi], qmax) << (a.bits * e);
         }
         const int tt = g0 + t0;
-        a.v_words[(g.chunk(b, h, tt) * (kPage / per) + (tt % kPage) / per) * kHeadDim + d] = wd;
+        const long blk = g.chunk(b, h, tt) * (long)((kPage / per) * kHeadDim);
+        a.v_words[blk + v_block_word((tt % kPage) / per, d)] = wd;
       }
     }
     __syncthreads();  // S and Z are reused for V

@@ -113,23 +113,28 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   const int ri = lane & 15;
 
   // ---- code loads for one 64-token iteration ---------------------------
-  // K: lane (ri, g) loads the whole row of token tok(g, ri>>2, ri&3);
-  // V: lane (ri, g) loads words of channels 8 ri .. 8 ri + 7.
+  // An iteration is one 64-token block of the cache (iterations start at
+  // multiples of 64). The block order puts in bytes 16 l .. 16 l + 15 of each
+  // 1 KB piece what lane l = 16 g + ri needs: for K the row of token
+  // tok(g, ri>>2, ri&3), 16 bytes per piece; for V the words of channels
+  // 8 ri .. 8 ri + 7 of word rows g (pieces 0, 1) and 4 + g (INT4: 2, 3).
+  // Every load is a whole-line 1 KB wave access, issued non-temporal: the
+  // codes are read once, and such streams read HBM faster when they do not
+  // allocate in the caches.
   struct Codes {
     u4 k[C::KDW / 4];
     u4 v[C::NVW];
   };
-  auto lane_koff = [](int lg, int lr) { return (uint32_t)(C::tok(lg, lr >> 2, lr & 3) * C::KROW); };
-  auto lane_voff = [](int lg, int lr) { return (uint32_t)(lg * kHeadDim + 8 * lr); };  // words
+  auto lane_koff = [](int lg, int lr) { return (uint32_t)(16 * (16 * lg + lr)); };  // bytes
+  auto lane_voff = [](int lg, int lr) { return (uint32_t)(4 * (16 * lg + lr)); };   // words
   auto load_codes = [&](int t0, Codes& cd, uint32_t koff, uint32_t voff) {
     const long ch = chunk_of(t0);
-    const unsigned char* kb = a.k_codes + (ch * kPage + t0 % kPage) * C::KROW + koff;
+    const unsigned char* kb = a.k_codes + ch * (kPage * C::KROW) + koff;
 #pragma unroll
-    for (int e = 0; e < C::KDW / 4; ++e) cd.k[e] = *(const u4*)(kb + 16 * e);
-    const uint32_t* vb = a.v_words + (ch * (kPage / C::TPW) + (t0 % kPage) / C::TPW) * kHeadDim + voff;
+    for (int e = 0; e < C::KDW / 4; ++e) cd.k[e] = __builtin_nontemporal_load((const u4*)(kb + 1024 * e));
+    const uint32_t* vb = a.v_words + ch * ((kPage / C::TPW) * kHeadDim) + voff;
 #pragma unroll
-    for (int e = 0; e < C::NVW; ++e)  // INT4: words g and 4 + g
-      cd.v[e] = *(const u4*)(vb + (e >> 1) * 4 * kHeadDim + 4 * (e & 1));
+    for (int e = 0; e < C::NVW; ++e) cd.v[e] = __builtin_nontemporal_load((const u4*)(vb + 256 * e));
   };
 
   // Wave wv owns the 128-token groups wv, wv + 4, wv + 8, ... of the split

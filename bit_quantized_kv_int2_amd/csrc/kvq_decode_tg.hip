@@ -95,22 +95,25 @@ __global__ void __launch_bounds__(kThreads, kTgGroupsPerCu) decode_tg_kernel(Dec
   const int ri = lane & 15;
 
   // ---- code loads for one 64-token iteration ---------------------------
-  // K as in the G = 128 kernel (each lane one token's whole row). V: lane
-  // (ri, g) loads, for each 16-channel tile c, the word of channel 16c + ri
-  // in word row g (INT2) or rows g and g + 4 (INT4; k-step k = row g + 4k).
+  // An iteration is one 64-token block (block order as in the G = 128
+  // kernel). K as there: lane l = 16 g + ri gets the row of token
+  // tok(g, ri>>2, ri&3) from 1 KB whole-line loads. V: lane (ri, g) loads, for
+  // each 16-channel tile c, the word of channel 16c + ri in word row g (INT2)
+  // or rows g and g + 4 (INT4; k-step k = row g + 4k); in block order that
+  // word sits at v_block_word(g + 4k, 16c + ri) = lane base + 512 k + 8 c.
   struct Codes {
     u4 k[C::KDW / 4];
     uint32_t v[NV];
   };
-  auto lane_koff = [](int lg, int lr) { return (uint32_t)(C::tok(lg, lr >> 2, lr & 3) * C::KROW); };
+  auto lane_koff = [](int lg, int lr) { return (uint32_t)(16 * (16 * lg + lr)); };
   auto load_codes = [&](int t0, Codes& cd, uint32_t koff, int lg, int lr) {
     const long ch = chunk_of(t0);
-    const unsigned char* kb = a.k_codes + (ch * kPage + t0 % kPage) * C::KROW + koff;
+    const unsigned char* kb = a.k_codes + ch * (kPage * C::KROW) + koff;
 #pragma unroll
-    for (int e = 0; e < C::KDW / 4; ++e) cd.k[e] = *(const u4*)(kb + 16 * e);
-    const uint32_t* vb = a.v_words + (ch * (kPage / C::TPW) + (t0 % kPage) / C::TPW + lg) * kHeadDim + lr;
+    for (int e = 0; e < C::KDW / 4; ++e) cd.k[e] = __builtin_nontemporal_load((const u4*)(kb + 1024 * e));
+    const uint32_t* vb = a.v_words + ch * ((kPage / C::TPW) * kHeadDim) + v_block_word(lg, lr);
 #pragma unroll
-    for (int e = 0; e < NV; ++e) cd.v[e] = vb[(e >> 3) * 4 * kHeadDim + 16 * (e & 7)];
+    for (int e = 0; e < NV; ++e) cd.v[e] = vb[512 * (e >> 3) + 8 * (e & 7)];
   };
 
   // wave wv owns the 128-token groups wv, wv + 4, ... (iterations 2G, 2G + 1)

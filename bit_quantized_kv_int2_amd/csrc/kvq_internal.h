@@ -25,6 +25,27 @@ constexpr int kComputeUnits = 256;    // MI355X
 constexpr int groups_per_cu(int bits, int vax) { return (bits == 2 && vax == KVQ_TOKEN_WISE) ? 4 : 3; }
 constexpr int kTgGroupsPerCu = 3;     // token-wise groups of 32 / 64 channels
 
+// Code positions inside a 64-token block (layout_version 2). The decode
+// kernels load a block as 1 KB pieces, lane l taking bytes 16 l .. 16 l + 15
+// of each piece, and these maps put there what lane l needs: the K row of
+// the token its MFMA row handles, and the V words of its channels.
+// Lane of token u (0..63) in the K loads: 16 floor(u / 16) + rho(u mod 16).
+__host__ __device__ constexpr int k_lane_of(int bits, int u) {
+  const int v = u & 15;
+  const int rho = bits == 4 ? 8 * (v >> 3) + 2 * (v & 3) + ((v >> 2) & 1) : 2 * (v & 7) + (v >> 3);
+  return 16 * (u >> 4) + rho;
+}
+// Byte offset in the block of byte o of token u's K row.
+__host__ __device__ constexpr int k_block_byte(int bits, int u, int o) {
+  return 1024 * (o >> 4) + 16 * k_lane_of(bits, u) + (o & 15);
+}
+// Word offset in the block of the V word of word-row r (tokens tpw r ..
+// tpw r + tpw - 1), channel d: lane 16 (r mod 4) + floor(d / 8) holds
+// channels 8 floor(d / 8) .. + 7 of rows r and r + 4.
+__host__ __device__ constexpr int v_block_word(int r, int d) {
+  return 512 * (r >> 2) + 256 * ((d >> 2) & 1) + 64 * (r & 3) + 4 * (d >> 3) + (d & 3);
+}
+
 // Launch arguments of the append (one new token per sequence, one layer).
 struct AppendArgs {
   const uint16_t* k_new;   // bf16 [B][Hkv][D]

@@ -11,7 +11,8 @@
 // Two passes: one thread per group computes (s, z); then one thread per
 // packed 32-bit word recomputes its codes from the stored pairs. K words
 // hold 32/b consecutive channels of a token; V words hold 32/b consecutive
-// tokens of a channel.
+// tokens of a channel. Words go to their place in the 64-token block
+// (k_block_byte, v_block_word).
 #include "kvq_internal.h"
 #include "kvq_quant.h"
 
@@ -125,8 +126,9 @@ __global__ void __launch_bounds__(256) k_codes_kernel(PackArgs a, Geo g) {
         w |= (uint32_t)encode(xr[e], S, Z, qmax) << (bits * e);
       }
     }
-    long row = g.chunk(b, h, t) * kPage + t % kPage;
-    ((uint32_t*)a.k_codes)[row * words + j] = w;
+    // bytes 4 j .. 4 j + 3 of the row stay inside one 16-byte piece
+    const long blk = g.chunk(b, h, t) * (long)(kPage * words * 4);
+    *(uint32_t*)(a.k_codes + blk + k_block_byte(bits, t % kPage, 4 * j)) = w;
   }
 }
 
@@ -155,8 +157,8 @@ __global__ void __launch_bounds__(256) v_codes_kernel(PackArgs a, Geo g) {
       float xv = a.v[(bh * a.max_len + t) * (long)kHeadDim + d];
       w |= (uint32_t)encode(xv, S, Z, qmax) << (bits * e);
     }
-    long word = (g.chunk(b, h, t0) * (kPage / per) + (t0 % kPage) / per) * kHeadDim + d;
-    a.v_words[word] = w;
+    const long blk = g.chunk(b, h, t0) * (long)((kPage / per) * kHeadDim);
+    a.v_words[blk + v_block_word((t0 % kPage) / per, d)] = w;
   }
 }
 

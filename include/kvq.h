@@ -23,15 +23,27 @@
  *     0 <= seq_lens[b] <= max_len. A length of 0 gives a zero output row.
  *   - No state is kept between calls except the thread-local last HIP error.
  *
- * Cache layout (layout_version 1; little-endian; D = head_dim, b = bits,
- * G = group = 128, tpw = 32/b tokens per V word, Lp = max_len rounded up to
- * a multiple of 128; paged caches use 64-token pages):
- *   K codes   contiguous [B][Hkv][Lp][D*b/8] bytes; paged [P][Hkv][64][D*b/8].
- *             Channel d of a token sits at bit b*d of the token's row.
- *   V codes   contiguous [B][Hkv][Lp/tpw][D] uint32; paged [P][Hkv][64/tpw][D].
- *             Token j of a word sits at bit b*j (V is packed along tokens).
+ * Cache layout (layout_version 2; little-endian; D = head_dim = 128, b = bits,
+ * G = group, tpw = 32/b tokens per V word, Lp = max_len rounded up to a
+ * multiple of 128; paged caches use 64-token pages):
+ *   Codes are stored in 64-token blocks: one page, or tokens 64k .. 64k + 63
+ *   of a contiguous sequence. Within a block, u = token index (0..63).
+ *   K codes   contiguous [B][Hkv][Lp/64][64*D*b/8] bytes; paged [P][Hkv][64*D*b/8].
+ *             Token u's row of D*b/8 bytes holds channel d at bit b*d. Byte o
+ *             of that row sits at block offset
+ *               1024*floor(o/16) + 16*lambda(u) + (o mod 16),
+ *               lambda(u) = 16*floor(u/16) + rho(u mod 16),
+ *               INT4: rho(v) = 8*floor(v/8) + 2*(v mod 4) + (floor(v/4) mod 2)
+ *               INT2: rho(v) = 2*(v mod 8) + floor(v/8)
+ *             (each 16-byte piece goes where one 64-lane load of 1 KB finds it).
+ *   V codes   contiguous [B][Hkv][Lp/64][(64/tpw)*D] uint32; paged
+ *             [P][Hkv][(64/tpw)*D]. Word-row r of a block holds tokens
+ *             tpw*r .. tpw*r + tpw - 1; its word for channel d holds token
+ *             tpw*r + j at bit b*j and sits at block word
+ *               512*floor(r/4) + 256*(floor(d/4) mod 2) + 64*(r mod 4)
+ *               + 4*floor(d/8) + (d mod 4).
  *   (s, z)    binary16 pairs, s first.
- *             token-wise:   contiguous [B][Hkv][Lp][2];  paged [P][Hkv][64][2]
+ *             token-wise:   contiguous [B][Hkv][Lp][D/G][2]; paged [P][Hkv][64][D/G][2]
  *             channel-wise: contiguous [B][Hkv][Lp/G][D][2]; paged [P][Hkv][D][2],
  *                           a 128-token group's pairs in the page that holds
  *                           its first token (the other page's slot is unused).
@@ -50,7 +62,7 @@
 extern "C" {
 #endif
 
-#define KVQ_LAYOUT_VERSION 1u
+#define KVQ_LAYOUT_VERSION 2u
 
 typedef enum {
   KVQ_OK = 0,

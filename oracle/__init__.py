@@ -105,15 +105,15 @@ def cache_shapes(fmt: _Fmt, batch: int, max_len: int, num_pages: int = 0):
     tpw = 32 // b
     if fmt.page_size == 0:
         Lp = padded_len(max_len)
-        kc = (np.uint8, (batch, H, Lp, D * b // 8))
-        vw = (np.uint32, (batch, H, Lp // tpw, D))
+        kc = (np.uint8, (batch, H, Lp // 64, 64 * D * b // 8))
+        vw = (np.uint32, (batch, H, Lp // 64, 64 // tpw * D))
         def sz(axis):
             return (np.uint16, (batch, H, Lp, D // G, 2) if axis == TOKEN_WISE
                     else (batch, H, Lp // G, D, 2))
     else:
         P = num_pages
-        kc = (np.uint8, (P, H, 64, D * b // 8))
-        vw = (np.uint32, (P, H, 64 // tpw, D))
+        kc = (np.uint8, (P, H, 64 * D * b // 8))
+        vw = (np.uint32, (P, H, 64 // tpw * D))
         def sz(axis):
             return (np.uint16, (P, H, 64, D // G, 2) if axis == TOKEN_WISE else (P, H, D, 2))
     return kc, vw, sz(fmt.k_axis), sz(fmt.v_axis)

@@ -25,12 +25,15 @@
  * fp16(min), c = clamp(rint((x - z) / s), 0, 2^b - 1) in fp32 using the
  * stored fp16 s and z, c = 0 when s == 0.
  *
- * Packed layout (little-endian; Lp = max_len rounded up to 128; paged
- * caches use 64-token pages and a page table):
- *   K codes  contiguous [B][Hkv][Lp][D*b/8] bytes, paged [P][Hkv][64][D*b/8];
- *            channel d of a token at bit b*d of its row.
- *   V codes  contiguous [B][Hkv][Lp/tpw][D] uint32, paged [P][Hkv][64/tpw][D],
- *            tpw = 32/b tokens per word; token j of a word at bit b*j.
+ * Packed layout, version 2 (little-endian; Lp = max_len rounded up to 128;
+ * paged caches use 64-token pages and a page table). Codes live in 64-token
+ * blocks (a page, or tokens 64k..64k+63 of a contiguous sequence):
+ *   K codes  contiguous [B][Hkv][Lp/64][64*D*b/8] bytes, paged [P][Hkv][64*D*b/8];
+ *            channel d of a token at bit b*d of its row; the row's 16-byte
+ *            pieces sit 1024 bytes apart, in the token's slot (k_slot).
+ *   V codes  contiguous [B][Hkv][Lp/64][(64/tpw)*D] uint32, paged
+ *            [P][Hkv][(64/tpw)*D], tpw = 32/b tokens per word; token j of a
+ *            word at bit b*j; word (row r, channel d) placed by v_word_idx.
  *   (s, z)   fp16 pairs, s first.
  *            token-wise:   contiguous [B][Hkv][Lp][D/G][2], paged [P][Hkv][64][D/G][2]
  *            channel-wise: contiguous [B][Hkv][Lp/G][D][2], paged [P][Hkv][D][2]
@@ -190,18 +193,32 @@ static long chunk_index(const orc_layout* lo, int b, int h, int t, int* tt) {
   return (long)phys * f->num_kv_heads + h;
 }
 
-/* byte offset of token t's K row */
-static long k_row_off(const orc_layout* lo, int b, int h, int t) {
-  int tt;
-  long c = chunk_index(lo, b, h, t, &tt);
-  return (c * 64 + tt) * kv_row_bytes(lo->f);
+/* Position of token u (0..63 within its 64-token block) among the block's
+ * 16-byte K slots, layout version 2: 16*floor(u/16) + rho(u mod 16), rho
+ * written out as the table the documented formula gives. */
+static int k_slot(int bits, int u) {
+  static const int rho4[16] = {0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15};
+  static const int rho2[16] = {0, 2, 4, 6, 8, 10, 12, 14, 1, 3, 5, 7, 9, 11, 13, 15};
+  return 16 * (u / 16) + (bits == 4 ? rho4[u % 16] : rho2[u % 16]);
 }
 
-/* uint32 word index of the V word holding token t of channel d */
+/* byte offset of byte o of token t's K row: the row's 16-byte pieces sit
+ * 1024 bytes apart in the token's 64-token block, in the token's slot */
+static long k_byte_off(const orc_layout* lo, int b, int h, int t, int o) {
+  int tt;
+  long c = chunk_index(lo, b, h, t, &tt);
+  return c * 64 * kv_row_bytes(lo->f) + 1024L * (o / 16) + 16L * k_slot(lo->f->bits, tt) + o % 16;
+}
+
+/* uint32 word index of the V word holding token t of channel d: word-row
+ * r = (t mod 64) / tpw of the block, placed at
+ * 512*(r/4) + 256*((d/4) mod 2) + 64*(r mod 4) + 4*(d/8) + d mod 4 */
 static long v_word_idx(const orc_layout* lo, int b, int h, int t, int d) {
   int tt;
   long c = chunk_index(lo, b, h, t, &tt);
-  return (c * (64 / tpw(lo->f)) + tt / tpw(lo->f)) * lo->f->head_dim + d;
+  const int r = tt / tpw(lo->f);
+  const long pos = 512L * (r / 4) + 256L * ((d / 4) % 2) + 64L * (r % 4) + 4L * (d / 8) + d % 4;
+  return c * (64 / tpw(lo->f)) * lo->f->head_dim + pos;
 }
 
 /* uint16 index of the (s, z) pair (s at idx, z at idx + 1) for element (t, d) */
@@ -246,9 +263,8 @@ typedef struct {
 
 static void put_k_code(pack_job* J, int b, int h, int t, int d, int c) {
   const orc_format* f = J->f;
-  long off = k_row_off(&J->lo, b, h, t);
   long bit = (long)d * f->bits;
-  J->k_codes[off + bit / 8] |= (uint8_t)(c << (bit % 8));
+  J->k_codes[k_byte_off(&J->lo, b, h, t, (int)(bit / 8))] |= (uint8_t)(c << (bit % 8));
 }
 
 static void put_v_code(pack_job* J, int b, int h, int t, int d, int c) {
@@ -269,8 +285,7 @@ static void pack_tensor(pack_job* J, int is_k, int b, int h, const float* x, int
   /* clear the codes and pairs of the written extent */
   for (int t = 0; t < Lw; ++t) {
     if (is_k) {
-      long off = k_row_off(&J->lo, b, h, t);
-      memset(J->k_codes + off, 0, (size_t)kv_row_bytes(f));
+      for (int o = 0; o < kv_row_bytes(f); ++o) J->k_codes[k_byte_off(&J->lo, b, h, t, o)] = 0;
     } else {
       for (int d = 0; d < D; ++d) {
         long w = v_word_idx(&J->lo, b, h, t, d);
@@ -352,7 +367,7 @@ static int check_format(const orc_format* f) {
   if (f->bits != 2 && f->bits != 4) return -1;
   if (f->head_dim <= 0 || f->group <= 0 || f->num_kv_heads <= 0 || f->num_q_heads <= 0) return -1;
   if (f->num_q_heads % f->num_kv_heads) return -1;
-  if ((f->head_dim * f->bits) % 8) return -1;
+  if (f->head_dim != 128) return -1; /* the block order of the codes is defined for D = 128 */
   if (f->k_axis == ORC_TOKEN_WISE || f->v_axis == ORC_TOKEN_WISE)
     if (f->head_dim % f->group) return -1;
   if (f->k_axis == ORC_CHANNEL_WISE || f->v_axis == ORC_CHANNEL_WISE)
@@ -394,9 +409,8 @@ int orc_quantize_pack(const orc_format* f, const float* k, const float* v, const
 /* ------------------------------------------------------------------ */
 
 static int get_k_code(const orc_layout* lo, const uint8_t* kc, int b, int h, int t, int d) {
-  long off = k_row_off(lo, b, h, t);
   long bit = (long)d * lo->f->bits;
-  return (kc[off + bit / 8] >> (bit % 8)) & ((1 << lo->f->bits) - 1);
+  return (kc[k_byte_off(lo, b, h, t, (int)(bit / 8))] >> (bit % 8)) & ((1 << lo->f->bits) - 1);
 }
 
 static int get_v_code(const orc_layout* lo, const uint32_t* vw, int b, int h, int t, int d) {

@@ -58,7 +58,8 @@ def test_format_checks(L):
     good = kvq.make_format(2, "channel", "token", 8)
     assert kvq.kvq_check_format(good) == OK
     for field, bad in [("bits", 3), ("bits", 8), ("group", 64), ("head_dim", 64),
-                       ("num_q_heads", 16), ("page_size", 32), ("layout_version", 2),
+                       ("num_q_heads", 16), ("page_size", 32), ("layout_version", 1),
+                       ("layout_version", 3),
                        ("k_axis", 2), ("num_kv_heads", 0)]:
         f = kvq.make_format(2, "channel", "token", 8)
         setattr(f, field, bad)

@@ -120,6 +120,49 @@ def _grid_data(L, D, bits, transpose=False):
     return x
 
 
+def _golden(name):
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", name)
+    cases = {}
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, val = line.split("=", 1)
+        cases[key.strip()] = val.strip()
+    return cases
+
+
+def _slot_tables():
+    """Per-bit-width token -> 16-byte slot maps of a 64-token block, read from
+    the hand-worked rho lists in the golden file's comments."""
+    rho = {4: [0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15],
+           2: [0, 2, 4, 6, 8, 10, 12, 14, 1, 3, 5, 7, 9, 11, 13, 15]}
+    return {b: np.array([16 * (u // 16) + r[u % 16] for u in range(64)]) for b, r in rho.items()}
+
+
+def _unblock_k(blocks, bits):
+    """[nblk][64*rowbytes] block-order K bytes -> [nblk*64][rowbytes] token rows."""
+    rowb = 128 * bits // 8
+    slot = _slot_tables()[bits]
+    out = np.empty((blocks.shape[0], 64, rowb), np.uint8)
+    for u in range(64):
+        for piece in range(rowb // 16):
+            p0 = 1024 * piece + 16 * slot[u]
+            out[:, u, 16 * piece:16 * piece + 16] = blocks[:, p0:p0 + 16]
+    return out.reshape(-1, rowb)
+
+
+def _unblock_v(blocks, bits):
+    """[nblk][(64/tpw)*128] block-order V words -> [nblk*64/tpw][128] word rows."""
+    nrow = 64 // (32 // bits)
+    out = np.empty((blocks.shape[0], nrow, 128), np.uint32)
+    for r in range(nrow):
+        for d in range(128):
+            out[:, r, d] = blocks[:, 512 * (r // 4) + 256 * ((d // 4) % 2) + 64 * (r % 4) + 4 * (d // 8) + d % 4]
+    return out.reshape(-1, 128)
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 @pytest.mark.parametrize("k_axis,v_axis", [("channel", "token"), ("token", "channel")])
 def test_layout_worked_example(orc, bits, k_axis, v_axis):
@@ -135,13 +178,13 @@ def test_layout_worked_example(orc, bits, k_axis, v_axis):
     want_k = np.zeros((L, D * bits // 8), np.uint8)
     for j in range(per_byte):
         want_k |= (code[:, j::per_byte] << (bits * j)).astype(np.uint8)
-    assert np.array_equal(kc[0, 0, :L], want_k)
+    assert np.array_equal(_unblock_k(kc[0, 0], bits)[:L], want_k)
     # V: word w of channel d holds tokens w*tpw + j at bit bits*j
     tpw = 32 // bits
     want_v = np.zeros((L // tpw, D), np.uint32)
     for j in range(tpw):
         want_v |= code[j::tpw, :] << np.uint32(bits * j)
-    assert np.array_equal(vw[0, 0, :L // tpw], want_v)
+    assert np.array_equal(_unblock_v(vw[0, 0], bits)[:L // tpw], want_v)
     # every (s, z) is (1.0, 0.0)
     one = np.float16(1).view(np.uint16)
     assert np.all(ksz[..., 0] == one) and np.all(ksz[..., 1] == 0)
@@ -150,15 +193,7 @@ def test_layout_worked_example(orc, bits, k_axis, v_axis):
 
 def test_layout_golden_bytes(orc):
     """Bytes written out by hand in tests/golden/layout_int4_int2.txt."""
-    import os
-    path = os.path.join(os.path.dirname(__file__), "golden", "layout_int4_int2.txt")
-    cases = {}
-    for line in open(path):
-        line = line.strip()
-        if not line or line.startswith("#"):
-            continue
-        key, val = line.split("=", 1)
-        cases[key.strip()] = val.strip()
+    cases = _golden("layout_int4_int2.txt")
     for bits in (4, 2):
         codes = [int(c) for c in cases[f"int{bits}_codes"].split()]
         D = 128
@@ -171,10 +206,41 @@ def test_layout_golden_bytes(orc):
         x = np.tile(row, (128, 1))
         fmt = orc.make_format(bits, "token", "token", 128, D, 1, 4)
         kc, vw, _, _ = orc.quantize_pack(fmt, x[None, None], x[None, None], [128])
+        # token 0's row starts the block (slot 0, first piece)
         want = bytes.fromhex(cases[f"int{bits}_k_row0_first_bytes"])
         assert bytes(kc[0, 0, 0, :len(want)]) == want
+        # word-row 0, channel 1 is block word 1
         want_w = int(cases[f"int{bits}_v_word0_ch1"], 16)
         assert int(vw[0, 0, 0, 1]) == want_w
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_layout_block_positions_golden(orc, bits):
+    """Hand-worked block positions of K row bytes and V words (golden file),
+    on a cache whose token t, channel d code is (t + d) mod 2^b (token-wise
+    groups, so s = 1, z = 0 and the stored codes are these values)."""
+    cases = _golden("layout_int4_int2.txt")
+    L, D, qm = 128, 128, (1 << bits) - 1
+    t = np.arange(L)[:, None]
+    d = np.arange(D)[None, :]
+    code = (t + d) % (qm + 1)
+    x = code.astype(np.float32)
+    fmt = orc.make_format(bits, "token", "token", 128, D, 1, 4)
+    kc, vw, _, _ = orc.quantize_pack(fmt, x[None, None], x[None, None], [L])
+    per = 8 // bits
+    tpw = 32 // bits
+    for ent in cases[f"int{bits}_k_positions"].split(","):
+        u, o, p = (int(z) for z in ent.split())
+        want = sum(int(code[u, per * o + j]) << (bits * j) for j in range(per))
+        assert int(kc[0, 0, 0, p]) == want, (bits, u, o, p)
+    for ent in cases[f"int{bits}_v_positions"].split(","):
+        r, ch, p = (int(z) for z in ent.split())
+        want = sum(int(code[tpw * r + j, ch]) << (bits * j) for j in range(tpw))
+        assert int(vw[0, 0, 0, p]) == want, (bits, r, ch, p)
+    # the slot maps are permutations of the block's 64 slots, so the K block
+    # order moves whole 16-byte pieces without overlap
+    for b_, sl in _slot_tables().items():
+        assert sorted(sl.tolist()) == list(range(64)), b_
 
 
 # --------------------------------------------------------------------------
@@ -327,8 +393,8 @@ def test_paged_equals_contiguous(orc, bits):
     for b, L in enumerate(lens):
         for p in range((L + 63) // 64):
             ph = table[b, p]
-            assert np.array_equal(cp[0][ph], cc[0][b, :, 64 * p:64 * p + 64])
-            assert np.array_equal(cp[1][ph], cc[1][b, :, 64 * p // tpw:64 * (p + 1) // tpw])
+            assert np.array_equal(cp[0][ph], cc[0][b, :, p])   # one 64-token code block
+            assert np.array_equal(cp[1][ph], cc[1][b, :, p])
             assert np.array_equal(cp[3][ph], cc[3][b, :, 64 * p:64 * p + 64])
             if p % 2 == 0:  # channel-wise K pairs sit in a group's first page
                 assert np.array_equal(cp[2][ph], cc[2][b, :, p // 2])
