@@ -38,7 +38,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=100,
+    p.add_argument("--warmup", type=int, default=300,
                    help="untimed calls first: the chip takes several dozen back-to-back calls "
                         "(tens of ms) to settle at its sustained clocks")
     p.add_argument("--batch", type=int, default=128)

@@ -98,7 +98,7 @@ kvq_status kvq_cache_sizes(const kvq_format* f, int32_t batch, int32_t max_len,
 static constexpr long kBf16Slots = 1024;
 
 static long quant_slots(const kvq_format* f) {
-  const int per_cu = f->group == kGroup ? groups_per_cu(f->bits, f->v_axis) : kTgGroupsPerCu;
+  const int per_cu = f->group == kGroup ? groups_per_cu(f->bits, f->v_axis) : tg_groups_per_cu(f->bits, kHeadDim / f->group);
   return (long)kComputeUnits * per_cu;
 }
 

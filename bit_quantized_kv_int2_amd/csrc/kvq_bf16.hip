@@ -11,6 +11,9 @@
 //     token pairs of one channel into the A operand of 8 channel tiles.
 //   * Online softmax with a lazily moved maximum; the normaliser is summed
 //     from the rounded bf16 probabilities that feed the PV product.
+//   * K and V loads are non-temporal: the cache is streamed once, and such
+//     streams read HBM faster when they do not allocate in the caches (each
+//     K load still covers whole 64-byte halves of the rows it touches).
 #include <math.h>
 
 #include "kvq_internal.h"
@@ -95,12 +98,12 @@ __global__ void __launch_bounds__(kThreads) bf16_kernel(Bf16Args a) {
     for (int T = 0; T < 2; ++T) {
       const long r = row_of(t0 + 8 * (ri >> 2) + 4 * T + (ri & 3));
 #pragma unroll
-      for (int s = 0; s < 4; ++s) x.k[T][s] = *(const u4*)(a.k + r * kHeadDim + 32 * s + 8 * g);
+      for (int s = 0; s < 4; ++s) x.k[T][s] = __builtin_nontemporal_load((const u4*)(a.k + r * kHeadDim + 32 * s + 8 * g));
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const long r = row_of(t0 + 8 * g + j);
-      x.v[j] = *(const u4*)(a.v + r * kHeadDim + 8 * ri);
+      x.v[j] = __builtin_nontemporal_load((const u4*)(a.v + r * kHeadDim + 8 * ri));
     }
   };
 

@@ -44,7 +44,7 @@ struct TgLds {
 };
 
 template <int BITS, int NG>
-__global__ void __launch_bounds__(kThreads, kTgGroupsPerCu) decode_tg_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_tg_kernel(DecodeArgs a) {
   using C = Cfg<BITS>;
   using M = TgLds<BITS, NG>;
   constexpr int G = kHeadDim / NG;   // channels per group

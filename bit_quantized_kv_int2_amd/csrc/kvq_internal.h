@@ -23,7 +23,9 @@ constexpr int kComputeUnits = 256;    // MI355X
 // accumulator tile and INT4 twice the codes. The split planner sizes grids
 // by the same numbers.
 constexpr int groups_per_cu(int bits, int vax) { return (bits == 2 && vax == KVQ_TOKEN_WISE) ? 4 : 3; }
-constexpr int kTgGroupsPerCu = 3;     // token-wise groups of 32 / 64 channels
+// Token-wise groups of 32 / 64 channels: 3 per CU, except INT4 with four
+// groups per token, whose per-group accumulators need the 256 VGPRs of 2.
+constexpr int tg_groups_per_cu(int bits, int ng) { return (bits == 4 && ng == 4) ? 2 : 3; }
 
 // Code positions inside a 64-token block (layout_version 2). The decode
 // kernels load a block as 1 KB pieces, lane l taking bytes 16 l .. 16 l + 15

@@ -1,6 +1,7 @@
-// Streaming-read reference kernel: reads a buffer once with 128-bit loads.
-// It is the practical HBM read ceiling that the decode rates are compared
-// against (same byte count, no arithmetic beyond an XOR per word).
+// Streaming-read reference kernel: reads a buffer once with 128-bit
+// non-temporal loads (as the decode kernels stream their codes). It is the
+// practical HBM read ceiling that the decode rates are compared against
+// (same byte count, no arithmetic beyond an XOR per word).
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -24,7 +25,7 @@ __global__ void __launch_bounds__(kStreamThreads) stream_read_kernel(const u4* _
   for (; i + kStreamUnroll * kStreamThreads <= end; i += kStreamUnroll * kStreamThreads) {
     u4 v[kStreamUnroll];
 #pragma unroll
-    for (int u = 0; u < kStreamUnroll; ++u) v[u] = p[i + u * kStreamThreads + tid];
+    for (int u = 0; u < kStreamUnroll; ++u) v[u] = __builtin_nontemporal_load(p + i + u * kStreamThreads + tid);
 #pragma unroll
     for (int u = 0; u < kStreamUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
