@@ -28,8 +28,9 @@ struct TgLds {
   static constexpr int QS = 0;                               // float q [4][128]
   static constexpr int QB = QS + 4 * 128 * 4;                // u4 q'' [4 heads][18]
   static constexpr int QZ = QB + 4 * HEAD_STRIDE + 16;       // 256 B of zeros, 16 B into a 128-byte line
-  static constexpr int KB = QZ + 256 + 112;                  // float2 (s', z'') [CHUNK tokens][NG]
-  static constexpr int VA = KB + CHUNK * NG * 8;             // float coef [NG][CHUNK], pairs XOR-permuted
+  static constexpr int KB = QZ + 256 + 112;                  // float2 (s', z'') [CHUNK tokens][NG], skewed
+  static constexpr int KB_BYTES = CHUNK * NG * 8 + CHUNK;    // + 16 B per 16-token run
+  static constexpr int VA = KB + KB_BYTES;                   // float coef [NG][CHUNK], pairs XOR-permuted
   static constexpr int VA_GROUP = CHUNK * 4;
   static constexpr int VR = VA + NG * VA_GROUP;              // fp16 offset-tile rows [NG][hi, lo][VR_LO]
   static constexpr int VR_LO = CHUNK + 32;                   // halfwords (lo row 64 B off the hi row's banks)
@@ -41,6 +42,11 @@ struct TgLds {
   static_assert(ML + 4 * 4 * 2 * 4 <= RED, "merge area overlaps reductions");
   static_assert(QB % 128 == 0 && (QZ - QB) % 128 == 16, "bank layout");
   static_assert(KB % 16 == 0 && VA % 16 == 0 && VR % 16 == 0, "alignment");
+  static_assert(3 * TOTAL <= 160 * 1024, "three work-groups per CU");
+  // byte offset of token t's NG (s', z'') pairs: each run of 16 tokens starts
+  // 16 B further into the bank rotation than the last, so the two tokens 16
+  // apart that one 8-lane group of a 128-bit read fetches use different banks
+  __device__ static inline int kb_off(int t) { return t * NG * 8 + 16 * (t >> 4); }
 };
 
 template <int BITS, int NG>
@@ -248,12 +254,12 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
       ((u4*)rh)[pblk] = u4{hi[0], hi[1], hi[2], hi[3]};
       ((u4*)(rh + M::VR_LO))[pblk] = u4{lo[0], lo[1], lo[2], lo[3]};
       // token-wise K: (s', z'') of (token, group pj)
-      float2* ktok = (float2*)(lds + M::KB);
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          ktok[(tb_run[rr] + e) * NG + pj] = make_float2(f16lo(kz[rr][e]) * ktok_sc, f16hi(kz[rr][e]) * alpha);
+          *(float2*)(lds + M::KB + M::kb_off(tb_run[rr] + e) + 8 * pj) =
+              make_float2(f16lo(kz[rr][e]) * ktok_sc, f16hi(kz[rr][e]) * alpha);
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
@@ -302,15 +308,16 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
           const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, s & 1);
           acc[j] = mfma(av, qb[s], acc[j]);
         }
-        const float2* kt = (const float2*)(lds + M::KB);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int t = rel + tk0 + (q4 >> 1) + C::D2 * (q4 & 1);  // S[q4]'s token
+          const float4* kt = (const float4*)(lds + M::KB + M::kb_off(t));  // two groups per float4
           float sv = 0.f;
 #pragma unroll
-          for (int j = 0; j < NG; ++j) {
-            const float2 p = kt[t * NG + j];
-            sv = fmaf(acc[j][q4], p.x, fmaf(p.y, Qs[j], sv));
+          for (int j2 = 0; j2 < NG; j2 += 2) {
+            const float4 p = kt[j2 / 2];
+            sv = fmaf(acc[j2][q4], p.x, fmaf(p.y, Qs[j2], sv));
+            sv = fmaf(acc[j2 + 1][q4], p.z, fmaf(p.w, Qs[j2 + 1], sv));
           }
           S[q4] = sv;
         }
