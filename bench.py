@@ -268,6 +268,28 @@ def main():
         else:
             out4 = out.clone()
 
+    # ---- the fp8-operand q.K^T variant on the same caches --------------------
+    fp8 = {}
+    for bits in widths:
+        fmt, cache = fmts[bits], caches[bits]
+        ws = kvq.workspace_tensor(fmt, B, L, device=dev)
+        eff = sum(kvq.kvq_cache_sizes(fmt, B, L))
+        out8 = torch.empty_like(out)
+
+        def call8():
+            kvq.decode_attention_quant(fmt, q, cache, lens, L, scale, out8, workspace=ws,
+                                       fp8_qk=True)
+
+        per, total_ms = time_calls(call8, args.steps, args.warmup, stream)
+        us = total_ms * 1e3 / args.steps
+        ref16 = out2 if bits == 2 else out4
+        fp8[f"int{bits}"] = dict(us_per_call=round(us, 2), us_median=round(float(np.median(per)), 2),
+                                 gbs=round(eff / (us * 1e-6) / 1e9, 1),
+                                 pct_peak=round(100.0 * eff / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+                                 rel_l2_vs_fp16_path=float((out8 - ref16).norm() / ref16.norm()))
+        log(f"fp8 q.K^T INT{bits}: {us:.1f} us/call ({fp8[f'int{bits}']['pct_peak']:.1f}%), "
+            f"rel-L2 vs fp16-operand path {fp8[f'int{bits}']['rel_l2_vs_fp16_path']:.2e}")
+
     # ---- token-wise K and V with 128, 64 or 32 channels per group ------------
     groups = {}
     for name, f in inp["xfmts"].items():
@@ -453,6 +475,7 @@ def main():
         "append": append,
         "token_wise_groups": groups or None,
         "tp8_share": share,
+        "fp8_qk": fp8 or None,
     }
     for b, v in stream_ref.items():
         line[f"int{b}_vs_stream_read"] = round(v["us"] / results[b]["us_per_call"], 4)

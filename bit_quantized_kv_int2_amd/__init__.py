@@ -83,6 +83,7 @@ def lib():
         L.kv_quantize_pack.argtypes = [FP, _P, _P, _P, _P, _I, _I, _I, ctypes.POINTER(Cache), _P]
         L.decode_attention_quant.argtypes = [FP, _P, ctypes.POINTER(Cache), _P, _P, _I, _I, _I,
                                              ctypes.c_float, _P, _I, _I, _P, ctypes.c_size_t, _P]
+        L.decode_attention_quant_fp8.argtypes = L.decode_attention_quant.argtypes
         L.decode_attention_bf16.argtypes = [FP, _P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_float,
                                             _P, _I, _I, _P, ctypes.c_size_t, _P]
         L.kvq_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
@@ -92,7 +93,8 @@ def lib():
                                                     _I, _I, _I, ctypes.c_float, _P, _I, _I, _P,
                                                     ctypes.c_size_t, _P]
         for fn in ("kvq_check_format", "kvq_cache_sizes", "kvq_plan_splits", "kvq_workspace_size",
-                   "kv_quantize_pack", "decode_attention_quant", "decode_attention_bf16",
+                   "kv_quantize_pack", "decode_attention_quant", "decode_attention_quant_fp8",
+                   "decode_attention_bf16",
                    "kvq_stream_read", "kv_append", "kvq_window_workspace_size",
                    "decode_attention_quant_window"):
             getattr(L, fn).restype = ctypes.c_int
@@ -187,8 +189,10 @@ def kv_quantize_pack(fmt: Format, k, v, seq_lens, cache, page_table=None, max_le
 
 
 def decode_attention_quant(fmt: Format, q, cache, seq_lens, max_len, softmax_scale, out,
-                           page_table=None, num_splits=0, workspace=None, stream=None):
-    """out[B][Hq][D] (fp32 or bf16 tensor) = decode attention of q (bf16) over cache."""
+                           page_table=None, num_splits=0, workspace=None, stream=None,
+                           fp8_qk=False):
+    """out[B][Hq][D] (fp32 or bf16 tensor) = decode attention of q (bf16) over cache.
+    fp8_qk=True calls decode_attention_quant_fp8 (q.K^T on E4M3 operands)."""
     import torch
     _require_gpu(q, seq_lens, out, page_table)
     B = q.shape[0]
@@ -197,11 +201,11 @@ def decode_attention_quant(fmt: Format, q, cache, seq_lens, max_len, softmax_sca
     maxp = 0 if page_table is None else page_table.shape[1]
     od = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
     cs = _cache_struct(cache)
-    _check(lib().decode_attention_quant(ctypes.byref(fmt), _ptr(q), ctypes.byref(cs),
-                                        _ptr(seq_lens), _ptr(page_table), maxp, B, max_len,
-                                        float(softmax_scale), _ptr(out), od, num_splits,
-                                        _ptr(workspace), workspace.numel(), _stream(stream)),
-           "decode_attention_quant")
+    name = "decode_attention_quant_fp8" if fp8_qk else "decode_attention_quant"
+    _check(getattr(lib(), name)(ctypes.byref(fmt), _ptr(q), ctypes.byref(cs),
+                                _ptr(seq_lens), _ptr(page_table), maxp, B, max_len,
+                                float(softmax_scale), _ptr(out), od, num_splits,
+                                _ptr(workspace), workspace.numel(), _stream(stream)), name)
     return out
 
 

@@ -232,14 +232,15 @@ static kvq_status check_out(const void* q, void* out, int32_t out_dtype) {
   return KVQ_OK;
 }
 
-kvq_status decode_attention_quant(const kvq_format* f, const void* q, const kvq_cache* cache,
-                                  const int32_t* seq_lens, const int32_t* page_table,
-                                  int32_t max_pages_per_seq, int32_t batch, int32_t max_len,
-                                  float softmax_scale, void* out, int32_t out_dtype,
-                                  int32_t num_splits, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+static kvq_status decode_quant_impl(const kvq_format* f, const void* q, const kvq_cache* cache,
+                                    const int32_t* seq_lens, const int32_t* page_table,
+                                    int32_t max_pages_per_seq, int32_t batch, int32_t max_len,
+                                    float softmax_scale, void* out, int32_t out_dtype,
+                                    int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                    void* stream, int fp8_qk) {
   kvq_status st = kvq_check_format(f);
   if (st != KVQ_OK) return st;
+  if (fp8_qk && f->group != kGroup) return KVQ_ERR_BAD_FORMAT;
   st = check_out(q, out, out_dtype);
   if (st != KVQ_OK) return st;
   st = check_cache_ptrs(cache);
@@ -277,6 +278,7 @@ kvq_status decode_attention_quant(const kvq_format* f, const void* q, const kvq_
   a.out_bf16 = out_dtype == KVQ_OUT_BF16;
   a.direct_out = nsplit == 1;
   a.part_stride = nsplit;
+  a.fp8_qk = fp8_qk;
   if (nsplit > 1) {
     const size_t rows = (size_t)batch * f->num_q_heads;
     a.part_o = (float*)workspace;
@@ -288,6 +290,28 @@ kvq_status decode_attention_quant(const kvq_format* f, const void* q, const kvq_
   if (st != KVQ_OK || nsplit == 1) return st;
   return hip_status(launch_combine(a.part_o, a.part_ml, batch * f->num_q_heads, nsplit, out,
                                    a.out_bf16, s));
+}
+
+kvq_status decode_attention_quant(const kvq_format* f, const void* q, const kvq_cache* cache,
+                                  const int32_t* seq_lens, const int32_t* page_table,
+                                  int32_t max_pages_per_seq, int32_t batch, int32_t max_len,
+                                  float softmax_scale, void* out, int32_t out_dtype,
+                                  int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return decode_quant_impl(f, q, cache, seq_lens, page_table, max_pages_per_seq, batch, max_len,
+                           softmax_scale, out, out_dtype, num_splits, workspace, workspace_bytes,
+                           stream, 0);
+}
+
+kvq_status decode_attention_quant_fp8(const kvq_format* f, const void* q, const kvq_cache* cache,
+                                      const int32_t* seq_lens, const int32_t* page_table,
+                                      int32_t max_pages_per_seq, int32_t batch, int32_t max_len,
+                                      float softmax_scale, void* out, int32_t out_dtype,
+                                      int32_t num_splits, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return decode_quant_impl(f, q, cache, seq_lens, page_table, max_pages_per_seq, batch, max_len,
+                           softmax_scale, out, out_dtype, num_splits, workspace, workspace_bytes,
+                           stream, 1);
 }
 
 kvq_status decode_attention_bf16(const kvq_format* f, const void* q, const void* k,

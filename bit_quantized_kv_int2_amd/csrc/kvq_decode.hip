@@ -48,7 +48,7 @@ namespace kvq {
 namespace {
 
 
-template <int BITS, int KAX, int VAX, bool PAGED>
+template <int BITS, int KAX, int VAX, bool PAGED, bool FP8>
 __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_kernel(DecodeArgs a) {
   using C = Cfg<BITS>;
   using M = Lds<KAX, VAX>;
@@ -162,8 +162,13 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       const int Eq = exp_above(m);
       const float t = ldexpf(1.f, -Eq);
       _Float16* qh = (_Float16*)(lds + M::QS) + wv * 128;
-      qh[C::qpos(d)] = (_Float16)(q0 * t * C::inv_wd(d));
-      qh[C::qpos(d + 1)] = (_Float16)(q1 * t * C::inv_wd(d + 1));
+      if (FP8) {  // fp8 QK^T: positions and weights of the E4M3 code bytes
+        qh[C::qpos8(d)] = (_Float16)(q0 * t / C::w8(d));
+        qh[C::qpos8(d + 1)] = (_Float16)(q1 * t / C::w8(d + 1));
+      } else {
+        qh[C::qpos(d)] = (_Float16)(q0 * t * C::inv_wd(d));
+        qh[C::qpos(d + 1)] = (_Float16)(q1 * t * C::inv_wd(d + 1));
+      }
       if (lane == 0) redu[wv] = (unsigned)Eq;
     } else {
       qs[wv * 128 + d] = q0;
@@ -178,7 +183,29 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     // token-wise K: q'' = q * 2^-E / w (max |q''| < 2^14), shared by all waves
     const float qmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const int E = exp_above(qmax) - 14;
-    if (tid < 64) {
+    if (tid < 64 && FP8) {
+      // fp8: q * 2^-(E + 6) / w8 (< 2^8) as an E4M3 pair hi + lo / 16, hi in
+      // bytes 0-127 and lo in 128-255 of the head's row; a bf16 q needs at
+      // most 8 significant bits, so hi + lo / 16 is q exactly
+      const float two_mE6 = ldexpf(1.f, -E - 6);
+      const int ck = tid & 15, qh = tid >> 4;
+      uint32_t hw[2], lw[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float x[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int d = C::ch8(ck, t, b);
+          x[b] = qs[qh * 128 + d] * two_mE6 / C::w8(d);
+        }
+        hw[t] = cvt_fp8x2<true>(x[2], x[3], cvt_fp8x2<false>(x[0], x[1], 0u));
+        const f2 h01 = fp8x2_val<false>(hw[t]), h23 = fp8x2_val<true>(hw[t]);
+        lw[t] = cvt_fp8x2<true>((x[2] - h23.x) * 16.f, (x[3] - h23.y) * 16.f,
+                                cvt_fp8x2<false>((x[0] - h01.x) * 16.f, (x[1] - h01.y) * 16.f, 0u));
+      }
+      *(u2*)(lds + M::QB + qh * M::HEAD_STRIDE + 8 * ck) = u2{hw[0], hw[1]};
+      *(u2*)(lds + M::QB + qh * M::HEAD_STRIDE + 128 + 8 * ck) = u2{lw[0], lw[1]};
+    } else if (tid < 64) {
       const float two_mE = ldexpf(1.f, -E);
       const int s = tid & 15, qh = tid >> 4;
       uint32_t wds[4];
@@ -193,7 +220,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     __syncthreads();
   }
   const float ktok_sc = KAX == KVQ_TOKEN_WISE
-      ? alpha * ldexpf(1.f, exp_above(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))) - 14 + 24)
+      ? alpha * ldexpf(1.f, exp_above(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))) - 14 + (FP8 ? 6 : 24))
       : 0.f;
 
   // accumulators: O and X in units of 2^-F, m_run in log2 units
@@ -266,6 +293,20 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr)
         if (tb_run[rr] < ntok) kz[rr] = *(const u4*)ksz_tok(cb + tb_run[rr]);
+    } else if (glive && FP8) {
+      // the 8 channels of B-operand positions 8 ck_s .. + 7: pair e = 2 b + t
+      // is channel ch8(ck_s, t, b)
+      if (BITS == 4) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) kz[hf] = *(const u4*)ksz_chan(cb + gl * kGroup, 8 * ck_s + 4 * hf);
+      } else {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const u2 pr = *(const u2*)ksz_chan(cb + gl * kGroup, C::ch8(ck_s, 0, b));
+          kz[b >> 1][2 * (b & 1)] = pr[0];
+          kz[b >> 1][2 * (b & 1) + 1] = pr[1];
+        }
+      }
     } else if (glive) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) kz[hf] = *(const u4*)ksz_chan(cb + gl * kGroup, C::k_run(ck_s, hf));
@@ -329,7 +370,61 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
                                        s1 != 0.f ? s1 : 1.f, s1 != 0.f ? z1 * __builtin_amdgcn_rcpf(s1) : z1);
       }
     }
-    if (KAX == KVQ_CHANNEL_WISE) {
+    if (KAX == KVQ_CHANNEL_WISE && FP8) {
+      // fp8 QK^T: x = q 2^-Eq / w8 * s 2^(8 - es) (< 2^8; s == 0 counts as
+      // 2^(es - 1), offset weight adjusted to match) as E4M3 hi + lo / 16;
+      // rho8 = w8 (z / s) 2^(es - 8); the offset sum uses the rounded pair,
+      // and S = alpha 2^(es + Eq - 8) acc + alpha 2^Eq sum (hi + lo/16) rho8.
+      const uint32_t mb = row_max_u(max_lo16(kz[0], kz[1]));
+      const int es = (int)(mb >> 10) - 14;
+      const float up = ldexpf(1.f, 8 - es), dn = ldexpf(1.f, es - 8);
+      float sp[8], rho[8];  // index e = 2 b + t
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t pr = kz[e >> 2][e & 3];
+        const float sv = f16lo(pr), zv = f16hi(pr);
+        const bool nz = sv != 0.f;
+        const float wt = (BITS == 2 && (e & 1)) ? 4.f : 1.f;
+        sp[e] = nz ? sv * up : 128.f;
+        rho[e] = zv * (nz ? __builtin_amdgcn_rcpf(sv) * (wt * dn) : wt * (1.f / 128.f));
+      }
+      float2* kb = (float2*)(lds + M::KB);
+      const u4* qh = (const u4*)(lds + M::QS);
+#pragma unroll 1
+      for (int qh_i = 0; qh_i < 4; ++qh_i) {
+        const u4 qv = qh[qh_i * 16 + ck_s];  // positions 8 ck_s + 4 t + b
+        uint32_t hw[2], lw[2];
+        float bias = 0.f;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float x[4];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const uint32_t hv = qv[2 * t + (b >> 1)];
+            x[b] = ((b & 1) ? f16hi(hv) : f16lo(hv)) * sp[2 * b + t];
+          }
+          hw[t] = cvt_fp8x2<true>(x[2], x[3], cvt_fp8x2<false>(x[0], x[1], 0u));
+          const f2 h01 = fp8x2_val<false>(hw[t]), h23 = fp8x2_val<true>(hw[t]);
+          lw[t] = cvt_fp8x2<true>((x[2] - h23.x) * 16.f, (x[3] - h23.y) * 16.f,
+                                  cvt_fp8x2<false>((x[0] - h01.x) * 16.f, (x[1] - h01.y) * 16.f, 0u));
+          const f2 l01 = fp8x2_val<false>(lw[t]), l23 = fp8x2_val<true>(lw[t]);
+          bias = fmaf(fmaf(l01.x, 0.0625f, h01.x), rho[t], bias);
+          bias = fmaf(fmaf(l01.y, 0.0625f, h01.y), rho[2 + t], bias);
+          bias = fmaf(fmaf(l23.x, 0.0625f, h23.x), rho[4 + t], bias);
+          bias = fmaf(fmaf(l23.y, 0.0625f, h23.y), rho[6 + t], bias);
+        }
+        if (glive) {
+          unsigned char* qrow = lds + M::QB + gl * M::GROUP_STRIDE + qh_i * M::HEAD_STRIDE;
+          *(u2*)(qrow + 8 * ck_s) = u2{hw[0], hw[1]};
+          *(u2*)(qrow + 128 + 8 * ck_s) = u2{lw[0], lw[1]};
+        }
+        bias = row_sum(bias);
+        if (glive && ck_s == 0) {
+          const int Eq = (int)redu[qh_i];
+          kb[gl * 4 + qh_i] = make_float2(alpha * ldexpf(1.f, es + Eq - 8), alpha * ldexpf(bias, Eq));
+        }
+      }
+    } else if (KAX == KVQ_CHANNEL_WISE) {
       // s' = s * 2^(14 - es) with every s of the group < 2^es (s' < 2^14), and
       // the offset weight rho' = w * (z / s) * 2^(es - 14); a channel with
       // s == 0 (all codes 0) takes s' = 2^13 and rho' = w * z * 2^-13, which
@@ -445,12 +540,22 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
                                                       mhh * M::HEAD_STRIDE
                                                 : M::QZ));
         f4 c0 = f4{0.f, 0.f, 0.f, 0.f}, c1 = f4{0.f, 0.f, 0.f, 0.f};
+        if (FP8) {
+          // 4 MFMAs of 32 channels per k-group, hi and lo (scale 2^-4) parts
 #pragma unroll
-        for (int s = 0; s < 16; ++s) {
-          const uint32_t w = BITS == 4 ? cur.k[s >> 2][s & 3] : cur.k[s >> 3][(s >> 1) & 3];
-          const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, s & 1);
-          if (s & 1) c1 = mfma(av, qb[s], c1);
-          else c0 = mfma(av, qb[s], c0);
+          for (int j = 0; j < 4; ++j) {
+            const v8i av = unpack_k8<BITS>(cur.k, j);
+            c0 = mfma8(av, cat8(qb[2 * j], qb[2 * j + 1]), c0, kE8M0One);
+            c1 = mfma8(av, cat8(qb[8 + 2 * j], qb[9 + 2 * j]), c1, kE8M0One - 4);
+          }
+        } else {
+#pragma unroll
+          for (int s = 0; s < 16; ++s) {
+            const uint32_t w = BITS == 4 ? cur.k[s >> 2][s & 3] : cur.k[s >> 3][(s >> 1) & 3];
+            const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, s & 1);
+            if (s & 1) c1 = mfma(av, qb[s], c1);
+            else c0 = mfma(av, qb[s], c0);
+          }
         }
         const f4 acc = c0 + c1;
         if (KAX == KVQ_CHANNEL_WISE) {
@@ -657,7 +762,8 @@ __global__ void __launch_bounds__(128) combine_kernel(const float* part_o, const
 template <int BITS, int KAX, int VAX, bool PAGED>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
   dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
-  decode_kernel<BITS, KAX, VAX, PAGED><<<grid, kThreads, 0, s>>>(a);
+  if (a.fp8_qk) decode_kernel<BITS, KAX, VAX, PAGED, true><<<grid, kThreads, 0, s>>>(a);
+  else decode_kernel<BITS, KAX, VAX, PAGED, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -26,8 +26,33 @@ __device__ inline f4 mfma(u4 a, u4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a), as_h8(b), c, 0, 0, 0);
 }
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+// ---- fp8 (OCP E4M3) QK^T operands --------------------------------------
+// An E4M3 byte whose low 4 bits hold n (all other bits 0) is exactly
+// n * 2^-9 (subnormal for n < 8, the first binade above for 8 <= n < 16), so
+// a 2- or 4-bit code masked into its byte, at bit offset 0 or 2 (INT2) or 0
+// (INT4), is a matrix operand with no shift and no base constant.
+typedef int v8i __attribute__((ext_vector_type(8)));
+constexpr int kE8M0One = 127;      // E8M0 scale 2^0
+constexpr int kScaleCodes = 127 + 9;  // A scale 2^9: an A byte n * 2^-9 counts as n
+// 16x16x128 fp8 x fp8 product with per-operand power-of-two scales (one E8M0
+// byte per lane, byte 0 selected)
+__device__ inline f4 mfma8(v8i a, v8i b, f4 c, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kScaleCodes, 0, scale_b);
+}
+__device__ inline v8i cat8(u4 x, u4 y) {
+  return v8i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
+}
+// two fp32 values to E4M3 (round to nearest even) into half HF of `old`
+template <bool HF>
+__device__ inline uint32_t cvt_fp8x2(float a, float b, uint32_t old) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HF);
+}
+// the two E4M3 bytes of half HF of w, as fp32 (exact)
+template <bool HF>
+__device__ inline f2 fp8x2_val(uint32_t w) { return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HF); }
 __device__ inline uint32_t pack_f16x2(float lo, float hi) {
   // v_cvt_pk_f16_f32: both halves rounded to nearest even in one instruction
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{lo, hi}), h2));
@@ -173,7 +198,48 @@ struct Cfg {
   }
   // 1 / weight of channel d's code slot (its bit offset within its byte)
   __device__ static inline float inv_wd(int d) { return 1.0f / (float)(1 << (BITS * (d % SLOTS))); }
+
+  // ---- fp8 QK^T: 4 MFMAs of 32 channels per 128-channel row; MFMA j's A
+  // operand (8 dwords) comes from the row's K words 2j, 2j + 1 (INT2) or
+  // 4j .. 4j + 3 (INT4). INT2: dword D of a word pair holds channels
+  // 16 w + 4 b + m (w = 2j + D/4, m = D%4, byte b) at weight 4^(m&1); INT4:
+  // dword D holds channels 8 w + 2 b + (D&1) (w = 4j + D/2) at weight 1.
+  // Byte position (32 j + 4 D + b) of channel d in that order:
+  __device__ static inline int qpos8(int d) {
+    if (BITS == 4) {
+      const int w = d >> 3, b = (d >> 1) & 3, hf = d & 1;
+      return 32 * (w >> 2) + 4 * (2 * (w & 3) + hf) + b;
+    }
+    const int w = d >> 4, b = (d >> 2) & 3, m = d & 3;
+    return 32 * (w >> 1) + 4 * (4 * (w & 1) + m) + b;
+  }
+  // weight of channel d's byte (2^(2 * (bit offset in byte) / 2) for INT2)
+  __device__ static inline float w8(int d) { return (BITS == 2 && (d & 1)) ? 4.f : 1.f; }
+  // channel at position 8 ck + i (i = 4 t + b) of the B-operand order: the
+  // 8 positions lane ck of a group's prologue converts
+  __device__ static inline int ch8(int ck, int t, int b) {
+    if (BITS == 4) return 8 * ck + 2 * b + t;
+    return 16 * (2 * (ck >> 2) + ((ck & 3) >> 1)) + 4 * b + 2 * (ck & 1) + t;
+  }
 };
+
+// A operand of fp8 QK^T MFMA j from a lane's K row (layout-version-2 pieces:
+// k[p][c] is the row's 32-bit word 4 p + c)
+template <int BITS>
+__device__ inline v8i unpack_k8(const u4* k, int j) {
+  if (BITS == 2) {
+    const uint32_t w0 = k[j >> 1][2 * (j & 1)], w1 = k[j >> 1][2 * (j & 1) + 1];
+    const uint32_t t0 = w0 >> 4, t1 = w1 >> 4;
+    return v8i{(int)(w0 & 0x03030303u), (int)(w0 & 0x0C0C0C0Cu), (int)(t0 & 0x03030303u),
+               (int)(t0 & 0x0C0C0C0Cu), (int)(w1 & 0x03030303u), (int)(w1 & 0x0C0C0C0Cu),
+               (int)(t1 & 0x03030303u), (int)(t1 & 0x0C0C0C0Cu)};
+  }
+  const u4 w = k[j];
+  return v8i{(int)(w[0] & 0x0F0F0F0Fu), (int)((w[0] >> 4) & 0x0F0F0F0Fu),
+             (int)(w[1] & 0x0F0F0F0Fu), (int)((w[1] >> 4) & 0x0F0F0F0Fu),
+             (int)(w[2] & 0x0F0F0F0Fu), (int)((w[2] >> 4) & 0x0F0F0F0Fu),
+             (int)(w[3] & 0x0F0F0F0Fu), (int)((w[3] >> 4) & 0x0F0F0F0Fu)};
+}
 
 // LDS layout (bytes) for one chunk. LDS serves 128 bytes per clock in 32
 // four-byte banks; the q'' rows of the four heads are 288 bytes apart (16 k-steps

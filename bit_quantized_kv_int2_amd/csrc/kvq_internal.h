@@ -97,6 +97,7 @@ struct DecodeArgs {
   int part_stride;         // partial slots per (sequence, query head)
   int part_base;
   int len_mode;            // 0: L = seq_lens[b]; 1: L rounded down to whole 128-token groups
+  int fp8_qk;              // 1: q.K^T on fp8 (E4M3) operands, hi/lo query parts
 };
 
 struct Bf16Args {

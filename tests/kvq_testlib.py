@@ -91,13 +91,14 @@ class GpuRun:
     def cache_host(self):
         return [c.cpu().numpy() for c in self.cache]
 
-    def decode(self, num_splits=0, out_dtype=None):
+    def decode(self, num_splits=0, out_dtype=None, fp8_qk=False):
         import torch
         w = self.inp.w
         out = torch.empty((w.batch, w.num_q_heads, w.head_dim), device=self.q.device,
                           dtype=out_dtype or torch.float32)
         self.kvq.decode_attention_quant(self.fmt, self.q, self.cache, self.lens, w.max_len, SCALE,
-                                        out, page_table=self.table, num_splits=num_splits)
+                                        out, page_table=self.table, num_splits=num_splits,
+                                        fp8_qk=fp8_qk)
         torch.cuda.synchronize()
         return out.float().cpu().numpy().astype(np.float64)
 

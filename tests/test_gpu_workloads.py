@@ -21,7 +21,7 @@ from kvq_testlib import (MAX_ABS_TOL, REL_L2_TOL, SCALE, gpu_format, max_abs, pa
 pytestmark = pytest.mark.gpu
 
 
-def _decode(w, fmt, cache, table=None):
+def _decode(w, fmt, cache, table=None, fp8_qk=False):
     import torch
     import bit_quantized_kv_int2_amd as kvq
     dev = cache[0].device
@@ -29,7 +29,8 @@ def _decode(w, fmt, cache, table=None):
     lens = torch.tensor(w.seq_lens, dtype=torch.int32, device=dev)
     pt = None if table is None else torch.from_numpy(table).to(dev)
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
-    kvq.decode_attention_quant(fmt, q, cache, lens, w.max_len, SCALE, out, page_table=pt)
+    kvq.decode_attention_quant(fmt, q, cache, lens, w.max_len, SCALE, out, page_table=pt,
+                               fp8_qk=fp8_qk)
     return out
 
 
@@ -75,6 +76,17 @@ def test_headline_sampled(bits, k_axis, v_axis):
     got = unit_host_cache(w, oracle.fmt_of(w), cache, b)
     for g, o in zip(got, ref):
         assert np.array_equal(np.ascontiguousarray(g).view(np.uint8), np.ascontiguousarray(o).view(np.uint8))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_headline_sampled_fp8(bits):
+    """The fp8-operand q.K^T variant at the full headline size (its own bound:
+    the same gate), on the same sampled units."""
+    w = synth.headline(bits)
+    fmt = gpu_format(w)
+    cache = pack_rowwise(w, fmt)
+    out = _decode(w, fmt, cache, fp8_qk=True)
+    _check_units(w, cache, out, [(0, 0), (37, 5), (64, 3), (127, 7)], label=w.name + "_fp8")
 
 
 @pytest.mark.parametrize("bits", [2, 4])
