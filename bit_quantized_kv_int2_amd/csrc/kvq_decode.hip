@@ -51,6 +51,9 @@ namespace {
 template <int BITS, int KAX, int VAX, bool PAGED, bool FP8>
 __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_kernel(DecodeArgs a) {
   using C = Cfg<BITS>;
+  // fp8 operands for P.V too (token-wise V): O[0..3] are the four 128-deep
+  // products' accumulators, X[0] the offset sum
+  constexpr bool PV8 = FP8 && VAX == KVQ_TOKEN_WISE;
   using M = Lds<KAX, VAX>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[M::TOTAL];
   float* qs = (float*)(lds + M::QS);
@@ -320,7 +323,8 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       // every scale of this wave's tokens < 2^Fs (scales of 0 are replaced by
       // 1, hence Fs >= 1; bit patterns of scales >= 0 order as values)
       const uint32_t mb = wave_max_u(max_lo16(vz[0], vz[1]));
-      const int Fc = max((int)(mb >> 10) - 14, 1) + kThr - 14;
+      // (fp8 P.V: P'' < 2^8 for E4M3, six binades lower)
+      const int Fc = max((int)(mb >> 10) - 14, 1) + kThr - 14 + (PV8 ? 6 : 0);
       if (cb == tb) {
         F = Fc;
       } else if (Fc > F) {
@@ -342,24 +346,32 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         float cf[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float wt = (float)(1 << (BITS * (e % C::SLOTS)));
+          // weight of the token's code: fp16 subnormal slot, or (fp8 P.V)
+          // its E4M3 byte's bit offset (INT2 tokens 4b + 1, 4b + 3: 4)
+          const float wt = PV8 ? ((BITS == 2 && (e & 1)) ? 4.f : 1.f)
+                               : (float)(1 << (BITS * (e % C::SLOTS)));
           const float sv = f16lo(vz[rr][e]), zv = f16hi(vz[rr][e]);
           const float sg = sv != 0.f ? sv : 1.f;
           cf[e] = sg * (two_mF / wt);
           rw[rr][e] = zv * (__builtin_amdgcn_rcpf(sg) * wt);
         }
         *(float4*)(coef + coef_off<BITS>(tb_run[rr] / 2)) = make_float4(cf[0], cf[1], cf[2], cf[3]);
+        if (PV8)  // fp32 w * rho per token, addressed like coef
+          *(float4*)(lds + M::VR + coef_off<BITS>(tb_run[rr] / 2)) =
+              make_float4(rw[rr][0], rw[rr][1], rw[rr][2], rw[rr][3]);
       }
       // A-operand element 2 m + hf of this block is token run hf, slot m
-      uint32_t hi[4], lo[4];
+      if (!PV8) {
+        uint32_t hi[4], lo[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float a0 = rw[0][m], a1 = rw[1][m];
-        hi[m] = pack_f16x2(a0, a1);
-        lo[m] = pack_f16x2(a0 - f16lo(hi[m]), a1 - f16hi(hi[m]));
+        for (int m = 0; m < 4; ++m) {
+          const float a0 = rw[0][m], a1 = rw[1][m];
+          hi[m] = pack_f16x2(a0, a1);
+          lo[m] = pack_f16x2(a0 - f16lo(hi[m]), a1 - f16hi(hi[m]));
+        }
+        ((u4*)rh)[pblk] = u4{hi[0], hi[1], hi[2], hi[3]};
+        ((u4*)(rh + M::VR_LO))[pblk] = u4{lo[0], lo[1], lo[2], lo[3]};
       }
-      ((u4*)rh)[pblk] = u4{hi[0], hi[1], hi[2], hi[3]};
-      ((u4*)(rh + M::VR_LO))[pblk] = u4{lo[0], lo[1], lo[2], lo[3]};
     } else if (glive) {
       // (sigma, rho) of two channels per float4
 #pragma unroll
@@ -509,6 +521,24 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         const int sg = BITS == 2 ? 2 * k + m2 : 2 * (mg & 1) + m2;
         src[k][m2] = 4 * (mhh + 4 * sq + 16 * sg);  // byte address for ds_bpermute
       }
+    // fp8 P.V: this lane's A row r = mn_ holds head r & 3 for the channel half
+    // (r >> 2) & 1, part hi (r < 8) or lo; its 16 probability bytes come from
+    // four score lanes (ds_bpermute byte addresses asrc), two per dword
+    const int arow_j = (mn_ >> 2) & 1, arow_lo = mn_ >> 3;
+    const int ascale = arow_lo ? kE8M0One - 4 : kE8M0One;
+    int asrc[4];
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      int ls;
+      if (BITS == 2) {
+        const int gi = (qd >> 1) | ((qd & 1) << 1);  // 0, 2, 1, 3
+        ls = (mhh + 4 * mg) + 16 * gi;
+      } else {
+        const int gi = 2 * (mg & 1) + (qd & 1), nq = (mg >> 1) + 2 * (qd >> 1);
+        ls = (mhh + 4 * nq) + 16 * gi;
+      }
+      asrc[qd] = 4 * ls;
+    }
     const _Float16* rbase = (const _Float16*)(lds + M::VR);
     // extra-tile rows: even = hi part, odd = lo part; only rows 0 and 1 of
     // the accumulator are used, the others repeat them
@@ -590,72 +620,114 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
 #pragma unroll
       for (int j = 0; j < 4; ++j) P[j] = exp2_fast(S[j] - m_run);
 
-      // P'' into packed pairs: pk[a] = (token tk0 + a, token tk0 + a + D2)
-      uint32_t pk[2];
-      if (VAX == KVQ_TOKEN_WISE) {
+      if (PV8) {
+        // P'' = P * coef as an E4M3 pair hi + lo / 16 in bytes [jj0, jj1, jj2, jj3]
+        // (tokens tk0, tk0 + D2, tk0 + 1, tk0 + D2 + 1)
         const unsigned char* cf = lds + M::VA;
         const float2 c0 = *(const float2*)(cf + coef_off<BITS>((rel + tk0) / 2));
         const float2 c1 = *(const float2*)(cf + coef_off<BITS>((rel + tk0 + C::D2) / 2));
-        pk[0] = pack_f16x2(P[0] * c0.x, P[1] * c1.x);
-        pk[1] = pack_f16x2(P[2] * c0.y, P[3] * c1.y);
+        const float x0 = P[0] * c0.x, x1 = P[1] * c1.x, x2 = P[2] * c0.y, x3 = P[3] * c1.y;
         lsum += (P[0] + P[1]) + (P[2] + P[3]);
+        const uint32_t hw = cvt_fp8x2<true>(x2, x3, cvt_fp8x2<false>(x0, x1, 0u));
+        const f2 h01 = fp8x2_val<false>(hw), h23 = fp8x2_val<true>(hw);
+        const uint32_t lw = cvt_fp8x2<true>((x2 - h23.x) * 16.f, (x3 - h23.y) * 16.f,
+                                            cvt_fp8x2<false>((x0 - h01.x) * 16.f, (x1 - h01.y) * 16.f, 0u));
+        const f2 l01 = fp8x2_val<false>(lw), l23 = fp8x2_val<true>(lw);
+        // offset sum from the same rounded P'' (consistent offsets)
+        const unsigned char* rb = lds + M::VR;
+        const float2 r0 = *(const float2*)(rb + coef_off<BITS>((rel + tk0) / 2));
+        const float2 r1 = *(const float2*)(rb + coef_off<BITS>((rel + tk0 + C::D2) / 2));
+        float ox = X[0];
+        ox = fmaf(fmaf(l01.x, 0.0625f, h01.x), r0.x, ox);
+        ox = fmaf(fmaf(l01.y, 0.0625f, h01.y), r1.x, ox);
+        ox = fmaf(fmaf(l23.x, 0.0625f, h23.x), r0.y, ox);
+        ox = fmaf(fmaf(l23.y, 0.0625f, h23.y), r1.y, ox);
+        X[0] = ox;
+        // gather the A row: two source dwords per A dword, byte-interleaved
+        uint32_t G[4];
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const uint32_t gh = (uint32_t)__builtin_amdgcn_ds_bpermute(asrc[qd], (int)hw);
+          const uint32_t gl = (uint32_t)__builtin_amdgcn_ds_bpermute(asrc[qd], (int)lw);
+          G[qd] = arow_lo ? gl : gh;
+        }
+        uint32_t hv[4];
+#pragma unroll
+        for (int dw = 0; dw < 4; ++dw)
+          hv[dw] = __builtin_amdgcn_perm(G[2 * (dw >> 1) + 1], G[2 * (dw >> 1)],
+                                         (dw & 1) ? 0x07030602u : 0x05010400u);
+        const v8i av = arow_j ? v8i{0, 0, 0, 0, (int)hv[0], (int)hv[1], (int)hv[2], (int)hv[3]}
+                              : v8i{(int)hv[0], (int)hv[1], (int)hv[2], (int)hv[3], 0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) O[c] = mfma8pv(av, unpack_v8<BITS>(cur.v, c), O[c], ascale);
       } else {
-        pk[0] = pack_f16x2(P[0] * cw[0], P[1] * cw[0]);
-        pk[1] = pack_f16x2(P[2] * cw[1], P[3] * cw[1]);
-      }
-      u4 bp[2];
+        // P'' into packed pairs: pk[a] = (token tk0 + a, token tk0 + a + D2)
+        uint32_t pk[2];
+        if (VAX == KVQ_TOKEN_WISE) {
+          const unsigned char* cf = lds + M::VA;
+          const float2 c0 = *(const float2*)(cf + coef_off<BITS>((rel + tk0) / 2));
+          const float2 c1 = *(const float2*)(cf + coef_off<BITS>((rel + tk0 + C::D2) / 2));
+          pk[0] = pack_f16x2(P[0] * c0.x, P[1] * c1.x);
+          pk[1] = pack_f16x2(P[2] * c0.y, P[3] * c1.y);
+          lsum += (P[0] + P[1]) + (P[2] + P[3]);
+        } else {
+          pk[0] = pack_f16x2(P[0] * cw[0], P[1] * cw[0]);
+          pk[1] = pack_f16x2(P[2] * cw[1], P[3] * cw[1]);
+        }
+        u4 bp[2];
 #pragma unroll
-      for (int k = 0; k < 2; ++k)
+        for (int k = 0; k < 2; ++k)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) bp[k][m] = (uint32_t)__builtin_amdgcn_ds_bpermute(src[k][m >> 1], (int)pk[m & 1]);
+          for (int m = 0; m < 4; ++m) bp[k][m] = (uint32_t)__builtin_amdgcn_ds_bpermute(src[k][m >> 1], (int)pk[m & 1]);
 
-      // PV: 8 channel tiles + the extra tile, 2 k-steps of 32 tokens
-      if (VAX == KVQ_TOKEN_WISE) {
+        // PV: 8 channel tiles + the extra tile, 2 k-steps of 32 tokens
+        if (VAX == KVQ_TOKEN_WISE) {
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+          for (int k = 0; k < 2; ++k) {
 #pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const uint32_t w = BITS == 4 ? cur.v[2 * k + (c >> 2)][c & 3] : cur.v[c >> 2][c & 3];
-            const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
-            O[c] = mfma(av, bp[k], O[c]);
+            for (int c = 0; c < 8; ++c) {
+              const uint32_t w = BITS == 4 ? cur.v[2 * k + (c >> 2)][c & 3] : cur.v[c >> 2][c & 3];
+              const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
+              O[c] = mfma(av, bp[k], O[c]);
+            }
+            const int pos = ((rel / C::TIT) * C::NK + k) * 32;  // wave-uniform part
+            X = mfma(*(const u4*)(rbase + rrow + pos), bp[k], X);
           }
-          const int pos = ((rel / C::TIT) * C::NK + k) * 32;  // wave-uniform part
-          X = mfma(*(const u4*)(rbase + rrow + pos), bp[k], X);
+        } else {
+          f4 G8[8];
+          f4 Xg = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < 8; ++c) G8[c] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+              const uint32_t w = BITS == 4 ? cur.v[2 * k + (c >> 2)][c & 3] : cur.v[c >> 2][c & 3];
+              const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
+              G8[c] = mfma(av, bp[k], G8[c]);
+            }
+            u4 ones = u4{0u, 0u, 0u, 0u};
+            if (mn_ == 0) {
+#pragma unroll
+              for (int m = 0; m < 4; ++m) ones[m] = 0x00010001u << (BITS * (m % C::SLOTS));
+            }
+            Xg = mfma(ones, bp[k], Xg);
+          }
+          // fold this group's partial: O_d += sigma_d (G_d + rho_d * sum P)
+          const float psum = __shfl(Xg[0], mn_);  // row 0 lives in lane group 0
+          const float4* vg = (const float4*)(lds + M::VA + vg_off<KAX, VAX>(gi, 32 * mg));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int c = 0; c < 8; c += 2) {
+              // channels 32g + 8j + c and +1: (sigma, rho, sigma, rho)
+              float4 sr = vg[(8 * j + c) / 2];
+              O[c][j] = fmaf(sr.x, fmaf(sr.y, psum, G8[c][j]), O[c][j]);
+              O[c + 1][j] = fmaf(sr.z, fmaf(sr.w, psum, G8[c + 1][j]), O[c + 1][j]);
+            }
+          }
+          lsum += psum;
         }
-      } else {
-        f4 G8[8];
-        f4 Xg = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) G8[c] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const uint32_t w = BITS == 4 ? cur.v[2 * k + (c >> 2)][c & 3] : cur.v[c >> 2][c & 3];
-            const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
-            G8[c] = mfma(av, bp[k], G8[c]);
-          }
-          u4 ones = u4{0u, 0u, 0u, 0u};
-          if (mn_ == 0) {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) ones[m] = 0x00010001u << (BITS * (m % C::SLOTS));
-          }
-          Xg = mfma(ones, bp[k], Xg);
-        }
-        // fold this group's partial: O_d += sigma_d (G_d + rho_d * sum P)
-        const float psum = __shfl(Xg[0], mn_);  // row 0 lives in lane group 0
-        const float4* vg = (const float4*)(lds + M::VA + vg_off<KAX, VAX>(gi, 32 * mg));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-          for (int c = 0; c < 8; c += 2) {
-            // channels 32g + 8j + c and +1: (sigma, rho, sigma, rho)
-            float4 sr = vg[(8 * j + c) / 2];
-            O[c][j] = fmaf(sr.x, fmaf(sr.y, psum, G8[c][j]), O[c][j]);
-            O[c + 1][j] = fmaf(sr.z, fmaf(sr.w, psum, G8[c + 1][j]), O[c + 1][j]);
-          }
-        }
-        lsum += psum;
       }
       cur = nxt;
     }
@@ -664,7 +736,22 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
 
   // ---- per-wave result: numerator N and normaliser l (same scale) --------
   float lw;
-  if (VAX == KVQ_TOKEN_WISE) {
+  if (PV8) {
+    // C rows 4 g + x of the four products: head x, channel half g & 1, part
+    // g >> 1 (lo rows already scaled by 2^-4): add the lo rows (lane + 32),
+    // then O[c][x] = (sum + offset of head x) * 2^F for channel 8 n + 2 c + (g & 1)
+    lsum = head_sum(lsum);
+    const float offh = head_sum(X[0]);
+    const float sF = ldexpf(1.f, F);
+    float offx[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) offx[x] = __shfl(offh, x);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) O[c][x] = (O[c][x] + __shfl_xor(O[c][x], 32) + offx[x]) * sF;
+    lw = lsum;
+  } else if (VAX == KVQ_TOKEN_WISE) {
     lsum = head_sum(lsum);
     const float off = __shfl(X[0] + X[1], n);
     const float s24 = ldexpf(1.f, F + 24), sF = ldexpf(1.f, F);
@@ -693,7 +780,18 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   for (int w = 0; w < kWaves; ++w) mall = fmaxf(mall, ml[(w * 4 + hh) * 2]);
   const float f = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - mall);
   __syncthreads();
-  if (n < 4) {
+  if (PV8) {
+    float fx[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) fx[x] = __shfl(f, x);  // lane x holds head x
+    if (g < 2) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mo[(wv * 4 + x) * kHeadDim + 8 * n + 2 * c + g] = O[c][x] * fx[x];
+    }
+    if (n < 4 && g == 0) ml[(wv * 4 + n) * 2 + 1] = lw * f;
+  } else if (n < 4) {
     float* dst = mo + (wv * 4 + n) * kHeadDim + 32 * g;
 #pragma unroll
     for (int j = 0; j < 4; ++j)

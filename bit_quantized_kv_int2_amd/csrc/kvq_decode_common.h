@@ -223,6 +223,42 @@ struct Cfg {
   }
 };
 
+// B operand of fp8 P.V MFMA c from a lane's V words (layout version 2: lane
+// (ri, g) holds channels 8 ri + m, m = 4 e + k in v[e][k] for INT2 (word row
+// g, 16 tokens), or m = 4 (e & 1) + k for INT4 (word rows g + 4 (e >> 1), 8
+// tokens each)): bytes 0-15 are the 16 tokens of channel 8 ri + 2c, bytes
+// 16-31 those of channel 8 ri + 2c + 1. INT2 dword D of a half holds token
+// 4 b + D of the word row (byte b) at weight 4^(D&1); INT4 dword 2 s + D'
+// holds token 2 b + D' of word row g + 4 s.
+template <int BITS>
+__device__ inline v8i unpack_v8(const u4* v, int c) {
+  uint32_t d[8];
+#pragma unroll
+  for (int jh = 0; jh < 2; ++jh) {
+    const int m = 2 * c + jh;
+    if (BITS == 2) {
+      const uint32_t w = v[m >> 2][m & 3], t = w >> 4;
+      d[4 * jh] = w & 0x03030303u;
+      d[4 * jh + 1] = w & 0x0C0C0C0Cu;
+      d[4 * jh + 2] = t & 0x03030303u;
+      d[4 * jh + 3] = t & 0x0C0C0C0Cu;
+    } else {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint32_t w = v[2 * s + (m >> 2)][m & 3];
+        d[4 * jh + 2 * s] = w & 0x0F0F0F0Fu;
+        d[4 * jh + 2 * s + 1] = (w >> 4) & 0x0F0F0F0Fu;
+      }
+    }
+  }
+  return v8i{(int)d[0], (int)d[1], (int)d[2], (int)d[3], (int)d[4], (int)d[5], (int)d[6], (int)d[7]};
+}
+// fp8 P.V product: A = probabilities (per-lane scale: 2^0 for hi rows, 2^-4
+// for lo rows), B = codes (2^9)
+__device__ inline f4 mfma8pv(v8i a, v8i b, f4 c, int scale_a) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, kScaleCodes);
+}
+
 // A operand of fp8 QK^T MFMA j from a lane's K row (layout-version-2 pieces:
 // k[p][c] is the row's 32-bit word 4 p + c)
 template <int BITS>

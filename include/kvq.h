@@ -163,18 +163,20 @@ kvq_status decode_attention_quant(const kvq_format* fmt, const void* q, const kv
                                   void* stream);
 
 /*
- * decode_attention_quant_fp8 -- decode_attention_quant with q.K^T on fp8
- * matrix operands (v_mfma_scale_f32_16x16x128_f8f6f4), the analogue of the
- * pages' Blackwell path that injects codes into the low bits of E4M3 / E2M1
- * (rag-lover.com explainer). A K code masked into its byte is the E4M3
- * value code * 2^-9 (exact, codes < 16), so 32 channels of a token enter one
- * 128-deep product and q.K^T takes 8 instead of 16 matrix instructions per
- * 64 tokens, with 40 instead of 72 unpacking instructions (INT2). The query
- * side is an E4M3 pair hi + lo / 16 of q * s (channel-wise K) or q
- * (token-wise K): at least 8 significant bits per element (relative error
- * <= 2^-8, the precision of a bf16 operand), exactly q for token-wise K. The
- * offset term of channel-wise K is summed from the same rounded pair. P.V is
- * unchanged (fp16 operands).
+ * decode_attention_quant_fp8 -- decode_attention_quant on fp8 matrix operands
+ * (v_mfma_scale_f32_16x16x128_f8f6f4), the analogue of the pages' Blackwell
+ * path that injects codes into the low bits of E4M3 / E2M1 (rag-lover.com
+ * explainer). A 2- or 4-bit code masked into its byte is the E4M3 value
+ * code * 2^-9 (exact, codes < 16), so one 128-deep product takes 32 channels
+ * of a token (q.K^T) or 16 tokens of two channels (P.V).
+ *   q.K^T: the query side is an E4M3 pair hi + lo / 16 of q * s
+ *   (channel-wise K) or q (token-wise K): at least 8 significant bits
+ *   (relative error <= 2^-8, the precision of a bf16 operand), exactly q for
+ *   token-wise K; the channel-wise-K offset sum uses the same rounded pair.
+ *   P.V (token-wise V): the probabilities P * s are E4M3 pairs hi + lo / 16
+ *   in the rows of the product (hi and lo rows summed once at the end), the
+ *   offset sum over tokens again from the rounded pair. Channel-wise V keeps
+ *   fp16 P.V operands.
  * Numeric bound: the output meets rel-L2 <= 4e-3 and max-abs <= 2e-2 against
  * the fp64 oracle, the same gate as decode_attention_quant.
  *   Formats with groups of 128 only (others: KVQ_ERR_BAD_FORMAT); all other
