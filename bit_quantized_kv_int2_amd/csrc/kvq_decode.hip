@@ -165,7 +165,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       const int Eq = exp_above(m);
       const float t = ldexpf(1.f, -Eq);
       _Float16* qh = (_Float16*)(lds + M::QS) + wv * 128;
-      if (FP8) {  // fp8 QK^T: positions and weights of the E4M3 code bytes
+      if (FP8) {  // fp8 / fp4 QK^T: positions of the codes' A elements
         qh[C::qpos8(d)] = (_Float16)(q0 * t / C::w8(d));
         qh[C::qpos8(d + 1)] = (_Float16)(q1 * t / C::w8(d + 1));
       } else {
@@ -180,7 +180,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       if (lane == 0) { red[wv] = m; red[20 + wv] = sum; }
     }
   }
-  if (tid < 16) ((u4*)(lds + M::QZ))[tid] = u4{0u, 0u, 0u, 0u};
+  if (tid < M::QZ_BYTES / 16) ((u4*)(lds + M::QZ))[tid] = u4{0u, 0u, 0u, 0u};
   __syncthreads();
   if (KAX == KVQ_TOKEN_WISE) {
     // token-wise K: q'' = q * 2^-E / w (max |q''| < 2^14), shared by all waves
@@ -201,10 +201,10 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
           const int d = C::ch8(ck, t, b);
           x[b] = qs[qh * 128 + d] * two_mE6 / C::w8(d);
         }
-        hw[t] = cvt_fp8x2<true>(x[2], x[3], cvt_fp8x2<false>(x[0], x[1], 0u));
+        hw[t] = cvt_fp8x2<true>(x[2], x[3], cvt_fp8x2<false>(x[0], x[1], any_u32()));
         const f2 h01 = fp8x2_val<false>(hw[t]), h23 = fp8x2_val<true>(hw[t]);
         lw[t] = cvt_fp8x2<true>((x[2] - h23.x) * 16.f, (x[3] - h23.y) * 16.f,
-                                cvt_fp8x2<false>((x[0] - h01.x) * 16.f, (x[1] - h01.y) * 16.f, 0u));
+                                cvt_fp8x2<false>((x[0] - h01.x) * 16.f, (x[1] - h01.y) * 16.f, any_u32()));
       }
       *(u2*)(lds + M::QB + qh * M::HEAD_STRIDE + 8 * ck) = u2{hw[0], hw[1]};
       *(u2*)(lds + M::QB + qh * M::HEAD_STRIDE + 128 + 8 * ck) = u2{lw[0], lw[1]};
@@ -302,13 +302,9 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       if (BITS == 4) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) kz[hf] = *(const u4*)ksz_chan(cb + gl * kGroup, 8 * ck_s + 4 * hf);
-      } else {
+      } else {  // every other channel of 16
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const u2 pr = *(const u2*)ksz_chan(cb + gl * kGroup, C::ch8(ck_s, 0, b));
-          kz[b >> 1][2 * (b & 1)] = pr[0];
-          kz[b >> 1][2 * (b & 1) + 1] = pr[1];
-        }
+        for (int e = 0; e < 8; ++e) kz[e >> 2][e & 3] = *(const uint32_t*)ksz_chan(cb + gl * kGroup, C::ch8(ck_s, e & 1, e >> 1));
       }
     } else if (glive) {
 #pragma unroll
@@ -396,7 +392,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         const uint32_t pr = kz[e >> 2][e & 3];
         const float sv = f16lo(pr), zv = f16hi(pr);
         const bool nz = sv != 0.f;
-        const float wt = (BITS == 2 && (e & 1)) ? 4.f : 1.f;
+        const float wt = C::w8(C::ch8(ck_s, e & 1, e >> 1));
         sp[e] = nz ? sv * up : 128.f;
         rho[e] = zv * (nz ? __builtin_amdgcn_rcpf(sv) * (wt * dn) : wt * (1.f / 128.f));
       }
@@ -415,10 +411,10 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
             const uint32_t hv = qv[2 * t + (b >> 1)];
             x[b] = ((b & 1) ? f16hi(hv) : f16lo(hv)) * sp[2 * b + t];
           }
-          hw[t] = cvt_fp8x2<true>(x[2], x[3], cvt_fp8x2<false>(x[0], x[1], 0u));
+          hw[t] = cvt_fp8x2<true>(x[2], x[3], cvt_fp8x2<false>(x[0], x[1], any_u32()));
           const f2 h01 = fp8x2_val<false>(hw[t]), h23 = fp8x2_val<true>(hw[t]);
           lw[t] = cvt_fp8x2<true>((x[2] - h23.x) * 16.f, (x[3] - h23.y) * 16.f,
-                                  cvt_fp8x2<false>((x[0] - h01.x) * 16.f, (x[1] - h01.y) * 16.f, 0u));
+                                  cvt_fp8x2<false>((x[0] - h01.x) * 16.f, (x[1] - h01.y) * 16.f, any_u32()));
           const f2 l01 = fp8x2_val<false>(lw[t]), l23 = fp8x2_val<true>(lw[t]);
           bias = fmaf(fmaf(l01.x, 0.0625f, h01.x), rho[t], bias);
           bias = fmaf(fmaf(l01.y, 0.0625f, h01.y), rho[2 + t], bias);
@@ -526,6 +522,15 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     // four score lanes (ds_bpermute byte addresses asrc), two per dword
     const int arow_j = (mn_ >> 2) & 1, arow_lo = mn_ >> 3;
     const int ascale = arow_lo ? kE8M0One - 4 : kE8M0One;
+    // v_perm selectors of the A row's two halves: byte-interleave two
+    // gathered dwords (even / odd A dwords), or 0x0C (a zero byte) in every
+    // position for the half of the other channel
+    uint32_t asel[2][2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      asel[hf][0] = hf == arow_j ? 0x05010400u : 0x0C0C0C0Cu;
+      asel[hf][1] = hf == arow_j ? 0x07030602u : 0x0C0C0C0Cu;
+    }
     int asrc[4];
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) {
@@ -570,7 +575,26 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
                                                       mhh * M::HEAD_STRIDE
                                                 : M::QZ));
         f4 c0 = f4{0.f, 0.f, 0.f, 0.f}, c1 = f4{0.f, 0.f, 0.f, 0.f};
-        if (FP8) {
+        if (FP8 && BITS == 2) {
+          // E2M1 codes: the 32 channels of A lane group g pair with the E4M3
+          // bytes of half g >> 1 of lane groups 2 (g & 1) and 2 (g & 1) + 1.
+          // So column (head, q) takes 16 bytes of its q'' row (offset
+          // 16 (mg & 1) in each 32-channel run) into half q >> 1 when
+          // mg >> 1 == q & 1, and zeros everywhere else. Zero reads go to the
+          // bank group next to the rows' (odd or even 16-byte slot).
+          const bool live = (mg >> 1) == (mnq & 1);
+          const unsigned char* qrow = lds + M::QB + (KAX == KVQ_CHANNEL_WISE ? gi : 0) * M::GROUP_STRIDE +
+                                      mhh * M::HEAD_STRIDE + 16 * (mg & 1);
+          const unsigned char* zrow = lds + M::QZ + 112 * (mg & 1);
+          const u4* b0 = (const u4*)(live && mnq < 2 ? qrow : zrow);
+          const u4* b1 = (const u4*)(live && mnq >= 2 ? qrow : zrow);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const v8i av = unpack_k8<BITS>(cur.k, j);
+            c0 = mfma4k(av, cat8(b0[2 * j], b1[2 * j]), c0, kE8M0One);
+            c1 = mfma4k(av, cat8(b0[8 + 2 * j], b1[8 + 2 * j]), c1, kE8M0One - 4);
+          }
+        } else if (FP8) {
           // 4 MFMAs of 32 channels per k-group, hi and lo (scale 2^-4) parts
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -601,7 +625,10 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
           S[3] = fmaf(acc[3], p1.z, p1.w * Qh);  // tk0 + D2 + 1
         }
       }
-      if (t0 + C::TIT > te) {
+      if (t0 + C::TIT > te) {  // the split's partial last iteration only
+        // (an instruction with side effects keeps this a branch: speculated,
+        // the masks would cost 8 vector instructions in every iteration)
+        asm volatile("");
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           if (t0 + tk0 + (j >> 1) + C::D2 * (j & 1) >= te) S[j] = -INFINITY;
@@ -628,10 +655,10 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         const float2 c1 = *(const float2*)(cf + coef_off<BITS>((rel + tk0 + C::D2) / 2));
         const float x0 = P[0] * c0.x, x1 = P[1] * c1.x, x2 = P[2] * c0.y, x3 = P[3] * c1.y;
         lsum += (P[0] + P[1]) + (P[2] + P[3]);
-        const uint32_t hw = cvt_fp8x2<true>(x2, x3, cvt_fp8x2<false>(x0, x1, 0u));
+        const uint32_t hw = cvt_fp8x2<true>(x2, x3, cvt_fp8x2<false>(x0, x1, any_u32()));
         const f2 h01 = fp8x2_val<false>(hw), h23 = fp8x2_val<true>(hw);
         const uint32_t lw = cvt_fp8x2<true>((x2 - h23.x) * 16.f, (x3 - h23.y) * 16.f,
-                                            cvt_fp8x2<false>((x0 - h01.x) * 16.f, (x1 - h01.y) * 16.f, 0u));
+                                            cvt_fp8x2<false>((x0 - h01.x) * 16.f, (x1 - h01.y) * 16.f, any_u32()));
         const f2 l01 = fp8x2_val<false>(lw), l23 = fp8x2_val<true>(lw);
         // offset sum from the same rounded P'' (consistent offsets)
         const unsigned char* rb = lds + M::VR;
@@ -651,13 +678,12 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
           const uint32_t gl = (uint32_t)__builtin_amdgcn_ds_bpermute(asrc[qd], (int)lw);
           G[qd] = arow_lo ? gl : gh;
         }
-        uint32_t hv[4];
+        int hv[8];
 #pragma unroll
-        for (int dw = 0; dw < 4; ++dw)
-          hv[dw] = __builtin_amdgcn_perm(G[2 * (dw >> 1) + 1], G[2 * (dw >> 1)],
-                                         (dw & 1) ? 0x07030602u : 0x05010400u);
-        const v8i av = arow_j ? v8i{0, 0, 0, 0, (int)hv[0], (int)hv[1], (int)hv[2], (int)hv[3]}
-                              : v8i{(int)hv[0], (int)hv[1], (int)hv[2], (int)hv[3], 0, 0, 0, 0};
+        for (int dw = 0; dw < 8; ++dw)
+          hv[dw] = (int)__builtin_amdgcn_perm(G[2 * ((dw >> 1) & 1) + 1], G[2 * ((dw >> 1) & 1)],
+                                              asel[dw >> 2][dw & 1]);
+        const v8i av = v8i{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]};
 #pragma unroll
         for (int c = 0; c < 4; ++c) O[c] = mfma8pv(av, unpack_v8<BITS>(cur.v, c), O[c], ascale);
       } else {

@@ -29,22 +29,37 @@ __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-// ---- fp8 (OCP E4M3) QK^T operands --------------------------------------
+// ---- fp8 (OCP E4M3) and fp4 (OCP E2M1) matrix operands -----------------
 // An E4M3 byte whose low 4 bits hold n (all other bits 0) is exactly
 // n * 2^-9 (subnormal for n < 8, the first binade above for 8 <= n < 16), so
 // a 2- or 4-bit code masked into its byte, at bit offset 0 or 2 (INT2) or 0
-// (INT4), is a matrix operand with no shift and no base constant.
+// (INT4), is a matrix operand with no shift and no base constant. An E2M1
+// nibble whose low 2 bits hold n < 4 is exactly n / 2 (0, 0.5 subnormal, 1,
+// 1.5), so an INT2 code masked into its nibble is one too, at 8 codes per
+// AND (q.K^T of the INT2 cache).
 typedef int v8i __attribute__((ext_vector_type(8)));
 constexpr int kE8M0One = 127;      // E8M0 scale 2^0
 constexpr int kScaleCodes = 127 + 9;  // A scale 2^9: an A byte n * 2^-9 counts as n
+constexpr int kScaleCodes4 = 127 + 1;  // A scale 2^1: an A nibble n / 2 counts as n
 // 16x16x128 fp8 x fp8 product with per-operand power-of-two scales (one E8M0
 // byte per lane, byte 0 selected)
 __device__ inline f4 mfma8(v8i a, v8i b, f4 c, int scale_b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kScaleCodes, 0, scale_b);
 }
+// the same product with A in E2M1 (its first 4 dwords; the rest is ignored).
+// Operand k-order with mixed formats: an E2M1 lane of lane group g holds
+// k = 32 g .. 32 g + 31 in nibble order, while an E4M3 lane of lane group g
+// holds k = 16 g .. 16 g + 15 in bytes 0-15 and k = 64 + 16 g .. in bytes
+// 16-31 (checked on the device with one-hot operands)
+__device__ inline f4 mfma4k(v8i a, v8i b, f4 c, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, kScaleCodes4, 0, scale_b);
+}
 __device__ inline v8i cat8(u4 x, u4 y) {
   return v8i{(int)x[0], (int)x[1], (int)x[2], (int)x[3], (int)y[0], (int)y[1], (int)y[2], (int)y[3]};
 }
+// a value whose bits do not matter (the first of two conversions that
+// together write every byte of a dword): no register has to be cleared
+__device__ inline uint32_t any_u32() { return __builtin_nondeterministic_value(0u); }
 // two fp32 values to E4M3 (round to nearest even) into half HF of `old`
 template <bool HF>
 __device__ inline uint32_t cvt_fp8x2(float a, float b, uint32_t old) {
@@ -199,27 +214,28 @@ struct Cfg {
   // 1 / weight of channel d's code slot (its bit offset within its byte)
   __device__ static inline float inv_wd(int d) { return 1.0f / (float)(1 << (BITS * (d % SLOTS))); }
 
-  // ---- fp8 QK^T: 4 MFMAs of 32 channels per 128-channel row; MFMA j's A
-  // operand (8 dwords) comes from the row's K words 2j, 2j + 1 (INT2) or
-  // 4j .. 4j + 3 (INT4). INT2: dword D of a word pair holds channels
-  // 16 w + 4 b + m (w = 2j + D/4, m = D%4, byte b) at weight 4^(m&1); INT4:
-  // dword D holds channels 8 w + 2 b + (D&1) (w = 4j + D/2) at weight 1.
-  // Byte position (32 j + 4 D + b) of channel d in that order:
+  // ---- fp8 / fp4 QK^T: 4 MFMAs of 32 channels per 128-channel row; MFMA
+  // j's A operand comes from the row's K words 2j, 2j + 1 (INT2, E2M1) or
+  // 4j .. 4j + 3 (INT4, E4M3). INT2: nibble n of dword D holds channel
+  // 16 (2j + D/2) + 2n + (D&1); INT4: byte b of dword D holds channel
+  // 8 w + 2 b + (D&1) (w = 4j + D/2). All at weight 1.
+  // Position of channel d in the q'' row of the B operand: byte 32 j + 4 D + b
+  // (INT4); byte 32 j + 16 p + i pairs with nibble 16 p + i of the INT2 A
+  // lane, i.e. channel 32 j + 16 p + 2 (i % 8) + i / 8 (INT2).
   __device__ static inline int qpos8(int d) {
     if (BITS == 4) {
       const int w = d >> 3, b = (d >> 1) & 3, hf = d & 1;
       return 32 * (w >> 2) + 4 * (2 * (w & 3) + hf) + b;
     }
-    const int w = d >> 4, b = (d >> 2) & 3, m = d & 3;
-    return 32 * (w >> 1) + 4 * (4 * (w & 1) + m) + b;
+    return (d & ~15) + 8 * (d & 1) + ((d & 15) >> 1);
   }
-  // weight of channel d's byte (2^(2 * (bit offset in byte) / 2) for INT2)
-  __device__ static inline float w8(int d) { return (BITS == 2 && (d & 1)) ? 4.f : 1.f; }
+  // weight of channel d's code in its A element (1: every code sits at bit 0)
+  __device__ static inline float w8(int) { return 1.f; }
   // channel at position 8 ck + i (i = 4 t + b) of the B-operand order: the
   // 8 positions lane ck of a group's prologue converts
   __device__ static inline int ch8(int ck, int t, int b) {
     if (BITS == 4) return 8 * ck + 2 * b + t;
-    return 16 * (2 * (ck >> 2) + ((ck & 3) >> 1)) + 4 * b + 2 * (ck & 1) + t;
+    return 16 * (ck >> 1) + 8 * t + 2 * b + (ck & 1);
   }
 };
 
@@ -259,16 +275,15 @@ __device__ inline f4 mfma8pv(v8i a, v8i b, f4 c, int scale_a) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, kScaleCodes);
 }
 
-// A operand of fp8 QK^T MFMA j from a lane's K row (layout-version-2 pieces:
-// k[p][c] is the row's 32-bit word 4 p + c)
+// A operand of fp8 / fp4 QK^T MFMA j from a lane's K row (layout-version-2
+// pieces: k[p][c] is the row's 32-bit word 4 p + c). INT2: E2M1, the even
+// and odd channels of words 2j and 2j + 1 (3 ops per 16 codes); INT4: E4M3.
 template <int BITS>
 __device__ inline v8i unpack_k8(const u4* k, int j) {
   if (BITS == 2) {
     const uint32_t w0 = k[j >> 1][2 * (j & 1)], w1 = k[j >> 1][2 * (j & 1) + 1];
-    const uint32_t t0 = w0 >> 4, t1 = w1 >> 4;
-    return v8i{(int)(w0 & 0x03030303u), (int)(w0 & 0x0C0C0C0Cu), (int)(t0 & 0x03030303u),
-               (int)(t0 & 0x0C0C0C0Cu), (int)(w1 & 0x03030303u), (int)(w1 & 0x0C0C0C0Cu),
-               (int)(t1 & 0x03030303u), (int)(t1 & 0x0C0C0C0Cu)};
+    return v8i{(int)(w0 & 0x33333333u), (int)((w0 >> 2) & 0x33333333u), (int)(w1 & 0x33333333u),
+               (int)((w1 >> 2) & 0x33333333u), 0, 0, 0, 0};
   }
   const u4 w = k[j];
   return v8i{(int)(w[0] & 0x0F0F0F0Fu), (int)((w[0] >> 4) & 0x0F0F0F0Fu),
@@ -289,8 +304,9 @@ struct Lds {
   static constexpr int QS = 0;                                   // float [4][128] / binary16 q
   static constexpr int QB = QS + 4 * 128 * 4;                    // u4 [groups][4 heads][18] (16 used)
   static constexpr int QB_BYTES = (KAX == KVQ_CHANNEL_WISE ? kMaxGroups : 1) * GROUP_STRIDE;
-  static constexpr int QZ = QB + QB_BYTES + 16;                  // 256 B of zeros (off-diagonal B)
-  static constexpr int KB = QZ + 256 + 112;                      // chan-K (scale, bias) [groups][4] / tok-K (s',z'') [tokens]
+  static constexpr int QZ = QB + QB_BYTES + 16;                  // 384 B of zeros (off-diagonal B)
+  static constexpr int QZ_BYTES = 384;
+  static constexpr int KB = QZ + QZ_BYTES + 112;                 // chan-K (scale, bias) [groups][4] / tok-K (s',z'') [tokens]
   static constexpr int KB_BYTES = KAX == KVQ_CHANNEL_WISE ? kMaxGroups * 4 * 8 : kChunkTokens * 8;
   static constexpr int VA = KB + KB_BYTES;                       // tok-V coef [tokens] / chan-V (sigma,rho) [groups][128]
   static constexpr int VG_BLOCK = 32 * 8 + 16;                   // chan-V: 32 channels' (sigma, rho) + 16 B padding

@@ -322,7 +322,8 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
           S[q4] = sv;
         }
       }
-      if (t0 + C::TIT > te) {
+      if (t0 + C::TIT > te) {  // the split's partial last iteration only
+        asm volatile("");  // keeps this a branch (see the quantised decode kernel)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           if (t0 + tk0 + (j >> 1) + C::D2 * (j & 1) >= te) S[j] = -INFINITY;

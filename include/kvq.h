@@ -163,12 +163,14 @@ kvq_status decode_attention_quant(const kvq_format* fmt, const void* q, const kv
                                   void* stream);
 
 /*
- * decode_attention_quant_fp8 -- decode_attention_quant on fp8 matrix operands
- * (v_mfma_scale_f32_16x16x128_f8f6f4), the analogue of the pages' Blackwell
- * path that injects codes into the low bits of E4M3 / E2M1 (rag-lover.com
- * explainer). A 2- or 4-bit code masked into its byte is the E4M3 value
- * code * 2^-9 (exact, codes < 16), so one 128-deep product takes 32 channels
- * of a token (q.K^T) or 16 tokens of two channels (P.V).
+ * decode_attention_quant_fp8 -- decode_attention_quant on fp8 / fp4 matrix
+ * operands (v_mfma_scale_f32_16x16x128_f8f6f4), the analogue of the pages'
+ * Blackwell path that injects codes into the low bits of E4M3 / E2M1
+ * (rag-lover.com explainer). A 2- or 4-bit code masked into its byte is the
+ * E4M3 value code * 2^-9 (exact, codes < 16), a 2-bit code masked into its
+ * nibble the E2M1 value code / 2 (INT2 K codes take this form), so one
+ * 128-deep product takes 32 channels of a token (q.K^T) or 16 tokens of two
+ * channels (P.V); codes enter the product exactly.
  *   q.K^T: the query side is an E4M3 pair hi + lo / 16 of q * s
  *   (channel-wise K) or q (token-wise K): at least 8 significant bits
  *   (relative error <= 2^-8, the precision of a bf16 operand), exactly q for
