@@ -50,6 +50,10 @@ def parse():
     p.add_argument("--no-append", action="store_true", help="skip the append / window timings")
     p.add_argument("--no-share", action="store_true",
                    help="skip the one-KV-head (8-way tensor-parallel share) timings")
+    p.add_argument("--no-paged", action="store_true",
+                   help="skip the paged long-context batch (4 layers INT4, INT2, INT4, INT2)")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip the graph-replayed timings of the short calls")
     p.add_argument("--no-groups", action="store_true",
                    help="skip the token-wise G = 128 / 64 / 32 timings")
     p.add_argument("--only", choices=["int2", "int4"], default=None,
@@ -99,6 +103,42 @@ def time_calls(fn, steps, warmup, stream):
     per = np.array([e0.elapsed_time(e1) for e0, e1 in evs]) * 1e3  # us
     total_ms = t_all0.elapsed_time(t_all1)
     return per, total_ms
+
+
+def graph_time(fn, calls_per_graph, replays, warmup_replays, stream, check=None):
+    """Time fn() captured calls_per_graph times into one HIP graph and replayed:
+    the rate of back-to-back calls without the host's per-call launch cost.
+    check(): called after the eager reference run and after each timed replay
+    batch; returns the tensor that must come out bit-identical each time."""
+    import torch
+    ref = None
+    if check is not None:
+        fn()
+        torch.cuda.synchronize()
+        ref = check().clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls_per_graph):
+            fn()
+    torch.cuda.synchronize()
+    for _ in range(warmup_replays):
+        g.replay()
+    torch.cuda.synchronize()
+    if ref is not None:
+        assert torch.equal(check(), ref), "graph replay output differs from the eager call"
+        fn()  # eager work between replays
+        torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(replays):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    if ref is not None:
+        assert torch.equal(check(), ref), "graph replay output differs from the eager call"
+    del g
+    return t0.elapsed_time(t1) * 1e3 / (replays * calls_per_graph)  # us per call
 
 
 def make_inputs(B, L, widths, need_bf16, dev, log=log, extra_formats=()):
@@ -206,7 +246,112 @@ def share_timings(B, L, widths, args, dev, stream):
                                  num_splits=kvq.kvq_plan_splits(fmt, B, L))
         log(f"TP-8 share INT{bits}: {us:.1f} us/call, {gbs:.0f} GB/s "
             f"({100 * gbs / PEAK_HBM_GBS:.1f}%), splits {res[f'int{bits}']['num_splits']}")
+        if not args.no_graph:
+            # the same calls replayed from a HIP graph: each call is ~60-100 us of
+            # GPU work, about what the host needs to issue it, so the eager rate
+            # above includes host launch gaps
+            usg = graph_time(call, 20, max(5, args.steps // 5), 10, stream, check=lambda: out)
+            res[f"int{bits}"].update(graph_us_per_call=round(usg, 2),
+                                     graph_gbs=round(eff / (usg * 1e-6) / 1e9, 1),
+                                     graph_pct_peak=round(100.0 * eff / (usg * 1e-6) / 1e9 / PEAK_HBM_GBS, 2))
+            log(f"TP-8 share INT{bits}, graph-replayed: {usg:.1f} us/call "
+                f"({res[f'int{bits}']['graph_pct_peak']:.1f}%)")
     res["shape"] = f"B={B} x {L} tokens, 1 KV head x 4 query heads (decode + combine)"
+    return res
+
+
+def paged_effective_bytes(bits, lens, H=8, D=128):
+    """Bytes a decode over a paged cache must read: packed K and V codes of the
+    tokens present, token-wise V (s, z) per token, channel-wise K (s, z) per
+    128-token group (a partial last group counts whole)."""
+    tot = 0
+    for L in lens:
+        tot += H * (L * (2 * D * bits // 8 + 4) + ((L + 127) // 128) * D * 4)
+    return tot
+
+
+def paged_timings(args, dev, stream):
+    """Long-context paged batch: 64 sequences with lengths log-uniform in
+    [1K, 128K], 64-token pages scattered through one pool per layer by a seeded
+    permutation, K channel-wise / V token-wise, four layers INT4, INT2, INT4,
+    INT2 decoded back to back on one stream. One step = the four calls."""
+    import torch
+    import synth
+    import bit_quantized_kv_int2_amd as kvq
+    layers = [synth.paged_long(layer) for layer in range(4)]
+    lens = layers[0].seq_lens
+    B, Lmax, H, D = len(lens), max(lens), 8, 128
+    table, num_pages = synth.build_page_table(lens, 64, seed=5)
+    tbl = torch.from_numpy(table).to(dev)
+    lens_d = torch.tensor(lens, dtype=torch.int32, device=dev)
+    t0 = time.time()
+    kh = np.empty((H, Lmax, D), np.float32)
+    vh = np.empty((H, Lmax, D), np.float32)
+    state = []
+    for w in layers:
+        fmt = kvq.make_format(w.bits, "channel", "token", H, page_size=64)
+        cache = kvq.cache_tensors(fmt, B, Lmax, num_pages, device=dev)
+        offs = w.outlier_offsets()
+        for b, Lb in enumerate(lens):
+            w.kv_row("k", b, length=Lb, offsets=offs, out=kh[:, :Lb])
+            w.kv_row("v", b, length=Lb, out=vh[:, :Lb])
+            kd = torch.from_numpy(np.ascontiguousarray(kh[:, :Lb])).to(dev)[None]
+            vd = torch.from_numpy(np.ascontiguousarray(vh[:, :Lb])).to(dev)[None]
+            # (one-row length and page-table tensors of their own: the library
+            # takes 16-byte aligned arrays, which row slices are not)
+            kvq.kv_quantize_pack(fmt, kd, vd, torch.tensor([Lb], dtype=torch.int32, device=dev),
+                                 cache, page_table=torch.from_numpy(table[b:b + 1].copy()).to(dev),
+                                 max_len=Lb)
+        torch.cuda.synchronize()
+        q = torch.from_numpy(w.q_bf16().view(np.int16)).to(dev).view(torch.bfloat16)
+        # the lengths are known on the host: plan the splits for them
+        ns = kvq.kvq_plan_splits_for_lengths(fmt, lens, Lmax)
+        ws = kvq.workspace_tensor(fmt, B, Lmax, ns, device=dev)
+        out = torch.empty((B, 4 * H, D), dtype=torch.float32, device=dev)
+        state.append((w.bits, fmt, cache, q, ws, out, ns))
+        log(f"paged layer {w.layer} (INT{w.bits}) packed ({time.time() - t0:.0f} s), {ns} splits")
+
+    def step():
+        for _, fmt, cache, q, ws, out, ns in state:
+            kvq.decode_attention_quant(fmt, q, cache, lens_d, Lmax, 1.0 / math.sqrt(D), out,
+                                       page_table=tbl, num_splits=ns, workspace=ws)
+
+    per, total_ms = time_calls(step, args.steps, max(10, args.warmup // 4), stream)
+    us = total_ms * 1e3 / args.steps
+    eff = sum(paged_effective_bytes(st[0], lens) for st in state)
+    res = {"shape": f"{B} sequences, lengths log-uniform in [1024, 131072] (total {sum(lens)} tokens, "
+                    f"max {Lmax}), 64-token pages in one pool per layer ({num_pages} pages), "
+                    f"8 KV x 32 query heads, layers INT4, INT2, INT4, INT2",
+           "us_per_step": round(us, 2), "us_median": round(float(np.median(per)), 2),
+           "effective_bytes": eff, "gbs": round(eff / (us * 1e-6) / 1e9, 1),
+           "pct_peak": round(100.0 * eff / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+           "num_splits": {f"int{st[0]}": st[-1] for st in state[:2]},
+           "num_splits_auto_plan": {f"int{bits}": kvq.kvq_plan_splits(fmt, B, Lmax)
+                                    for bits, fmt, *_ in state[:2]}}
+    log(f"paged 4 layers: {us:.1f} us/step, {res['gbs']:.0f} GB/s ({res['pct_peak']:.1f}%)")
+    if not args.no_graph:
+        usg = graph_time(step, 5, max(5, args.steps // 5), 5, stream, check=lambda: state[-1][5])
+        res.update(graph_us_per_step=round(usg, 2), graph_gbs=round(eff / (usg * 1e-6) / 1e9, 1),
+                   graph_pct_peak=round(100.0 * eff / (usg * 1e-6) / 1e9 / PEAK_HBM_GBS, 2))
+        log(f"paged 4 layers, graph-replayed: {usg:.1f} us/step ({res['graph_pct_peak']:.1f}%)")
+    # each layer alone (eager), with the length-aware plan and with the auto plan
+    for li, (bits, fmt, cache, q, ws, out, ns) in enumerate(state):
+        el = paged_effective_bytes(bits, lens)
+        entry = {}
+        for name, n in (("", ns), ("auto_plan_", 0)):
+            wsn = ws if n else kvq.workspace_tensor(fmt, B, Lmax, 0, device=dev)
+
+            def one():
+                kvq.decode_attention_quant(fmt, q, cache, lens_d, Lmax, 1.0 / math.sqrt(D), out,
+                                           page_table=tbl, num_splits=n, workspace=wsn)
+            _, tms = time_calls(one, args.steps, 10, stream)
+            ul = tms * 1e3 / args.steps
+            entry.update({f"{name}us_per_call": round(ul, 2), f"{name}gbs": round(el / (ul * 1e-6) / 1e9, 1),
+                          f"{name}pct_peak": round(100.0 * el / (ul * 1e-6) / 1e9 / PEAK_HBM_GBS, 2)})
+        res[f"layer{li}_int{bits}"] = entry
+        log(f"paged layer {li} INT{bits}: {entry['us_per_call']} us ({ns} splits), "
+            f"auto plan {entry['auto_plan_us_per_call']} us")
+    del state
     return res
 
 
@@ -310,6 +455,7 @@ def main():
     del inp["xcaches"]
 
     share = None if args.no_share or args.only else share_timings(B, L, widths, args, dev, stream)
+    paged = None if args.no_paged or args.only else paged_timings(args, dev, stream)
 
     # ---- streaming-read reference over the same byte count (context) --------
     stream_ref = {}
@@ -475,6 +621,7 @@ def main():
         "append": append,
         "token_wise_groups": groups or None,
         "tp8_share": share,
+        "paged_long_context": paged,
         "fp8_qk": fp8 or None,
     }
     for b, v in stream_ref.items():

@@ -79,6 +79,7 @@ def lib():
         L.kvq_check_format.argtypes = [FP]
         L.kvq_cache_sizes.argtypes = [FP, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]
         L.kvq_plan_splits.argtypes = [FP, _I, _I, ctypes.POINTER(ctypes.c_int32)]
+        L.kvq_plan_splits_for_lengths.argtypes = [FP, _I, _I, _P, ctypes.POINTER(ctypes.c_int32)]
         L.kvq_workspace_size.argtypes = [FP, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]
         L.kv_quantize_pack.argtypes = [FP, _P, _P, _P, _P, _I, _I, _I, ctypes.POINTER(Cache), _P]
         L.decode_attention_quant.argtypes = [FP, _P, ctypes.POINTER(Cache), _P, _P, _I, _I, _I,
@@ -92,7 +93,8 @@ def lib():
         L.decode_attention_quant_window.argtypes = [FP, _P, ctypes.POINTER(Cache), _P, _P, _P, _P,
                                                     _I, _I, _I, ctypes.c_float, _P, _I, _I, _P,
                                                     ctypes.c_size_t, _P]
-        for fn in ("kvq_check_format", "kvq_cache_sizes", "kvq_plan_splits", "kvq_workspace_size",
+        for fn in ("kvq_check_format", "kvq_cache_sizes", "kvq_plan_splits",
+                   "kvq_plan_splits_for_lengths", "kvq_workspace_size",
                    "kv_quantize_pack", "decode_attention_quant", "decode_attention_quant_fp8",
                    "decode_attention_bf16",
                    "kvq_stream_read", "kv_append", "kvq_window_workspace_size",
@@ -124,6 +126,17 @@ def kvq_plan_splits(fmt: Format, batch: int, max_len: int) -> int:
     n = ctypes.c_int32()
     _check(lib().kvq_plan_splits(ctypes.byref(fmt), batch, max_len, ctypes.byref(n)),
            "kvq_plan_splits")
+    return int(n.value)
+
+
+def kvq_plan_splits_for_lengths(fmt: Format, seq_lens, max_len: int) -> int:
+    """num_splits for a batch whose lengths are known on the host (sequence of ints)."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    n = ctypes.c_int32()
+    _check(lib().kvq_plan_splits_for_lengths(ctypes.byref(fmt), int(lens.size), int(max_len),
+                                             lens.ctypes.data_as(ctypes.c_void_p),
+                                             ctypes.byref(n)), "kvq_plan_splits_for_lengths")
     return int(n.value)
 
 

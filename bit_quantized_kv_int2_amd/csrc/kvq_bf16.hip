@@ -47,7 +47,9 @@ __global__ void __launch_bounds__(kThreads) bf16_kernel(Bf16Args a) {
   __shared__ __attribute__((aligned(16))) float mo[kWaves * 4 * 128];
   __shared__ float ml[kWaves * 4 * 2];
 
-  const int sp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const WorkItem wi = work_item(blockIdx.x, a.num_kv_heads, a.batch, a.num_splits);
+  if (!wi.live) return;  // padding to whole rounds of 8 rows
+  const int sp = wi.sp, h = wi.h, b = wi.b;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int H = a.num_kv_heads, Hq = H * kGqa;
   int L = max(a.seq_lens[b], 0);
@@ -226,7 +228,7 @@ __global__ void __launch_bounds__(kThreads) bf16_kernel(Bf16Args a) {
 }  // namespace
 
 hipError_t launch_decode_bf16(const Bf16Args& a, hipStream_t s) {
-  dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
+  dim3 grid((unsigned)decode_grid_blocks((long)a.batch * a.num_kv_heads, a.num_splits));
   if (a.page_size) bf16_kernel<true><<<grid, kThreads, 0, s>>>(a);
   else bf16_kernel<false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();

@@ -63,8 +63,9 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   // work-item and work-group ids straight from the builtins: this file is
   // built with the IEEE mode bit cleared, which keeps the device library's
   // id helpers from being inlined
-  const int sp = __builtin_amdgcn_workgroup_id_x(), h = __builtin_amdgcn_workgroup_id_y(),
-            b = __builtin_amdgcn_workgroup_id_z();
+  const WorkItem wi = work_item(__builtin_amdgcn_workgroup_id_x(), a.num_kv_heads, a.batch, a.num_splits);
+  if (!wi.live) return;  // padding to whole rounds of 8 rows
+  const int sp = wi.sp, h = wi.h, b = wi.b;
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps addressing scalar
   const int H = a.num_kv_heads, Hq = H * kGqa;
@@ -130,14 +131,31 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   };
   auto lane_koff = [](int lg, int lr) { return (uint32_t)(16 * (16 * lg + lr)); };  // bytes
   auto lane_voff = [](int lg, int lr) { return (uint32_t)(4 * (16 * lg + lr)); };   // words
-  auto load_codes = [&](int t0, Codes& cd, uint32_t koff, uint32_t voff) {
-    const long ch = chunk_of(t0);
+  auto load_block = [&](long ch, Codes& cd, uint32_t koff, uint32_t voff) {
     const unsigned char* kb = a.k_codes + ch * (kPage * C::KROW) + koff;
 #pragma unroll
     for (int e = 0; e < C::KDW / 4; ++e) cd.k[e] = __builtin_nontemporal_load((const u4*)(kb + 1024 * e));
     const uint32_t* vb = a.v_words + ch * ((kPage / C::TPW) * kHeadDim) + voff;
 #pragma unroll
     for (int e = 0; e < C::NVW; ++e) cd.v[e] = __builtin_nontemporal_load((const u4*)(vb + 256 * e));
+  };
+  auto load_codes = [&](int t0, Codes& cd, uint32_t koff, uint32_t voff) {
+    load_block(chunk_of(t0), cd, koff, voff);
+  };
+  // Paged caches: the physical page of a wave's next iteration is loaded one
+  // iteration before its codes, so the code loads never wait on a page-table
+  // read; the load's wait falls in with the code loads' own at the end of the
+  // iteration. A wave's next iteration is 64 tokens on within a 128-token group
+  // (iterations start at multiples of 64, and groups at multiples of 128), else
+  // 448 tokens on, in its next group of the same or the next chunk.
+  auto next_it = [](int t) { return t + (((t >> 6) & 1) ? 7 : 1) * C::TIT; };
+  // (the index is passed through a vector register so that the loaded page
+  // stays in one too: taken as wave-uniform, it would be moved to a scalar
+  // register, and waited for, right after the load)
+  auto page_at = [&](int t) -> int {
+    int z = 0;
+    asm volatile("" : "+v"(z));
+    return a.page_table[(long)b * a.max_pages + t / kPage + z];
   };
 
   // Wave wv owns the 128-token groups wv, wv + 4, wv + 8, ... of the split
@@ -148,9 +166,11 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   // The first iteration's codes go out before anything else; later
   // iterations (also across chunk boundaries) are loaded one ahead.
   Codes cur;
+  int pg_next = 0;  // paged: physical page of this wave's next iteration
   {
     const int t0 = tb + 2 * wv * C::TIT;
     if (t0 < te) load_codes(t0, cur, lane_koff(g, ri), lane_voff(g, ri));
+    if (PAGED && next_it(t0) < te) pg_next = page_at(next_it(t0));
   }
 
   // ---- query: once per split -------------------------------------------------
@@ -564,7 +584,14 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       if (t0 >= ce) break;
       Codes nxt;
       const int t1 = t0 + ((jj & 1) ? 7 : 1) * C::TIT;  // this wave's next iteration
-      if (t1 < te) load_codes(t1, nxt, koff, voff);
+      if (PAGED) {
+        if (t1 < te) {
+          load_block((long)pg_next * H + h, nxt, koff, voff);
+          if (next_it(t1) < te) pg_next = page_at(next_it(t1));
+        }
+      } else if (t1 < te) {
+        load_codes(t1, nxt, koff, voff);
+      }
       const int rel = t0 - cb;
       const int gi = rel / kGroup;
 
@@ -885,7 +912,7 @@ __global__ void __launch_bounds__(128) combine_kernel(const float* part_o, const
 
 template <int BITS, int KAX, int VAX, bool PAGED>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
+  dim3 grid((unsigned)decode_grid_blocks((long)a.batch * a.num_kv_heads, a.num_splits));
   if (a.fp8_qk) decode_kernel<BITS, KAX, VAX, PAGED, true><<<grid, kThreads, 0, s>>>(a);
   else decode_kernel<BITS, KAX, VAX, PAGED, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();

@@ -60,8 +60,9 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
   float* qs = (float*)(lds + M::QS);
   float* red = (float*)(lds + M::RED);
 
-  const int sp = __builtin_amdgcn_workgroup_id_x(), h = __builtin_amdgcn_workgroup_id_y(),
-            b = __builtin_amdgcn_workgroup_id_z();
+  const WorkItem wi = work_item(__builtin_amdgcn_workgroup_id_x(), a.num_kv_heads, a.batch, a.num_splits);
+  if (!wi.live) return;  // padding to whole rounds of 8 rows
+  const int sp = wi.sp, h = wi.h, b = wi.b;
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.num_kv_heads, Hq = H * kGqa;
@@ -448,7 +449,7 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
 
 template <int BITS, int NG>
 hipError_t launch_tg(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid(a.num_splits, a.num_kv_heads, a.batch);
+  dim3 grid((unsigned)decode_grid_blocks((long)a.batch * a.num_kv_heads, a.num_splits));
   decode_tg_kernel<BITS, NG><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -72,6 +72,29 @@ struct AppendArgs {
   uint16_t* v_sz;
 };
 
+// Work-groups of a decode launch: ns splits of each of the B H rows (row =
+// b H + h), on a 1-D grid. Work-groups are dealt to the 8 XCDs in turn, so the
+// one at launch index i runs on XCD i mod 8. Index i is read as position
+// p = i / 8 in the queue of XCD k = i mod 8, and that queue takes rows k, k + 8,
+// k + 16, ..., the ns splits of a row one after another. Every XCD then gets
+// the same number of rows (with 8 KV heads, one head of every sequence: the
+// same work even when the lengths are ragged), while a (split, head, sequence)
+// grid with the split fastest would put split s of every row on XCD
+// (s + X r) mod 8 for X columns, the same few XCDs for the rows' first splits
+// whenever X is even. Index counts are padded to whole rounds of 8 rows; the
+// padding work-groups return at once.
+inline long decode_grid_blocks(long rows, int ns) { return ((rows + 7) / 8) * 8 * (long)ns; }
+constexpr long kMaxGridBlocks = 1L << 24;  // 256-thread work-groups in a 32-bit grid
+struct WorkItem {
+  int sp, h, b;
+  bool live;
+};
+__device__ inline WorkItem work_item(unsigned i, unsigned H, unsigned B, unsigned ns) {
+  const unsigned k = i & 7u, p = i >> 3;
+  const unsigned row = k + 8u * (p / ns);
+  return WorkItem{(int)(p % ns), (int)(row % H), (int)(row / H), row < H * B};
+}
+
 // Launch arguments of the quantised decode (one layer).
 struct DecodeArgs {
   const uint16_t* q;       // bf16 [B][Hq][D]

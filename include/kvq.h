@@ -116,6 +116,24 @@ kvq_status kvq_cache_sizes(const kvq_format* fmt, int32_t batch, int32_t max_len
 kvq_status kvq_plan_splits(const kvq_format* fmt, int32_t batch, int32_t max_len,
                            int32_t* num_splits);
 
+/* Split-KV plan for a batch whose sequence lengths the caller knows on the
+ * host (a serving engine's scheduler does): the num_splits to pass to
+ * decode_attention_quant. Part of the decode's scheduling step: the pages put
+ * the kernel into a serving engine whose batches mix long and short contexts
+ * (FOSCAR arXiv:2611.09722; grafy.ai "How can developers integrate FOSCAR").
+ * The auto plan sizes splits from max_len alone, which fills the chip when the
+ * lengths are equal, and this returns the auto plan's count then. When the
+ * longest length exceeds 1.5x the mean, it returns a count whose splits are
+ * whole 2048-token chunks, about H * sum(len) / (2 * work-group slots) tokens
+ * long (the chunk count k0 nearest that, or k0 +- 1 where that makes the split
+ * count odd, else 2 mod 4; never longer than the auto plan's split), so that
+ * the longest sequences do not set the call time. seq_lens_host: [batch] int32
+ * in host memory (entries clamped to [0, max_len]); may be NULL when
+ * batch == 0. Pure host computation: no GPU call, no allocation. Errors:
+ * KVQ_ERR_NULL_POINTER, KVQ_ERR_BAD_SHAPE, or the format's. */
+kvq_status kvq_plan_splits_for_lengths(const kvq_format* fmt, int32_t batch, int32_t max_len,
+                                       const int32_t* seq_lens_host, int32_t* num_splits);
+
 /* Workspace bytes decode_attention_quant / decode_attention_bf16 need for a
  * given split count (0 = the auto plan). */
 kvq_status kvq_workspace_size(const kvq_format* fmt, int32_t batch, int32_t max_len,

@@ -122,6 +122,55 @@ def test_split_plan_and_workspace(L):
         kvq.kvq_workspace_size(f, 2, 1024, -1)
 
 
+def test_split_plan_for_known_lengths(L):
+    """Host-side plan over known lengths: the auto plan for (near-)equal lengths,
+    splits of whole 2048-token chunks sized to half the mean work per slot for a
+    ragged batch, and always a count the decode accepts."""
+    import synth
+    for bits in (2, 4):
+        f = kvq.make_format(bits, "channel", "token", 8)
+        auto = kvq.kvq_plan_splits(f, 128, 32768)
+        assert kvq.kvq_plan_splits_for_lengths(f, [32768] * 128, 32768) == auto
+        mild = list(range(30000, 30000 + 128 * 20, 20))
+        assert kvq.kvq_plan_splits_for_lengths(f, mild, 32768) == auto
+        share = kvq.make_format(bits, num_kv_heads=1)
+        assert kvq.kvq_plan_splits_for_lengths(share, [32768] * 128, 32768) == \
+            kvq.kvq_plan_splits(share, 128, 32768)
+        # the long-context paged batch: 64 sequences, log-uniform in [1K, 128K]
+        fp = kvq.make_format(bits, "channel", "token", 8, page_size=64)
+        lens = synth.paged_long(0).seq_lens
+        Lmax = max(lens)
+        ns = kvq.kvq_plan_splits_for_lengths(fp, lens, Lmax)
+        slots = 256 * (4 if bits == 2 else 3)
+        target = 8 * sum(lens) / (2 * slots)
+        k0 = max(1, int(target / 2048 + 0.5))
+        quanta = -(-Lmax // 256)                  # 256-token units of max_len
+
+        def count(chunks):                        # splits the decode makes of that length
+            req = -(-quanta // (8 * chunks))
+            return -(-Lmax // (256 * -(-quanta // req)))
+        cands = [count(k) for k in (k0, k0 + 1, k0 - 1) if k >= 1]
+        want = next((c for c in cands if c % 2), next((c for c in cands if c % 4 == 2), cands[0]))
+        assert ns == want
+        assert ns % 2 == 1 or ns % 4 == 2
+        assert ns > kvq.kvq_plan_splits(fp, 64, Lmax)
+        kvq.kvq_workspace_size(fp, 64, Lmax, ns)  # accepted as an explicit count
+        # one long sequence among short ones: one- or two-chunk splits
+        assert kvq.kvq_plan_splits_for_lengths(f, [131072] + [1024] * 63, 131072) in (32, 64)
+        # lengths are clamped to [0, max_len]; empty batches and all-empty lengths
+        assert kvq.kvq_plan_splits_for_lengths(f, [-5, 99999999] + [32768] * 126, 32768) == \
+            kvq.kvq_plan_splits_for_lengths(f, [0, 32768] + [32768] * 126, 32768)
+        assert kvq.kvq_plan_splits_for_lengths(f, [], 32768) == kvq.kvq_plan_splits(f, 0, 32768)
+        assert kvq.kvq_plan_splits_for_lengths(f, [0] * 8, 4096) == kvq.kvq_plan_splits(f, 8, 4096)
+    n = ctypes.c_int32()
+    f = kvq.make_format(2, "channel", "token", 8)
+    assert L.kvq_plan_splits_for_lengths(ctypes.byref(f), 4, 1024, None, ctypes.byref(n)) == NULLP
+    assert L.kvq_plan_splits_for_lengths(ctypes.byref(f), 0, 1024, None, ctypes.byref(n)) == OK
+    arr = (ctypes.c_int32 * 2)(5, 6)
+    assert L.kvq_plan_splits_for_lengths(ctypes.byref(f), 2, 1024, arr, None) == NULLP
+    assert L.kvq_plan_splits_for_lengths(ctypes.byref(f), -1, 1024, arr, ctypes.byref(n)) == BADSHAPE
+
+
 def _call_decode(L, fmt, q=16, cache=(16, 16, 16, 16), lens=16, table=None, maxp=0, B=1,
                  max_len=128, out=16, od=0, ns=0, ws=None, wsb=0):
     c = kvq.Cache(*cache) if cache is not None else None

@@ -199,3 +199,43 @@ def test_unread_hip_error_from_elsewhere_is_not_blamed():
     ref = oracle_attention(inp, orc_cache)
     got = out.double().cpu().numpy()
     assert rel_l2(got, ref) <= REL_L2_TOL and max_abs(got, ref) <= MAX_ABS_TOL
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_graph_replay_matches_eager(bits):
+    """decode_attention_quant (split decode + combine, paged cache) captured
+    into a HIP graph: every replay, with eager calls and synchronisations in
+    between, must give the eager call's output bit for bit. The library
+    records only kernel launches (no memsets) on the caller's stream."""
+    import torch
+    lens = [3000, 64, 1, 700, 129, 0]
+    w = synth.Workload("graph", len(lens), 2, 8, 128, lens, bits, "channel", "token", seed=81,
+                       outliers=True, page_size=64)
+    inp = Inputs(w)
+    run = GpuRun(inp)
+    kvq = run.kvq
+    ref_np = oracle_attention(inp, oracle_pack(inp))
+    ws = kvq.workspace_tensor(run.fmt, w.batch, w.max_len, 4, run.q.device)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), device=run.q.device)
+
+    def call():
+        kvq.decode_attention_quant(run.fmt, run.q, run.cache, run.lens, w.max_len, SCALE, out,
+                                   page_table=run.table, num_splits=4, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    got = eager.double().cpu().numpy()
+    assert rel_l2(got, ref_np) <= REL_L2_TOL and max_abs(got, ref_np) <= MAX_ABS_TOL
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep} differs from the eager call"
+        call()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)

@@ -21,7 +21,7 @@ from kvq_testlib import (MAX_ABS_TOL, REL_L2_TOL, SCALE, gpu_format, max_abs, pa
 pytestmark = pytest.mark.gpu
 
 
-def _decode(w, fmt, cache, table=None, fp8_qk=False):
+def _decode(w, fmt, cache, table=None, fp8_qk=False, num_splits=0):
     import torch
     import bit_quantized_kv_int2_amd as kvq
     dev = cache[0].device
@@ -30,7 +30,7 @@ def _decode(w, fmt, cache, table=None, fp8_qk=False):
     pt = None if table is None else torch.from_numpy(table).to(dev)
     out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
     kvq.decode_attention_quant(fmt, q, cache, lens, w.max_len, SCALE, out, page_table=pt,
-                               fp8_qk=fp8_qk)
+                               fp8_qk=fp8_qk, num_splits=num_splits)
     return out
 
 
@@ -119,6 +119,17 @@ def test_paged_long_context_four_layers():
     for li, (w, c, o) in enumerate(zip(layers, caches, outs)):
         units = [(b, (3 * b + li) % w.num_kv_heads) for b in sample]
         _check_units(w, c, o, units, table, num_pages, label=f"paged layer {li} int{w.bits}")
+    # the splits planned for these known lengths (what the benchmark runs): many
+    # more splits, an odd-padded grid, the combine over them
+    import bit_quantized_kv_int2_amd as kvq
+    for li in (0, 1):
+        w, c = layers[li], caches[li]
+        fmt = gpu_format(w)
+        ns = kvq.kvq_plan_splits_for_lengths(fmt, lens, w.max_len)
+        assert ns > kvq.kvq_plan_splits(fmt, w.batch, w.max_len)
+        o = _decode(w, fmt, c, table, num_splits=ns)
+        units = [(b, (5 * b + li) % w.num_kv_heads) for b in sample]
+        _check_units(w, c, o, units, table, num_pages, label=f"paged layer {li} int{w.bits}, {ns} splits")
 
 
 @pytest.mark.parametrize("paged", [False, True])
