@@ -378,6 +378,9 @@ def main():
     extra = []
     if not args.no_groups and args.only is None:
         for bits in (2, 4):
+            # the other fold pairing of the headline: K token-wise (acc-fold),
+            # V channel-wise (acc-fold per 128-token group)
+            extra.append((f"int{bits}_tc_g128", bits, "token", "channel", 128))
             for gsz in (128, 64, 32):
                 extra.append((f"int{bits}_tt_g{gsz}", bits, "token", "token", gsz))
     inp = make_inputs(B, L, widths, need_bf16, dev, extra_formats=extra)
@@ -435,7 +438,8 @@ def main():
         log(f"fp8 q.K^T INT{bits}: {us:.1f} us/call ({fp8[f'int{bits}']['pct_peak']:.1f}%), "
             f"rel-L2 vs fp16-operand path {fp8[f'int{bits}']['rel_l2_vs_fp16_path']:.2e}")
 
-    # ---- token-wise K and V with 128, 64 or 32 channels per group ------------
+    # ---- other formats on the same values: K token-wise / V channel-wise, and
+    # K and V token-wise with 128, 64 or 32 channels per group ----------------
     groups = {}
     for name, f in inp["xfmts"].items():
         cache = inp["xcaches"][name]
@@ -619,7 +623,7 @@ def main():
         "bf16": bf16,
         "stream_read_reference": {f"int{b}_bytes": v for b, v in stream_ref.items()},
         "append": append,
-        "token_wise_groups": groups or None,
+        "other_formats": groups or None,
         "tp8_share": share,
         "paged_long_context": paged,
         "fp8_qk": fp8 or None,
