@@ -747,18 +747,10 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
             X = mfma(*(const u4*)(rbase + rrow + pos), bp[k], X);
           }
         } else {
-          f4 G8[8];
+          // sum P'' of this iteration (the "code 1" row of the extra tile)
           f4 Xg = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int c = 0; c < 8; ++c) G8[c] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
           for (int k = 0; k < 2; ++k) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-              const uint32_t w = BITS == 4 ? cur.v[2 * k + (c >> 2)][c & 3] : cur.v[c >> 2][c & 3];
-              const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
-              G8[c] = mfma(av, bp[k], G8[c]);
-            }
             u4 ones = u4{0u, 0u, 0u, 0u};
             if (mn_ == 0) {
 #pragma unroll
@@ -766,17 +758,36 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
             }
             Xg = mfma(ones, bp[k], Xg);
           }
-          // fold this group's partial: O_d += sigma_d (G_d + rho_d * sum P)
           const float psum = __shfl(Xg[0], mn_);  // row 0 lives in lane group 0
           const float4* vg = (const float4*)(lds + M::VA + vg_off<KAX, VAX>(gi, 32 * mg));
+          // the group's partials in two halves of 4 channel tiles (16 accumulator
+          // registers live instead of 32), each folded as soon as it is complete:
+          // O_d += sigma_d (G_d + rho_d * sum P)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+          for (int hf = 0; hf < 2; ++hf) {
+            f4 G4[4];
 #pragma unroll
-            for (int c = 0; c < 8; c += 2) {
-              // channels 32g + 8j + c and +1: (sigma, rho, sigma, rho)
-              float4 sr = vg[(8 * j + c) / 2];
-              O[c][j] = fmaf(sr.x, fmaf(sr.y, psum, G8[c][j]), O[c][j]);
-              O[c + 1][j] = fmaf(sr.z, fmaf(sr.w, psum, G8[c + 1][j]), O[c + 1][j]);
+            for (int c = 0; c < 4; ++c) G4[c] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+#pragma unroll
+              for (int c4 = 0; c4 < 4; ++c4) {
+                const int c = 4 * hf + c4;
+                const uint32_t w = BITS == 4 ? cur.v[2 * k + (c >> 2)][c & 3] : cur.v[c >> 2][c & 3];
+                const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
+                G4[c4] = mfma(av, bp[k], G4[c4]);
+              }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+              for (int c4 = 0; c4 < 4; c4 += 2) {
+                // channels 32g + 8j + c and +1: (sigma, rho, sigma, rho)
+                const int c = 4 * hf + c4;
+                const float4 sr = vg[(8 * j + c) / 2];
+                O[c][j] = fmaf(sr.x, fmaf(sr.y, psum, G4[c4][j]), O[c][j]);
+                O[c + 1][j] = fmaf(sr.z, fmaf(sr.w, psum, G4[c4 + 1][j]), O[c + 1][j]);
+              }
             }
           }
           lsum += psum;

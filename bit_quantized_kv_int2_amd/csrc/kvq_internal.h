@@ -19,10 +19,13 @@ constexpr int kComputeUnits = 256;    // MI355X
 
 // Resident 256-thread decode work-groups per CU that the register allocation
 // targets (the kernels' launch bounds; 4 leave 128 VGPRs per lane, 3 leave
-// 168): INT2 with token-wise V fits in 128; channel-wise V keeps a second
-// accumulator tile and INT4 twice the codes. The split planner sizes grids
-// by the same numbers.
-constexpr int groups_per_cu(int bits, int vax) { return (bits == 2 && vax == KVQ_TOKEN_WISE) ? 4 : 3; }
+// 168): INT2 fits in 128 (with channel-wise V, whose per-group partials take
+// a second set of accumulator tiles, by folding them in two halves of 4
+// tiles; a few set-up values of the channel-wise-K and paged variants then
+// live in scratch from the prologue to the final merge, outside the loops);
+// INT4 holds twice the codes. The split planner sizes grids by the same
+// numbers.
+constexpr int groups_per_cu(int bits, int vax) { return (void)vax, bits == 2 ? 4 : 3; }
 // Token-wise groups of 32 / 64 channels: 3 per CU, except INT4 with four
 // groups per token, whose per-group accumulators need the 256 VGPRs of 2.
 constexpr int tg_groups_per_cu(int bits, int ng) { return (bits == 4 && ng == 4) ? 2 : 3; }

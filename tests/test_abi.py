@@ -103,14 +103,15 @@ def test_split_plan_and_workspace(L):
     # a single sequence is split finely enough to occupy the chip
     assert kvq.kvq_plan_splits(kvq.make_format(4, num_kv_heads=1), 1, 32768) >= 64
     assert kvq.kvq_plan_splits(kvq.make_format(4, num_kv_heads=1), 1, 1024) == 4
-    # the auto plan gives one round of resident work-groups (256 CUs x 4 for INT2
-    # with token-wise V, x 3 otherwise): no split at 1024 units, 8 / 6 splits at 128
+    # the auto plan gives one round of resident work-groups (256 CUs x 4 for INT2,
+    # x 3 for INT4): no split at 1024 units, 8 / 6 splits at 128
     assert kvq.kvq_plan_splits(f, 128, 32768) == 1
     assert kvq.kvq_plan_splits(kvq.make_format(4, "channel", "token", 8), 128, 32768) == 1
     share2, share4 = kvq.make_format(2, num_kv_heads=1), kvq.make_format(4, num_kv_heads=1)
     assert kvq.kvq_plan_splits(share2, 128, 32768) == 8
     assert kvq.kvq_plan_splits(share4, 128, 32768) == 6
-    assert kvq.kvq_plan_splits(kvq.make_format(2, "channel", "channel", 1), 128, 32768) == 6
+    assert kvq.kvq_plan_splits(kvq.make_format(2, "channel", "channel", 1), 128, 32768) == 8
+    assert kvq.kvq_plan_splits(kvq.make_format(4, "channel", "channel", 1), 128, 32768) == 6
     # the workspace also covers the bf16 decode's plan (1024 work-groups: 8 splits)
     assert kvq.kvq_workspace_size(share4, 128, 32768) == 128 * 4 * 8 * 130 * 4
     # explicit splits: any count from 1 to ceil(L / 256); one split needs no workspace
