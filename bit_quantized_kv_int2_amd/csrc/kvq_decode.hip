@@ -660,9 +660,12 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         for (int j = 0; j < 4; ++j)
           if (t0 + tk0 + (j >> 1) + C::D2 * (j & 1) >= te) S[j] = -INFINITY;
       }
-      const float mx = head_max(fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3])));
-      if (__any(mx > m_run + (float)kThr)) {
-        const float mn = fmaxf(m_run, mx);
+      // m_run is the same in all lanes of a head, so a lane's own maximum
+      // past m_run + kThr is the same test as its head's: the cross-lane
+      // reduction is needed only when the running maximum moves
+      const float lmx = fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3]));
+      if (__any(lmx > m_run + (float)kThr)) {
+        const float mn = fmaxf(m_run, head_max(lmx));
         const float sc = exp2_fast(m_run - mn);
 #pragma unroll
         for (int c = 0; c < 8; ++c) O[c] *= sc;
