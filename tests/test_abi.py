@@ -119,6 +119,11 @@ def test_split_plan_and_workspace(L):
     assert kvq.kvq_workspace_size(f, 2, 32768, 3) == 2 * 32 * 3 * 130 * 4
     with pytest.raises(kvq.KvqError):
         kvq.kvq_workspace_size(f, 2, 1024, 5)
+    # a decode launch is a 1-D grid of at most 2^24 work-groups: splits x rows,
+    # rows (sequences x KV heads) padded to a multiple of 8
+    assert kvq.kvq_workspace_size(f, 4096, 1 << 20, 512) == 4096 * 32 * 512 * 130 * 4
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_workspace_size(f, 4096, 1 << 20, 1024)
     with pytest.raises(kvq.KvqError):
         kvq.kvq_workspace_size(f, 2, 1024, -1)
 
