@@ -51,9 +51,9 @@ namespace {
 template <int BITS, int KAX, int VAX, bool PAGED, bool FP8>
 __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_kernel(DecodeArgs a) {
   using C = Cfg<BITS>;
-  // fp8 operands for P.V too (token-wise V): O[0..3] are the four 128-deep
-  // products' accumulators, X[0] the offset sum
-  constexpr bool PV8 = FP8 && VAX == KVQ_TOKEN_WISE;
+  // fp8 operands for P.V too: O[0..3] are the four 128-deep products'
+  // accumulators; token-wise V: X[0] the offset sum
+  constexpr bool PV8 = FP8;
   using M = Lds<KAX, VAX>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[M::TOTAL];
   float* qs = (float*)(lds + M::QS);
@@ -256,7 +256,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   // P'' = P * coef * 2^-F with max P'' < 2^14. Token-wise V: F follows the
   // largest scale this wave has seen and only grows (the accumulators are
   // rescaled by the exact power of two when it does); channel-wise V: constant.
-  int F = kThr - 14;
+  int F = kThr - 14 + (PV8 ? 6 : 0);
 
   // ---- chunks of up to kChunkTokens tokens: prologue, then the main loop ----
   for (int cb = tb; cb < te; cb += kChunkTokens) {
@@ -568,6 +568,8 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     // extra-tile rows: even = hi part, odd = lo part; only rows 0 and 1 of
     // the accumulator are used, the others repeat them
     const int rrow = (mn_ & 1) * M::VR_LO + 8 * mg;
+    // channel-wise V with fp8 P.V: 2^-F / E4M3 weight of the even / odd tokens
+    const float cw8[2] = {ldexpf(1.f, -F), ldexpf(1.f, -F) / (BITS == 2 ? 4.f : 1.f)};
     float cw[2];  // channel-wise V: 2^-F / weight of the compact values' tokens
 #pragma unroll
     for (int aa = 0; aa < 2; ++aa) {
@@ -680,26 +682,33 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       if (PV8) {
         // P'' = P * coef as an E4M3 pair hi + lo / 16 in bytes [jj0, jj1, jj2, jj3]
         // (tokens tk0, tk0 + D2, tk0 + 1, tk0 + D2 + 1)
-        const unsigned char* cf = lds + M::VA;
-        const float2 c0 = *(const float2*)(cf + coef_off<BITS>((rel + tk0) / 2));
-        const float2 c1 = *(const float2*)(cf + coef_off<BITS>((rel + tk0 + C::D2) / 2));
-        const float x0 = P[0] * c0.x, x1 = P[1] * c1.x, x2 = P[2] * c0.y, x3 = P[3] * c1.y;
+        float x0, x1, x2, x3;
+        if (VAX == KVQ_TOKEN_WISE) {
+          const unsigned char* cf = lds + M::VA;
+          const float2 c0 = *(const float2*)(cf + coef_off<BITS>((rel + tk0) / 2));
+          const float2 c1 = *(const float2*)(cf + coef_off<BITS>((rel + tk0 + C::D2) / 2));
+          x0 = P[0] * c0.x, x1 = P[1] * c1.x, x2 = P[2] * c0.y, x3 = P[3] * c1.y;
+        } else {  // P'' = P 2^-F / w8 (tk0 is even: INT2 tokens tk0 + 1, tk0 + D2 + 1 weigh 4)
+          x0 = P[0] * cw8[0], x1 = P[1] * cw8[0], x2 = P[2] * cw8[1], x3 = P[3] * cw8[1];
+        }
         lsum += (P[0] + P[1]) + (P[2] + P[3]);
         const uint32_t hw = cvt_fp8x2<true>(x2, x3, cvt_fp8x2<false>(x0, x1, any_u32()));
         const f2 h01 = fp8x2_val<false>(hw), h23 = fp8x2_val<true>(hw);
         const uint32_t lw = cvt_fp8x2<true>((x2 - h23.x) * 16.f, (x3 - h23.y) * 16.f,
                                             cvt_fp8x2<false>((x0 - h01.x) * 16.f, (x1 - h01.y) * 16.f, any_u32()));
-        const f2 l01 = fp8x2_val<false>(lw), l23 = fp8x2_val<true>(lw);
-        // offset sum from the same rounded P'' (consistent offsets)
-        const unsigned char* rb = lds + M::VR;
-        const float2 r0 = *(const float2*)(rb + coef_off<BITS>((rel + tk0) / 2));
-        const float2 r1 = *(const float2*)(rb + coef_off<BITS>((rel + tk0 + C::D2) / 2));
-        float ox = X[0];
-        ox = fmaf(fmaf(l01.x, 0.0625f, h01.x), r0.x, ox);
-        ox = fmaf(fmaf(l01.y, 0.0625f, h01.y), r1.x, ox);
-        ox = fmaf(fmaf(l23.x, 0.0625f, h23.x), r0.y, ox);
-        ox = fmaf(fmaf(l23.y, 0.0625f, h23.y), r1.y, ox);
-        X[0] = ox;
+        if (VAX == KVQ_TOKEN_WISE) {
+          // offset sum from the same rounded P'' (consistent offsets)
+          const f2 l01 = fp8x2_val<false>(lw), l23 = fp8x2_val<true>(lw);
+          const unsigned char* rb = lds + M::VR;
+          const float2 r0 = *(const float2*)(rb + coef_off<BITS>((rel + tk0) / 2));
+          const float2 r1 = *(const float2*)(rb + coef_off<BITS>((rel + tk0 + C::D2) / 2));
+          float ox = X[0];
+          ox = fmaf(fmaf(l01.x, 0.0625f, h01.x), r0.x, ox);
+          ox = fmaf(fmaf(l01.y, 0.0625f, h01.y), r1.x, ox);
+          ox = fmaf(fmaf(l23.x, 0.0625f, h23.x), r0.y, ox);
+          ox = fmaf(fmaf(l23.y, 0.0625f, h23.y), r1.y, ox);
+          X[0] = ox;
+        }
         // gather the A row: two source dwords per A dword, byte-interleaved
         uint32_t G[4];
 #pragma unroll
@@ -714,8 +723,29 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
           hv[dw] = (int)__builtin_amdgcn_perm(G[2 * ((dw >> 1) & 1) + 1], G[2 * ((dw >> 1) & 1)],
                                               asel[dw >> 2][dw & 1]);
         const v8i av = v8i{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]};
+        if (VAX == KVQ_TOKEN_WISE) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) O[c] = mfma8pv(av, unpack_v8<BITS>(cur.v, c), O[c], ascale);
+          for (int c = 0; c < 4; ++c) O[c] = mfma8pv(av, unpack_v8<BITS>(cur.v, c), O[c], ascale);
+        } else {
+          // channel-wise V, acc-fold per group: this iteration's products in
+          // fresh accumulators, and a fifth product against code 1 in every
+          // k position (weight 1 or 4 like the codes) that gives each row's
+          // sum of the same rounded P''; then O_d += sigma_d (G_d + rho_d sum P'')
+          // for this lane's channels 8 n + 2 c + (g & 1) (C row 4 g + x: head x,
+          // channel half g & 1, hi or lo part g >> 1)
+          f4 Gc[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            Gc[c] = mfma8pv(av, unpack_v8<BITS>(cur.v, c), f4{0.f, 0.f, 0.f, 0.f}, ascale);
+          const f4 ps = mfma8pv(av, ones8<BITS>(), f4{0.f, 0.f, 0.f, 0.f}, ascale);
+          const unsigned char* vgb = lds + M::VA + vg_off<KAX, VAX>(gi, 8 * mn_ + (mg & 1));
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float2 sr = *(const float2*)(vgb + 16 * c);  // (sigma, rho) of channel 8 n + 2 c + (g & 1)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) O[c][x] = fmaf(sr.x, fmaf(sr.y, ps[x], Gc[c][x]), O[c][x]);
+          }
+        }
       } else {
         // P'' into packed pairs: pk[a] = (token tk0 + a, token tk0 + a + D2)
         uint32_t pk[2];

@@ -275,6 +275,15 @@ __device__ inline f4 mfma8pv(v8i a, v8i b, f4 c, int scale_a) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, kScaleCodes);
 }
 
+// B operand holding code 1 at every k position of an fp8 P.V product, with
+// the weight the V codes there carry (INT2: the codes masked with 0x0C of a
+// byte count 4): the product gives each A row's weighted sum of P''
+template <int BITS>
+__device__ inline v8i ones8() {
+  const int a = 0x01010101, b = BITS == 2 ? 0x04040404 : 0x01010101;
+  return v8i{a, b, a, b, a, b, a, b};
+}
+
 // A operand of fp8 / fp4 QK^T MFMA j from a lane's K row (layout-version-2
 // pieces: k[p][c] is the row's 32-bit word 4 p + c). INT2: E2M1, the even
 // and odd channels of words 2j and 2j + 1 (3 ops per 16 codes); INT4: E4M3.

@@ -193,10 +193,12 @@ kvq_status decode_attention_quant(const kvq_format* fmt, const void* q, const kv
  *   (channel-wise K) or q (token-wise K): at least 8 significant bits
  *   (relative error <= 2^-8, the precision of a bf16 operand), exactly q for
  *   token-wise K; the channel-wise-K offset sum uses the same rounded pair.
- *   P.V (token-wise V): the probabilities P * s are E4M3 pairs hi + lo / 16
- *   in the rows of the product (hi and lo rows summed once at the end), the
- *   offset sum over tokens again from the rounded pair. Channel-wise V keeps
- *   fp16 P.V operands.
+ *   P.V: the probabilities (P * s for token-wise V, P for channel-wise V)
+ *   are E4M3 pairs hi + lo / 16 in the rows of the product (hi and lo rows
+ *   summed once at the end). Token-wise V: the offset sum over tokens from the
+ *   rounded pair. Channel-wise V: each 64-token step's products are folded
+ *   with its group's scale and offset, the offset weighted by the sum of the
+ *   same rounded pairs (a fifth product against code 1).
  * Numeric bound: the output meets rel-L2 <= 4e-3 and max-abs <= 2e-2 against
  * the fp64 oracle, the same gate as decode_attention_quant.
  *   Formats with groups of 128 only (others: KVQ_ERR_BAD_FORMAT); all other
