@@ -456,6 +456,15 @@ def main():
                             pct_peak=round(100.0 * eff / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2))
         log(f"{name}: {us:.1f} us/call, {groups[name]['gbs']:.0f} GB/s effective "
             f"({groups[name]['pct_peak']:.1f}%)")
+        if f.group == 128:  # the fp8 / fp4-operand variant on the same cache
+            def callg8():
+                kvq.decode_attention_quant(f, q, cache, lens, L, scale, out, workspace=wsg, fp8_qk=True)
+
+            _, total8 = time_calls(callg8, args.steps, args.warmup, stream)
+            us8 = total8 * 1e3 / args.steps
+            groups[name].update(fp8_us_per_call=round(us8, 2),
+                                fp8_pct_peak=round(100.0 * eff / (us8 * 1e-6) / 1e9 / PEAK_HBM_GBS, 2))
+            log(f"{name}, fp8 operands: {us8:.1f} us/call ({groups[name]['fp8_pct_peak']:.1f}%)")
     del inp["xcaches"]
 
     share = None if args.no_share or args.only else share_timings(B, L, widths, args, dev, stream)
