@@ -25,10 +25,14 @@ constexpr int kComputeUnits = 256;    // MI355X
 // live in scratch from the prologue to the final merge, outside the loops);
 // INT4 holds twice the codes. The split planner sizes grids by the same
 // numbers.
-constexpr int groups_per_cu(int bits, int vax) { return (void)vax, bits == 2 ? 4 : 3; }
-// Token-wise groups of 32 / 64 channels: 3 per CU, except INT4 with four
-// groups per token, whose per-group accumulators need the 256 VGPRs of 2.
-constexpr int tg_groups_per_cu(int bits, int ng) { return (bits == 4 && ng == 4) ? 2 : 3; }
+constexpr int groups_per_cu(int bits, int /*v_axis*/) { return bits == 2 ? 4 : 3; }
+// Token-wise groups of 32 / 64 channels: INT2 with two groups per token fits
+// in 128 VGPRs (4 per CU); INT2 with four groups and INT4 with two take 3;
+// INT4 with four groups per token, whose per-group accumulators need the 256
+// VGPRs of 2, takes 2.
+constexpr int tg_groups_per_cu(int bits, int ng) {
+  return bits == 2 ? (ng == 2 ? 4 : 3) : (ng == 4 ? 2 : 3);
+}
 
 // Code positions inside a 64-token block (layout_version 2). The decode
 // kernels load a block as 1 KB pieces, lane l taking bytes 16 l .. 16 l + 15
