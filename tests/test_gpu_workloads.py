@@ -130,6 +130,10 @@ def test_paged_long_context_four_layers():
         o = _decode(w, fmt, c, table, num_splits=ns)
         units = [(b, (5 * b + li) % w.num_kv_heads) for b in sample]
         _check_units(w, c, o, units, table, num_pages, label=f"paged layer {li} int{w.bits}, {ns} splits")
+        # the fp8 / fp4-operand variant on the same pages and splits (its bound: the same gate)
+        o8 = _decode(w, fmt, c, table, fp8_qk=True, num_splits=ns)
+        _check_units(w, c, o8, units, table, num_pages,
+                     label=f"paged layer {li} int{w.bits}, {ns} splits, fp8 operands")
 
 
 @pytest.mark.parametrize("paged", [False, True])
