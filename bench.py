@@ -141,6 +141,16 @@ def graph_time(fn, calls_per_graph, replays, warmup_replays, stream, check=None)
     return t0.elapsed_time(t1) * 1e3 / (replays * calls_per_graph)  # us per call
 
 
+def graph_time_median(fn, calls_per_graph, replays, warmup_replays, stream, check=None, repeats=3):
+    """graph_time repeated with a fresh capture each time: (median, all).
+    Back-to-back repeats of these short calls differ by up to ~15 % (the
+    first one after a run of eager calls is the slow one, however long its
+    warm-up); the median of three is the settled rate."""
+    ts = [graph_time(fn, calls_per_graph, replays, warmup_replays, stream, check=check)
+          for _ in range(repeats)]
+    return float(np.median(ts)), [round(t, 2) for t in ts]
+
+
 def make_inputs(B, L, widths, need_bf16, dev, log=log, extra_formats=()):
     """Headline inputs: fp32 K/V drawn per batch row on the host, packed on the
     GPU into one cache per bit width (and copied to bf16 for the baseline).
@@ -250,12 +260,13 @@ def share_timings(B, L, widths, args, dev, stream):
             # the same calls replayed from a HIP graph: each call is ~60-100 us of
             # GPU work, about what the host needs to issue it, so the eager rate
             # above includes host launch gaps
-            usg = graph_time(call, 20, max(5, args.steps // 5), 10, stream, check=lambda: out)
-            res[f"int{bits}"].update(graph_us_per_call=round(usg, 2),
+            usg, reps = graph_time_median(call, 20, max(5, args.steps // 5), 10, stream,
+                                          check=lambda: out)
+            res[f"int{bits}"].update(graph_us_per_call=round(usg, 2), graph_repeats_us=reps,
                                      graph_gbs=round(eff / (usg * 1e-6) / 1e9, 1),
                                      graph_pct_peak=round(100.0 * eff / (usg * 1e-6) / 1e9 / PEAK_HBM_GBS, 2))
             log(f"TP-8 share INT{bits}, graph-replayed: {usg:.1f} us/call "
-                f"({res[f'int{bits}']['graph_pct_peak']:.1f}%)")
+                f"({res[f'int{bits}']['graph_pct_peak']:.1f}%), repeats {reps}")
     res["shape"] = f"B={B} x {L} tokens, 1 KV head x 4 query heads (decode + combine)"
     return res
 
@@ -330,8 +341,9 @@ def paged_timings(args, dev, stream):
                                     for bits, fmt, *_ in state[:2]}}
     log(f"paged 4 layers: {us:.1f} us/step, {res['gbs']:.0f} GB/s ({res['pct_peak']:.1f}%)")
     if not args.no_graph:
-        usg = graph_time(step, 5, max(5, args.steps // 5), 5, stream, check=lambda: state[-1][5])
-        res.update(graph_us_per_step=round(usg, 2), graph_gbs=round(eff / (usg * 1e-6) / 1e9, 1),
+        usg, reps = graph_time_median(step, 5, max(5, args.steps // 5), 5, stream,
+                                      check=lambda: state[-1][5])
+        res.update(graph_us_per_step=round(usg, 2), graph_repeats_us=reps, graph_gbs=round(eff / (usg * 1e-6) / 1e9, 1),
                    graph_pct_peak=round(100.0 * eff / (usg * 1e-6) / 1e9 / PEAK_HBM_GBS, 2))
         log(f"paged 4 layers, graph-replayed: {usg:.1f} us/step ({res['graph_pct_peak']:.1f}%)")
     # each layer alone (eager), with the length-aware plan and with the auto plan
