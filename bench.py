@@ -370,7 +370,7 @@ def paged_timings(args, dev, stream):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
