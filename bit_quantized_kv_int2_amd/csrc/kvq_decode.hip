@@ -28,13 +28,14 @@
 //     code term and the offset term.
 //   * Token <-> tile maps are chosen so the QK^T accumulator layout is the PV
 //     B-operand layout: no cross-lane shuffles between the two products.
-//   * Per split (a multiple of 256 tokens, at most 2048), a prologue builds
-//     the fold operands in LDS: q*s per K group (channel-wise K) or q
-//     (token-wise K), per-token or per-group V coefficients. Four waves then
-//     stream 32 (INT4) or 64 (INT2) tokens per iteration each: 128-bit /
-//     64-bit coalesced code loads one iteration ahead, online softmax with a
-//     lazily moved maximum, and the (m, l, O) of the four waves are merged
-//     through LDS.
+//   * A work-group takes one split (a multiple of 256 tokens) of one
+//     (sequence, KV head) row, in the per-XCD order of work_item, and walks it
+//     in 2048-token chunks. Per chunk, each wave builds the fold operands of
+//     its own 128-token groups in LDS: q*s per K group (channel-wise K) or q
+//     (token-wise K), per-token or per-group V coefficients. The four waves
+//     then stream 64 tokens per iteration each: whole-line 1 KB wave loads of
+//     the codes one iteration ahead, online softmax with a lazily moved
+//     maximum; the (m, l, O) of the four waves are merged through LDS.
 //   * Extra PV tile: a 9th A tile whose rows hold hi/lo fp16 parts of the
 //     token-wise-V offset coefficient (or the subnormal "code 1" pattern for
 //     channel-wise V) gives sum_t P_t r_t (or sum_t P_t) from the same rounded
