@@ -92,6 +92,22 @@ def test_fp8_channel_wise_v_multi_chunk(bits):
         _check(inp, run, f"chunks_int{bits}_tc_splits{ns}", num_splits=ns)
 
 
+@pytest.mark.parametrize("v_axis", ["token", "channel"])
+def test_fp8_bf16_output(v_axis):
+    """bf16 output of the fp8 / fp4-operand variant: the gate holds after the
+    output rounding too, and the rows equal the fp32 output rounded."""
+    import torch
+    w = synth.mid_int2("channel", v_axis)
+    inp = Inputs(w)
+    run = GpuRun(inp)
+    ref = oracle_attention(inp, oracle_pack(inp))
+    ob = run.decode(out_dtype=torch.bfloat16, fp8_qk=True)
+    of = run.decode(fp8_qk=True)
+    assert rel_l2(ob, ref) <= REL_L2_TOL and max_abs(ob, ref) <= MAX_ABS_TOL
+    rounded = torch.from_numpy(of.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(ob.astype(np.float32), rounded)
+
+
 def test_fp8_rejects_small_groups():
     import torch
     import bit_quantized_kv_int2_amd as kvq
