@@ -143,6 +143,13 @@ def test_bf16_output():
     ref = oracle_attention(inp, oracle_pack(inp))
     o = run.decode(out_dtype=torch.bfloat16)
     assert rel_l2(o, ref) <= REL_L2_TOL and max_abs(o, ref) <= MAX_ABS_TOL
+    # the bf16 rows are the fp32 output rounded to nearest even, through the
+    # combine kernel (split plan) and straight from the decode (one split)
+    for ns in (0, 1):
+        ob = run.decode(num_splits=ns, out_dtype=torch.bfloat16)
+        of = run.decode(num_splits=ns)
+        rounded = torch.from_numpy(of.astype(np.float32)).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(ob.astype(np.float32), rounded), ns
 
 
 @pytest.mark.parametrize("bits,group", [(2, 32), (2, 64), (4, 32), (4, 64)])
