@@ -11,6 +11,7 @@ namespace kvq {
 namespace {
 
 constexpr int kAppendThreads = 256;
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
 __device__ inline float bf16_f32(uint16_t u) { return __builtin_bit_cast(float, (uint32_t)u << 16); }
 
@@ -40,9 +41,18 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
   // channels) or per channel (channel-wise)
   const int ng = a.ng, G = kHeadDim / ng;
   __shared__ float S[kGroup * 4], Z[kGroup * 4];
+  // the window of one tensor, staged in LDS with whole 16-byte loads: the
+  // min/max and encode loops below read each value once or twice at scattered
+  // places, which from global memory is a chain of cache-latency loads
+  __shared__ __attribute__((aligned(16))) uint16_t win[kGroup * kHeadDim];
 
   for (int is_k = 1; is_k >= 0; --is_k) {
-    const uint16_t* w = is_k ? kw : vw;
+    {
+      const u4* src = (const u4*)(is_k ? kw : vw);
+      for (int i = tid; i < kGroup * kHeadDim / 8; i += kAppendThreads) ((u4*)win)[i] = src[i];
+    }
+    __syncthreads();
+    const uint16_t* w = win;
     const int axis = is_k ? a.k_axis : a.v_axis;
     uint16_t* sz = is_k ? a.k_sz : a.v_sz;
     const int ngroups = axis == KVQ_TOKEN_WISE ? kGroup * ng : kHeadDim;
@@ -52,9 +62,11 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
       if (axis == KVQ_TOKEN_WISE) {  // group = channels [jG, jG + G) of token t
         const int t = gi / ng, j = gi % ng;
         const uint16_t* row = w + t * kHeadDim + j * G;
-        mn = mx = bf16_f32(row[0]);
-        for (int d = 1; d < G; ++d) {
-          const float v = bf16_f32(row[d]);
+        // start each thread's walk along its row at its own offset, so that
+        // the threads of a wave read different LDS banks at each step
+        mn = mx = bf16_f32(row[gi % G]);
+        for (int e = 1; e < G; ++e) {
+          const float v = bf16_f32(row[(gi + e) % G]);
           mn = fminf(mn, v);
           mx = fmaxf(mx, v);
         }
