@@ -89,6 +89,26 @@ def test_split_invariance_and_determinism(bits):
     assert np.array_equal(again, outs[0])
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+def test_odd_head_count_grid_padding(bits):
+    """3 KV heads x 5 sequences = 15 rows: the 1-D grid pads to 16 rows per
+    split and deals rows to 8 per-XCD queues; every (row, split) must be
+    computed once and the padding must write nothing."""
+    lens = [2500, 1, 777, 0, 4096]
+    w = synth.Workload("odd_heads", len(lens), 3, 12, 128, lens, bits, "channel", "token", seed=91,
+                       outliers=True)
+    inp = Inputs(w)
+    run = GpuRun(inp)
+    ref = oracle_attention(inp, oracle_pack(inp))
+    for ns in (1, 3, 0):
+        o = run.decode(num_splits=ns)
+        e2, ea = rel_l2(o, ref), max_abs(o, ref)
+        print(f"odd heads int{bits} splits {ns}: rel_l2={e2:.3e} max_abs={ea:.3e}")
+        assert np.isfinite(o).all()
+        assert e2 <= REL_L2_TOL and ea <= MAX_ABS_TOL, (ns, e2, ea)
+        assert not o[3].any()  # the empty sequence
+
+
 @pytest.mark.parametrize("bits,k_axis,v_axis", [(2, "channel", "token"), (4, "channel", "token"),
                                                 (2, "token", "channel"), (4, "token", "token"),
                                                 (2, "channel", "channel")])
