@@ -1,7 +1,8 @@
 """GPU parity at the full sizes of the named workloads, on sampled units the
 oracle recomputes one by one, plus the bf16 baseline kernel.
 
-- headline: B=128 x 32768 tokens, INT4 and INT2 (both fold pairings for INT2);
+- headline: B=128 x 32768 tokens, INT4 and INT2 (both fold pairings for INT2),
+  and token-wise K and V in 64- / 32-channel groups;
 - the headline's 8-way tensor-parallel share: one KV head, 4 query heads;
 - paged long context: 64 sequences, log-uniform lengths in [1K, 128K], 64-token
   pages scattered over one pool, four layers INT4, INT2, INT4, INT2 run back to
@@ -15,8 +16,8 @@ import pytest
 
 import oracle
 import synth
-from kvq_testlib import (MAX_ABS_TOL, REL_L2_TOL, SCALE, gpu_format, max_abs, pack_rowwise,
-                         rel_l2, unit_host_cache)
+from kvq_testlib import (MAX_ABS_TOL, REL_L2_TOL, SCALE, gpu_format, group_of, max_abs,
+                         pack_rowwise, rel_l2, unit_host_cache)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +36,7 @@ def _decode(w, fmt, cache, table=None, fp8_qk=False, num_splits=0):
 
 
 def _check_units(w, cache, out, units, table=None, num_pages=0, label=""):
-    fmt_o = oracle.fmt_of(w)
+    fmt_o = oracle.fmt_of(w, group_of(w))
     q = w.q_bf16()
     got_all, ref_all = [], []
     pool = unit_host_cache(w, fmt_o, cache, 0, table, num_pages) if table is not None else None
@@ -87,6 +88,20 @@ def test_headline_sampled_fp8(bits):
     cache = pack_rowwise(w, fmt)
     out = _decode(w, fmt, cache, fp8_qk=True)
     _check_units(w, cache, out, [(0, 0), (37, 5), (64, 3), (127, 7)], label=w.name + "_fp8")
+
+
+@pytest.mark.parametrize("bits,group", [(2, 64), (4, 32)])
+def test_headline_token_groups_sampled(bits, group):
+    """Token-wise K and V with 64 / 32 channels per (s, z) pair at the headline
+    size: the per-group kernel at its tightest register budgets (INT2 with two
+    groups per token at 4 work-groups per CU, INT4 with four at 2)."""
+    import dataclasses
+    base = synth.headline(bits, "token", "token")
+    w = dataclasses.replace(base, name=f"{base.name}_g{group}", extra={"group": group})
+    fmt = gpu_format(w)
+    cache = pack_rowwise(w, fmt)
+    out = _decode(w, fmt, cache)
+    _check_units(w, cache, out, [(0, 0), (37, 5), (64, 3), (127, 7)], label=w.name)
 
 
 @pytest.mark.parametrize("bits", [2, 4])
