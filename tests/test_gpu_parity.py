@@ -109,6 +109,30 @@ def test_odd_head_count_grid_padding(bits):
         assert not o[3].any()  # the empty sequence
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+def test_many_splits_combine(bits):
+    """More than 128 splits per row (157 splits of 256 tokens for 40000): the
+    combine reads the (m, l) pairs in two passes and the partials 8 at a time
+    plus a ragged rest; a 300-token sequence leaves all but two of its splits
+    empty, and an empty sequence has no live split at all."""
+    import bit_quantized_kv_int2_amd as kvq
+    lens = [40000, 300, 0, 39000]
+    w = synth.Workload("many_splits", len(lens), 2, 8, 128, lens, bits, "channel", "token", seed=93,
+                       outliers=True)
+    inp = Inputs(w)
+    run = GpuRun(inp)
+    ref = oracle_attention(inp, oracle_pack(inp))
+    ns = 157
+    assert kvq.kvq_workspace_size(run.fmt, w.batch, w.max_len, ns) == \
+        w.batch * w.num_q_heads * 157 * (128 + 2) * 4
+    o = run.decode(num_splits=ns)
+    e2, ea = rel_l2(o, ref), max_abs(o, ref)
+    print(f"many splits int{bits}: rel_l2={e2:.3e} max_abs={ea:.3e}")
+    assert np.isfinite(o).all()
+    assert e2 <= REL_L2_TOL and ea <= MAX_ABS_TOL, (e2, ea)
+    assert not o[2].any()
+
+
 @pytest.mark.parametrize("bits,k_axis,v_axis", [(2, "channel", "token"), (4, "channel", "token"),
                                                 (2, "token", "channel"), (4, "token", "token"),
                                                 (2, "channel", "channel")])
