@@ -20,6 +20,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# A test may point the loader at another build of oracle.c (a copy with a
+# planted mistake, to show that the pins catch it); that build is used as is.
+_LIB_OVERRIDE = os.environ.get("KVQ_ORACLE_LIB")
 
 TOKEN_WISE, CHANNEL_WISE = 0, 1
 _AXIS = {"token": TOKEN_WISE, "channel": CHANNEL_WISE, 0: TOKEN_WISE, 1: CHANNEL_WISE}
@@ -46,9 +49,12 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        L = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            L = ctypes.CDLL(_LIB)
         L.orc_f32_to_f16.restype = ctypes.c_uint16
         L.orc_f32_to_f16.argtypes = [ctypes.c_float]
         L.orc_f16_to_f64.restype = ctypes.c_double
