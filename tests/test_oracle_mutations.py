@@ -26,6 +26,17 @@ MUTATIONS = [
     # paged channel-wise (s, z): the pair looked up in each token's own page
     # instead of the page holding the group's first token
     ("paged_pair_page", "int t0 = (t / G) * G;", "int t0 = t;"),
+    # scale from 2^b levels instead of the 2^b - 1 steps between min and max
+    ("scale_levels", "range / (float)qmax;", "range / (float)(qmax + 1);"),
+    # binary16 subnormals decoded one binade too low
+    ("f16_subnormal", "if (e == 0) v = ldexp((double)m, -24);", "if (e == 0) v = ldexp((double)m, -25);"),
+    # the softmax scale left out of the reference attention
+    ("softmax_scale", "      w[t] = scale * acc;", "      w[t] = acc;"),
+    # V codes packed into a word from the top down
+    ("v_bit_order", "|= (uint32_t)c << (f->bits * (t % tpw(f)));",
+     "|= (uint32_t)c << (f->bits * (tpw(f) - 1 - t % tpw(f)));"),
+    # V word position in a 64-token block: channel half chosen by the wrong bit
+    ("v_block_word", "256L * ((d / 4) % 2)", "256L * ((d / 8) % 2)"),
 ]
 
 
