@@ -237,3 +237,19 @@ def test_calls_without_library_fail_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(kvq, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         kvq.lib()
+
+
+def test_product_path_does_not_reach_the_oracle(L):
+    """Nothing in the package (binding, build script, HIP sources) imports,
+    loads or links the CPU oracle, and the built library needs no oracle
+    symbol: the oracle is test infrastructure only."""
+    pkg = os.path.join(ROOT, "bit_quantized_kv_int2_amd")
+    pat = re.compile(r"\boracle\b|liboracle|\borc_")
+    for dirpath, _, files in os.walk(pkg):
+        for name in files:
+            if name.endswith((".py", ".hip", ".h", ".cpp", ".c")):
+                text = open(os.path.join(dirpath, name)).read()
+                assert not pat.search(text), os.path.join(dirpath, name)
+    with open(kvq.LIB_PATH, "rb") as f:
+        blob = f.read()
+    assert b"liboracle" not in blob and b"orc_attention" not in blob
