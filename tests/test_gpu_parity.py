@@ -110,6 +110,35 @@ def test_odd_head_count_grid_padding(bits):
 
 
 @pytest.mark.parametrize("bits", [2, 4])
+def test_maximum_batch_short_sequences(bits):
+    """The largest batch the boundary accepts (65535 sequences), one KV head,
+    lengths 0..16 (a fraction of one 128-token group each): a 65536-row grid
+    of work-groups that mostly read a partial block and return, every output
+    row against the oracle."""
+    import types
+    B, D, Lmax = 65535, 128, 16
+    lens = [(7 * b + 3) % (Lmax + 1) for b in range(B)]
+    w = synth.Workload("max_batch", B, 1, 4, D, lens, bits, "channel", "token", seed=95)
+    assert w.max_len == Lmax
+    inp = types.SimpleNamespace(
+        w=w, k=synth.normal_f32((B, 1, Lmax, D), 95, 1), v=synth.normal_f32((B, 1, Lmax, D), 95, 2),
+        q=synth.f32_to_bf16_bits(synth.normal_f32((B, 4, D), 95, 3)), lens=np.asarray(lens, np.int32),
+        table=None, num_pages=0)
+    run = GpuRun(inp)
+    orc_cache = oracle_pack(inp)
+    ok, msg = cache_bytes_equal(run.cache_host(), orc_cache)
+    assert ok, msg
+    ref = oracle_attention(inp, orc_cache)
+    o = run.decode()
+    e2, ea = rel_l2(o, ref), max_abs(o, ref)
+    print(f"max batch int{bits}: rel_l2={e2:.3e} max_abs={ea:.3e}")
+    assert np.isfinite(o).all()
+    assert e2 <= REL_L2_TOL and ea <= MAX_ABS_TOL, (e2, ea)
+    empty = np.asarray(lens) == 0
+    assert not o[empty].any()
+
+
+@pytest.mark.parametrize("bits", [2, 4])
 def test_many_splits_combine(bits):
     """More than 128 splits per row (157 splits of 256 tokens for 40000): the
     combine reads the (m, l) pairs in two passes and the partials 8 at a time
