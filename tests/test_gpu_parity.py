@@ -138,6 +138,31 @@ def test_maximum_batch_short_sequences(bits):
     assert not o[empty].any()
 
 
+def test_single_long_sequence():
+    """One sequence of 2^19 + 77 tokens and one KV head: the automatic plan
+    spreads it over the whole chip (more than 128 splits, merged by the
+    combine), with a ragged last group."""
+    import types
+    import bit_quantized_kv_int2_amd as kvq
+    D, L = 128, (1 << 19) + 77
+    w = synth.Workload("one_long", 1, 1, 4, D, [L], 2, "channel", "token", seed=97, outliers=True)
+    inp = types.SimpleNamespace(
+        w=w, k=synth.normal_f32((1, 1, L, D), 97, 1) + w.outlier_offsets()[None, :, None, :],
+        v=synth.normal_f32((1, 1, L, D), 97, 2), q=synth.f32_to_bf16_bits(synth.normal_f32((1, 4, D), 97, 3)),
+        lens=np.asarray([L], np.int32), table=None, num_pages=0)
+    run = GpuRun(inp)
+    assert kvq.kvq_plan_splits(run.fmt, 1, L) > 128
+    orc_cache = oracle_pack(inp)
+    ok, msg = cache_bytes_equal(run.cache_host(), orc_cache)
+    assert ok, msg
+    ref = oracle_attention(inp, orc_cache)
+    o = run.decode()
+    e2, ea = rel_l2(o, ref), max_abs(o, ref)
+    print(f"one long sequence: rel_l2={e2:.3e} max_abs={ea:.3e}")
+    assert np.isfinite(o).all()
+    assert e2 <= REL_L2_TOL and ea <= MAX_ABS_TOL, (e2, ea)
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 def test_many_splits_combine(bits):
     """More than 128 splits per row (157 splits of 256 tokens for 40000): the
