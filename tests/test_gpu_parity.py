@@ -163,6 +163,28 @@ def test_single_long_sequence():
     assert e2 <= REL_L2_TOL and ea <= MAX_ABS_TOL, (e2, ea)
 
 
+@pytest.mark.xfail(strict=False, reason="INT4 with channel-wise V and fp16 operands carries a signed "
+                   "bias shared by all outputs (about 8.5e-6) that does not shrink with the output; "
+                   "at 2^19 tokens on one KV head the relative error (4.1e-3) leaves the gate")
+@pytest.mark.parametrize("k_axis", ["token", "channel"])
+def test_long_sequence_int4_channel_wise_v(k_axis):
+    """The long-context case that is known to leave the gate (16 splits)."""
+    import types
+    D, L = 128, (1 << 19) + 77
+    w = synth.Workload("one_long_cv", 1, 1, 4, D, [L], 4, k_axis, "channel", seed=97)
+    inp = types.SimpleNamespace(
+        w=w, k=synth.normal_f32((1, 1, L, D), 97, 1), v=synth.normal_f32((1, 1, L, D), 97, 2),
+        q=synth.f32_to_bf16_bits(synth.normal_f32((1, 4, D), 97, 3)), lens=np.asarray([L], np.int32),
+        table=None, num_pages=0)
+    run = GpuRun(inp)
+    ref = oracle_attention(inp, oracle_pack(inp))
+    o = run.decode(num_splits=16)
+    e2, ea = rel_l2(o, ref), max_abs(o, ref)
+    print(f"long int4 {k_axis[0]}c: rel_l2={e2:.3e} max_abs={ea:.3e}")
+    assert np.isfinite(o).all()
+    assert e2 <= REL_L2_TOL and ea <= MAX_ABS_TOL, (e2, ea)
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 def test_many_splits_combine(bits):
     """More than 128 splits per row (157 splits of 256 tokens for 40000): the
