@@ -254,6 +254,10 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   f4 X = f4{0.f, 0.f, 0.f, 0.f};  // extra tile accumulator
   float m_run = -INFINITY;
   float lsum = 0.f;
+  // fp16 token-wise V: the running output starts from kSeedV (set when the
+  // first scores arrive), scaled along with it; kseed is its current value
+  constexpr bool SEED = !PV8 && VAX == KVQ_TOKEN_WISE;
+  float kseed = 0.f;
   // P'' = P * coef * 2^-F with max P'' < 2^14. Token-wise V: F follows the
   // largest scale this wave has seen and only grows (the accumulators are
   // rescaled by the exact power of two when it does); channel-wise V: constant.
@@ -349,6 +353,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
 #pragma unroll
         for (int c = 0; c < 8; ++c) O[c] *= sc;
         X *= sc;
+        if (SEED) kseed *= sc;
         F = Fc;
       }
       const float two_mF = ldexpf(1.f, -F);
@@ -369,8 +374,12 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
                                : (float)(1 << (BITS * (e % C::SLOTS)));
           const float sv = f16lo(vz[rr][e]), zv = f16hi(vz[rr][e]);
           const float sg = sv != 0.f ? sv : 1.f;
-          cf[e] = sg * (two_mF / wt);
-          rw[rr][e] = zv * (__builtin_amdgcn_rcpf(sg) * wt);
+          // fp16 P.V: tokens of the odd slots (e odd) enter mirrored, with
+          // the scale negated and the offset z + qmax s
+          const bool mir = !PV8 && (e & 1);
+          cf[e] = mir ? -(sg * (two_mF / wt)) : sg * (two_mF / wt);
+          rw[rr][e] = mir ? -((zv * __builtin_amdgcn_rcpf(sg) + (float)((1 << BITS) - 1)) * wt)
+                          : zv * (__builtin_amdgcn_rcpf(sg) * wt);
         }
         *(float4*)(coef + coef_off<BITS>(tb_run[rr] / 2)) = make_float4(cf[0], cf[1], cf[2], cf[3]);
         if (PV8)  // fp32 w * rho per token, addressed like coef
@@ -390,13 +399,16 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         ((u4*)(rh + M::VR_LO))[pblk] = u4{lo[0], lo[1], lo[2], lo[3]};
       }
     } else if (glive) {
-      // (sigma, rho) of two channels per float4
+      // (sigma, rho) of two channels per float4; fp16 P.V takes rho - kKappa
+      // (the products start from kKappa * sum P'')
+      const float kap = PV8 ? 0.f : kKappa;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const uint32_t p0 = vz[e >> 2][e & 3], p1 = vz[e >> 2][(e + 1) & 3];
         const float s0 = f16lo(p0), z0 = f16hi(p0), s1 = f16lo(p1), z1 = f16hi(p1);
-        *(float4*)(lds + M::VA + vg_off<KAX, VAX>(gl, 8 * ck_s + e)) = make_float4(s0 != 0.f ? s0 : 1.f, s0 != 0.f ? z0 * __builtin_amdgcn_rcpf(s0) : z0,
-                                       s1 != 0.f ? s1 : 1.f, s1 != 0.f ? z1 * __builtin_amdgcn_rcpf(s1) : z1);
+        *(float4*)(lds + M::VA + vg_off<KAX, VAX>(gl, 8 * ck_s + e)) =
+            make_float4(s0 != 0.f ? s0 : 1.f, (s0 != 0.f ? z0 * __builtin_amdgcn_rcpf(s0) : z0) - kap,
+                        s1 != 0.f ? s1 : 1.f, (s1 != 0.f ? z1 * __builtin_amdgcn_rcpf(s1) : z1) - kap);
       }
     }
     if (KAX == KVQ_CHANNEL_WISE && FP8) {
@@ -574,8 +586,9 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     float cw[2];  // channel-wise V: 2^-F / weight of the compact values' tokens
 #pragma unroll
     for (int aa = 0; aa < 2; ++aa) {
+      // tk0 is even: aa = 1 is an odd slot, whose codes enter mirrored
       const int slot = (tk0 + aa) % C::TPW;
-      cw[aa] = ldexpf(1.f, -F) / (float)(1 << (BITS * (slot % C::SLOTS)));
+      cw[aa] = (aa ? -1.f : 1.f) * ldexpf(1.f, -F) / (float)(1 << (BITS * (slot % C::SLOTS)));
     }
     const float Qh = KAX == KVQ_TOKEN_WISE ? red[20 + mhh] : 0.f;
 
@@ -670,8 +683,18 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       if (__any(lmx > m_run + (float)kThr)) {
         const float mn = fmaxf(m_run, head_max(lmx));
         const float sc = exp2_fast(m_run - mn);
+        if (SEED) {
+          // the first scores of this wave (sc = 0) plant the seed
+          const float k0 = m_run == -INFINITY ? kSeedV : 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) O[c] *= sc;
+          for (int c = 0; c < 8; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) O[c][j] = fmaf(O[c][j], sc, k0);
+          kseed = fmaf(kseed, sc, k0);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) O[c] *= sc;
+        }
         X *= sc;
         lsum *= sc;
         m_run = mn;
@@ -774,42 +797,59 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
               const uint32_t w = BITS == 4 ? cur.v[2 * k + (c >> 2)][c & 3] : cur.v[c >> 2][c & 3];
-              const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
+              const u4 av = BITS == 4 ? unpack4v(w) : unpack2v(w, k);
               O[c] = mfma(av, bp[k], O[c]);
             }
             const int pos = ((rel / C::TIT) * C::NK + k) * 32;  // wave-uniform part
             X = mfma(*(const u4*)(rbase + rrow + pos), bp[k], X);
           }
         } else {
-          // sum P'' of this iteration (the "code 1" row of the extra tile)
+          // offset weights from the extra tile: row 0 holds +-w 2^-14 (minus
+          // on the mirrored slots, whose P'' are negative) and gives sum P'';
+          // row 1 holds -w 2^-14 on the mirrored slots only and gives their
+          // sum. Normal binary16 rows: these sums keep the window's 24 bits.
           f4 Xg = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
             u4 ones = u4{0u, 0u, 0u, 0u};
-            if (mn_ == 0) {
+            if (mn_ < 2) {
 #pragma unroll
-              for (int m = 0; m < 4; ++m) ones[m] = 0x00010001u << (BITS * (m % C::SLOTS));
+              for (int m = 0; m < 4; ++m) {
+                const uint32_t hb = (uint32_t)(BITS * (m % C::SLOTS) + 1) << 10;  // w 2^-14
+                const bool odd = (m % C::SLOTS) & 1;
+                const uint32_t h = odd ? (hb | 0x8000u) : (mn_ == 0 ? hb : 0u);
+                ones[m] = h | (h << 16);
+              }
             }
             Xg = mfma(ones, bp[k], Xg);
           }
-          const float psum = __shfl(Xg[0], mn_);  // row 0 lives in lane group 0
+          // rows 0 and 1 live in lane group 0; back to the code products' units
+          const float psum = __shfl(Xg[0], mn_) * 0x1p-10f;
+          const float pneg = __shfl(Xg[1], mn_) * 0x1p-10f;
+          // the group's products start from qmax sum_N P'' (the mirrored
+          // tokens' offset) + kKappa sum P'' (taken back out through rho - kKappa)
+          const float c0 = fmaf((float)((1 << BITS) - 1), pneg, kKappa * psum);
           const float4* vg = (const float4*)(lds + M::VA + vg_off<KAX, VAX>(gi, 32 * mg));
           // the group's partials in two halves of 4 channel tiles (16 accumulator
           // registers live instead of 32), each folded as soon as it is complete:
           // O_d += sigma_d (G_d + rho_d * sum P)
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
+            // the start value is rebuilt per half from a copy the compiler
+            // must treat as new: four registers live only until the first
+            // products of the half have issued
+            float c0h = c0;
+            asm volatile("" : "+v"(c0h));
+            const f4 seed = f4{c0h, c0h, c0h, c0h};
             f4 G4[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) G4[c] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
 #pragma unroll
               for (int c4 = 0; c4 < 4; ++c4) {
                 const int c = 4 * hf + c4;
                 const uint32_t w = BITS == 4 ? cur.v[2 * k + (c >> 2)][c & 3] : cur.v[c >> 2][c & 3];
-                const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
-                G4[c4] = mfma(av, bp[k], G4[c4]);
+                const u4 av = BITS == 4 ? unpack4v(w) : unpack2v(w, k);
+                G4[c4] = mfma(av, bp[k], k == 0 ? seed : G4[c4]);
               }
             }
 #pragma unroll
@@ -853,10 +893,12 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     lsum = head_sum(lsum);
     const float off = __shfl(X[0] + X[1], n);
     const float s24 = ldexpf(1.f, F + 24), sF = ldexpf(1.f, F);
+    // (O - kseed) 2^(F + 24) + off 2^F
+    const float offk = fmaf(-kseed, s24, off * sF);
 #pragma unroll
     for (int c = 0; c < 8; ++c)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) O[c][j] = fmaf(O[c][j], s24, off * sF);
+      for (int j = 0; j < 4; ++j) O[c][j] = fmaf(O[c][j], s24, offk);
     lw = lsum;
   } else {
     const float s24 = ldexpf(1.f, F + 24);

@@ -174,6 +174,7 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
   float m_run = -INFINITY;
   float lsum = 0.f;
   int F = 0;  // P'' = P * s * 2^-F / w, running per wave
+  float kseed = 0.f;  // the running output's start value (kSeedV), scaled along
 
   for (int cb = tb; cb < te; cb += M::CHUNK) {
     const int ce = min(cb + M::CHUNK, te);
@@ -226,6 +227,7 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
         for (int c = 0; c < 8; ++c) O[c] *= sc;
 #pragma unroll
         for (int j = 0; j < NG; ++j) X[j] *= sc;
+        kseed *= sc;
         F = Fc;
       }
       const float two_mF = ldexpf(1.f, -F);
@@ -240,8 +242,12 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
           const float wt = (float)(1 << (BITS * (e % C::SLOTS)));
           const float sv = f16lo(vz[rr][e]), zv = f16hi(vz[rr][e]);
           const float sg = sv != 0.f ? sv : 1.f;
-          cf[e] = sg * (two_mF / wt);
-          rw[rr][e] = zv * (__builtin_amdgcn_rcpf(sg) * wt);
+          // tokens of the odd slots (e odd) enter mirrored: scale negated,
+          // offset z + qmax s
+          const bool mir = e & 1;
+          cf[e] = mir ? -(sg * (two_mF / wt)) : sg * (two_mF / wt);
+          rw[rr][e] = mir ? -((zv * __builtin_amdgcn_rcpf(sg) + (float)((1 << BITS) - 1)) * wt)
+                          : zv * (__builtin_amdgcn_rcpf(sg) * wt);
         }
         *(float4*)(coef + coef_off<BITS>(tb_run[rr] / 2)) = make_float4(cf[0], cf[1], cf[2], cf[3]);
       }
@@ -336,10 +342,15 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
       if (__any(lmx > m_run + (float)kThr)) {
         const float mn = fmaxf(m_run, head_max(lmx));
         const float sc = exp2_fast(m_run - mn);
+        // the first scores of this wave (sc = 0) plant the seed
+        const float k0 = m_run == -INFINITY ? kSeedV : 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) O[c] *= sc;
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) O[c][q4] = fmaf(O[c][q4], sc, k0);
 #pragma unroll
         for (int j = 0; j < NG; ++j) X[j] *= sc;
+        kseed = fmaf(kseed, sc, k0);
         lsum *= sc;
         m_run = mn;
       }
@@ -370,7 +381,7 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
           for (int ct = 0; ct < TPG; ++ct) {
             const int c = j * TPG + ct;
             const uint32_t w = BITS == 4 ? cur.v[8 * k + c] : cur.v[c];
-            const u4 av = BITS == 4 ? unpack4(w) : unpack2(w, k);
+            const u4 av = BITS == 4 ? unpack4v(w) : unpack2v(w, k);
             O[c] = mfma(av, bp[k], O[c]);
           }
           const int pos = ((rel / C::TIT) * C::NK + k) * 32;
@@ -389,10 +400,11 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
       const float off = __shfl(X[j][0] + X[j][1], n);  // rows 0, 1 live in lane group 0
+      const float offk = fmaf(-kseed, s24, off * sF);    // (O - kseed) 2^(F + 24) + off 2^F
 #pragma unroll
       for (int ct = 0; ct < TPG; ++ct)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) O[j * TPG + ct][q4] = fmaf(O[j * TPG + ct][q4], s24, off * sF);
+        for (int q4 = 0; q4 < 4; ++q4) O[j * TPG + ct][q4] = fmaf(O[j * TPG + ct][q4], s24, offk);
     }
   }
 

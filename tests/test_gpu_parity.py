@@ -84,7 +84,7 @@ def test_split_invariance_and_determinism(bits):
     for ns in (1, 2, 3, 4, 8, 16):
         d = rel_l2(outs[ns], outs[0])
         print(f"splits {ns} vs auto: rel_l2={d:.3e}")
-        assert d < 2e-3
+        assert d < 5e-4
     again = run.decode(num_splits=0)
     assert np.array_equal(again, outs[0])
 
@@ -163,26 +163,94 @@ def test_single_long_sequence():
     assert e2 <= REL_L2_TOL and ea <= MAX_ABS_TOL, (e2, ea)
 
 
-@pytest.mark.xfail(strict=False, reason="INT4 with channel-wise V and fp16 operands carries a signed "
-                   "bias shared by all outputs (about 8.5e-6) that does not shrink with the output; "
-                   "at 2^19 tokens on one KV head the relative error (4.1e-3) leaves the gate")
-@pytest.mark.parametrize("k_axis", ["token", "channel"])
-def test_long_sequence_int4_channel_wise_v(k_axis):
-    """The long-context case that is known to leave the gate (16 splits)."""
+_LONG_L = (1 << 19) + 77
+_long_draws = {}
+
+
+def _long_inputs(bits, k_axis, v_axis):
+    """One sequence of 2^19 + 77 tokens on one KV head (zero-mean V, no
+    outliers); the fp32 draws are shared by every pairing."""
     import types
-    D, L = 128, (1 << 19) + 77
-    w = synth.Workload("one_long_cv", 1, 1, 4, D, [L], 4, k_axis, "channel", seed=97)
-    inp = types.SimpleNamespace(
-        w=w, k=synth.normal_f32((1, 1, L, D), 97, 1), v=synth.normal_f32((1, 1, L, D), 97, 2),
-        q=synth.f32_to_bf16_bits(synth.normal_f32((1, 4, D), 97, 3)), lens=np.asarray([L], np.int32),
-        table=None, num_pages=0)
+    D = 128
+    if not _long_draws:
+        _long_draws["k"] = synth.normal_f32((1, 1, _LONG_L, D), 97, 1)
+        _long_draws["v"] = synth.normal_f32((1, 1, _LONG_L, D), 97, 2)
+        _long_draws["q"] = synth.f32_to_bf16_bits(synth.normal_f32((1, 4, D), 97, 3))
+    w = synth.Workload("one_long", 1, 1, 4, D, [_LONG_L], bits, k_axis, v_axis, seed=97)
+    return types.SimpleNamespace(w=w, k=_long_draws["k"], v=_long_draws["v"], q=_long_draws["q"],
+                                 lens=np.asarray([_LONG_L], np.int32), table=None, num_pages=0)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("k_axis,v_axis", [("channel", "token"), ("token", "channel"),
+                                           ("token", "token"), ("channel", "channel")])
+def test_long_context_every_pairing(bits, k_axis, v_axis):
+    """The output of zero-mean V shrinks as 1/sqrt(L), so an error shared by
+    all outputs (a bias) shows first at long context: at 2^19 + 77 tokens the
+    outputs are about 2.5e-3. One split (each wave accumulates 2^17 tokens)
+    and 16 splits must meet the gate, keep the mean signed error below 1e-6
+    (the matrix unit truncates its sums; the folds are built so that the
+    truncation errors cancel) and agree with each other."""
+    inp = _long_inputs(bits, k_axis, v_axis)
     run = GpuRun(inp)
     ref = oracle_attention(inp, oracle_pack(inp))
-    o = run.decode(num_splits=16)
-    e2, ea = rel_l2(o, ref), max_abs(o, ref)
-    print(f"long int4 {k_axis[0]}c: rel_l2={e2:.3e} max_abs={ea:.3e}")
-    assert np.isfinite(o).all()
-    assert e2 <= REL_L2_TOL and ea <= MAX_ABS_TOL, (e2, ea)
+    outs = {}
+    for ns in (1, 16):
+        o = run.decode(num_splits=ns)
+        e2, ea, bias = rel_l2(o, ref), max_abs(o, ref), float(np.mean(o - ref))
+        print(f"long int{bits} {k_axis[0]}{v_axis[0]} splits {ns}: rel_l2={e2:.3e} "
+              f"max_abs={ea:.3e} mean_err={bias:+.2e}")
+        assert np.isfinite(o).all()
+        assert e2 <= REL_L2_TOL and ea <= MAX_ABS_TOL, (ns, e2, ea)
+        assert abs(bias) <= 1e-6, (ns, bias)
+        outs[ns] = o
+    assert rel_l2(outs[1], outs[16]) <= 5e-4
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_combine_matches_fp64_merge(bits):
+    """The combine kernel alone: the per-split partials (m, l, O) are read back
+    from the workspace and merged on the host in fp64,
+    O = sum_i 2^(m_i - M) l_i O_i / sum_i 2^(m_i - M) l_i; the kernel's fp32
+    merge must agree to rounding (about 1e-6), independently of how each
+    split rounded its own operands. Empty splits (m = -inf) take no part."""
+    import torch
+    import bit_quantized_kv_int2_amd as kvq
+    lens = [40000, 300, 0, 39000, 2047]
+    w = synth.Workload("combine", len(lens), 2, 8, 128, lens, bits, "channel", "token", seed=95,
+                       outliers=True)
+    inp = Inputs(w)
+    run = GpuRun(inp)
+    for ns in (7, 40, 157):
+        ws = kvq.workspace_tensor(run.fmt, w.batch, w.max_len, ns, device="cuda")
+        out = torch.empty((w.batch, w.num_q_heads, 128), dtype=torch.float32, device="cuda")
+        kvq.decode_attention_quant(run.fmt, run.q, run.cache, run.lens, w.max_len, SCALE, out,
+                                   num_splits=ns, workspace=ws)
+        torch.cuda.synchronize()
+        rows = w.batch * w.num_q_heads
+        # splits are whole 256-token quanta: the count actually used
+        quanta = -(-w.max_len // 256)
+        per = -(-quanta // ns) * 256
+        nsp = -(-w.max_len // per)
+        assert kvq.kvq_workspace_size(run.fmt, w.batch, w.max_len, ns) == rows * nsp * 130 * 4
+        f = ws.cpu().numpy().view(np.float32)
+        part_o = f[:rows * nsp * 128].reshape(rows, nsp, 128).astype(np.float64)
+        part_ml = f[rows * nsp * 128:rows * nsp * 130].reshape(rows, nsp, 2).astype(np.float64)
+        m, l = part_ml[..., 0], part_ml[..., 1]
+        M = m.max(1, keepdims=True)
+        live = np.isfinite(m)
+        wt = np.where(live, np.exp2(np.where(live, m - np.where(np.isfinite(M), M, 0), 0)) * l, 0.0)
+        den = wt.sum(1)
+        num = (wt[..., None] * part_o).sum(1)
+        ref = np.where(den[:, None] > 0, num / np.where(den[:, None] > 0, den[:, None], 1), 0.0)
+        got = out.cpu().numpy().reshape(rows, 128).astype(np.float64)
+        d = np.abs(got - ref).max()
+        e2 = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+        print(f"combine int{bits} splits {ns}: rel_l2={e2:.2e} max_abs={d:.2e}")
+        assert e2 <= 2e-6 and d <= 1e-6, (ns, e2, d)
+        # the empty sequence has no live split and a zero output
+        assert not live[2 * w.num_q_heads:3 * w.num_q_heads].any()
+        assert np.all(got[2 * w.num_q_heads:3 * w.num_q_heads] == 0)
 
 
 @pytest.mark.parametrize("bits", [2, 4])
