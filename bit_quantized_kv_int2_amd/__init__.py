@@ -85,6 +85,8 @@ def lib():
         L.decode_attention_quant.argtypes = [FP, _P, ctypes.POINTER(Cache), _P, _P, _I, _I, _I,
                                              ctypes.c_float, _P, _I, _I, _P, ctypes.c_size_t, _P]
         L.decode_attention_quant_fp8.argtypes = L.decode_attention_quant.argtypes
+        L.decode_attention_quant_noalloc.argtypes = [FP, _P, ctypes.POINTER(Cache), _P, _P, _I, _I,
+                                                     _I, ctypes.c_float, _P, _I, _I, _P]
         L.decode_attention_bf16.argtypes = [FP, _P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_float,
                                             _P, _I, _I, _P, ctypes.c_size_t, _P]
         L.kvq_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
@@ -96,7 +98,7 @@ def lib():
         for fn in ("kvq_check_format", "kvq_cache_sizes", "kvq_plan_splits",
                    "kvq_plan_splits_for_lengths", "kvq_workspace_size",
                    "kv_quantize_pack", "decode_attention_quant", "decode_attention_quant_fp8",
-                   "decode_attention_bf16",
+                   "decode_attention_quant_noalloc", "decode_attention_bf16",
                    "kvq_stream_read", "kv_append", "kvq_window_workspace_size",
                    "decode_attention_quant_window"):
             getattr(L, fn).restype = ctypes.c_int
@@ -219,6 +221,24 @@ def decode_attention_quant(fmt: Format, q, cache, seq_lens, max_len, softmax_sca
                                 _ptr(seq_lens), _ptr(page_table), maxp, B, max_len,
                                 float(softmax_scale), _ptr(out), od, num_splits,
                                 _ptr(workspace), workspace.numel(), _stream(stream)), name)
+    return out
+
+
+def decode_attention_quant_noalloc(fmt: Format, q, cache, seq_lens, max_len, softmax_scale, out,
+                                   page_table=None, num_splits=0, stream=None):
+    """decode_attention_quant without a workspace: the split partials go to
+    the library's per-GPU scratch array (no allocation in the call)."""
+    import torch
+    _require_gpu(q, seq_lens, out, page_table)
+    B = q.shape[0]
+    maxp = 0 if page_table is None else page_table.shape[1]
+    od = OUT_BF16 if out.dtype == torch.bfloat16 else OUT_F32
+    cs = _cache_struct(cache)
+    _check(lib().decode_attention_quant_noalloc(ctypes.byref(fmt), _ptr(q), ctypes.byref(cs),
+                                                _ptr(seq_lens), _ptr(page_table), maxp, B,
+                                                max_len, float(softmax_scale), _ptr(out), od,
+                                                num_splits, _stream(stream)),
+           "decode_attention_quant_noalloc")
     return out
 
 

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kvq_internal.h"
 
 using namespace kvq;
@@ -22,6 +24,34 @@ static kvq_status hip_status(hipError_t e) {
 static void clear_stale_error() { (void)hipGetLastError(); }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ---- the scratch of decode_attention_quant_noalloc ------------------------
+// The split partials (m, l, O) of the allocation-free entry point live in
+// this file-scope device array, one copy per GPU, held until the process
+// ends. In host code `scratch` names a host-side stand-in, not the device
+// copy: its device address comes from hipGetSymbolAddress, resolved once per
+// device with that device current, and only that address is ever used.
+static __device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static kvq_status scratch_address(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return hip_status(hipErrorInvalidDevice);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return hip_status(hipErrorInvalidSymbol);
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return KVQ_OK;
+}
 
 extern "C" {
 
@@ -293,7 +323,7 @@ static kvq_status decode_quant_impl(const kvq_format* f, const void* q, const kv
                                     int32_t max_pages_per_seq, int32_t batch, int32_t max_len,
                                     float softmax_scale, void* out, int32_t out_dtype,
                                     int32_t num_splits, void* workspace, size_t workspace_bytes,
-                                    void* stream, int fp8_qk) {
+                                    void* stream, int fp8_qk, bool use_scratch = false) {
   kvq_status st = kvq_check_format(f);
   if (st != KVQ_OK) return st;
   if (fp8_qk && f->group != kGroup) return KVQ_ERR_BAD_FORMAT;
@@ -308,6 +338,16 @@ static kvq_status decode_quant_impl(const kvq_format* f, const void* q, const kv
   st = resolve_splits(f, quant_slots(f), batch, max_len, num_splits, &split_tokens, &nsplit);
   if (st != KVQ_OK) return st;
   size_t need = workspace_bytes_for(f, batch, nsplit);
+  if (use_scratch) {
+    // every check above is host-only; the scratch address is the first HIP call
+    if (need > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
+    if (batch == 0) return KVQ_OK;
+    if (need > 0) {
+      st = scratch_address(&workspace);
+      if (st != KVQ_OK) return st;
+      workspace_bytes = KVQ_NOALLOC_SCRATCH_BYTES;
+    }
+  }
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
     if (!aligned16(workspace)) return KVQ_ERR_MISALIGNED;
@@ -368,6 +408,16 @@ kvq_status decode_attention_quant_fp8(const kvq_format* f, const void* q, const 
   return decode_quant_impl(f, q, cache, seq_lens, page_table, max_pages_per_seq, batch, max_len,
                            softmax_scale, out, out_dtype, num_splits, workspace, workspace_bytes,
                            stream, 1);
+}
+
+kvq_status decode_attention_quant_noalloc(const kvq_format* f, const void* q,
+                                          const kvq_cache* cache, const int32_t* seq_lens,
+                                          const int32_t* page_table, int32_t max_pages_per_seq,
+                                          int32_t batch, int32_t max_len, float softmax_scale,
+                                          void* out, int32_t out_dtype, int32_t num_splits,
+                                          void* stream) {
+  return decode_quant_impl(f, q, cache, seq_lens, page_table, max_pages_per_seq, batch, max_len,
+                           softmax_scale, out, out_dtype, num_splits, nullptr, 0, stream, 0, true);
 }
 
 kvq_status decode_attention_bf16(const kvq_format* f, const void* q, const void* k,

@@ -21,7 +21,8 @@
  *     thread). A device fault shows up at the caller's next synchronisation.
  *   - seq_lens lives in device memory; max_len (host) is an upper bound,
  *     0 <= seq_lens[b] <= max_len. A length of 0 gives a zero output row.
- *   - No state is kept between calls except the thread-local last HIP error.
+ *   - No state is kept between calls except the thread-local last HIP error
+ *     (and, for decode_attention_quant_noalloc only, its per-GPU scratch).
  *
  * Cache layout (layout_version 2; little-endian; D = head_dim = 128, b = bits,
  * G = group, tpw = 32/b tokens per V word, Lp = max_len rounded up to a
@@ -210,6 +211,34 @@ kvq_status decode_attention_quant_fp8(const kvq_format* fmt, const void* q,
                                       int32_t batch, int32_t max_len, float softmax_scale,
                                       void* out, int32_t out_dtype, int32_t num_splits,
                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * decode_attention_quant_noalloc -- decode_attention_quant for callers that
+ * cannot allocate device memory or pass a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). The
+ * per-split partials go to a device array of KVQ_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every GPU it runs on until the process ends; the call
+ * itself allocates nothing (no hipMalloc, no allocating library routine).
+ *   Arguments as decode_attention_quant without the workspace; the current
+ *   device must be the one the stream runs on.
+ *   Limit: the split partials must fit, batch * Hq * splits * (D + 2) * 4
+ *   bytes <= KVQ_NOALLOC_SCRATCH_BYTES (kvq_workspace_size() gives the
+ *   figure); larger calls return KVQ_ERR_WORKSPACE before any HIP call. One
+ *   split needs no scratch.
+ *   The array keeps the last call's contents; nothing in it needs clearing
+ *   (every split writes its partial before the merge reads it). Calls on
+ *   one GPU share the array: calls that may overlap in time (different
+ *   streams, or threads) race and must be serialised by the caller.
+ *   Errors as decode_attention_quant; KVQ_ERR_HIP also if the array's device
+ *   address cannot be resolved (first call on a device).
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+kvq_status decode_attention_quant_noalloc(const kvq_format* fmt, const void* q,
+                                          const kvq_cache* cache, const int32_t* seq_lens,
+                                          const int32_t* page_table, int32_t max_pages_per_seq,
+                                          int32_t batch, int32_t max_len, float softmax_scale,
+                                          void* out, int32_t out_dtype, int32_t num_splits,
+                                          void* stream);
 
 /*
  * decode_attention_bf16 -- the same decode over an unquantised bf16 cache

@@ -210,6 +210,29 @@ def test_decode_validation_without_gpu(L):
     assert _call_decode(L, bad, cache=(A, A, A, A), lens=A, out=A, q=A) == BADFMT
 
 
+def test_noalloc_limit_without_gpu(L):
+    """decode_attention_quant_noalloc rejects calls whose split partials do
+    not fit its scratch array before any HIP call, and does nothing for an
+    empty batch (both paths run here, where there is no device)."""
+    f = kvq.make_format(4, "channel", "token", 8)
+    A = 4096
+    c = kvq.Cache(A, A, A, A)
+    limit = 32 << 20
+
+    def call(B, max_len, ns):
+        return L.decode_attention_quant_noalloc(ctypes.byref(f), A, ctypes.byref(c), A, None, 0,
+                                                B, max_len, ctypes.c_float(0.1), A, 0, ns, None)
+    # 127 sequences x 32 query heads x 16 splits x 130 floats: just over the limit
+    assert kvq.kvq_workspace_size(f, 127, 4096, 16) > limit
+    assert call(127, 4096, 16) == WORKSPACE
+    # 126 sequences fit (the check is on the bytes, not the shape)
+    assert kvq.kvq_workspace_size(f, 126, 4096, 16) <= limit
+    assert call(0, 4096, 16) == OK
+    assert call(-1, 4096, 16) == BADSHAPE
+    assert L.decode_attention_quant_noalloc(None, A, ctypes.byref(c), A, None, 0, 1, 128,
+                                            ctypes.c_float(0.1), A, 0, 0, None) == NULLP
+
+
 def test_pack_and_bf16_validation_without_gpu(L):
     f = kvq.make_format(2, "token", "channel", 2)
     A = 4096
