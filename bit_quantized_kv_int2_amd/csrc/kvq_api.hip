@@ -224,8 +224,14 @@ static kvq_status resolve_splits(const kvq_format* f, long slots, int batch, int
   if (req > quanta) return KVQ_ERR_BAD_SHAPE;
   *split_tokens = plan_split_tokens(slots, batch, f->num_kv_heads, max_len, req);
   *nsplit = splits_for(max_len, *split_tokens);
-  if (decode_grid_blocks((long)batch * f->num_kv_heads, *nsplit) > kMaxGridBlocks) return KVQ_ERR_BAD_SHAPE;
+  if (decode_grid_blocks((long)batch * f->num_kv_heads, *nsplit) >= kMaxGridBlocks) return KVQ_ERR_BAD_SHAPE;
   return KVQ_OK;
+}
+
+// The combine kernel runs batch * Hq work-groups of kHeadDim work-items; the
+// whole grid must count its work-items in 32 bits.
+static bool combine_grid_fits(const kvq_format* f, int batch) {
+  return (long)batch * f->num_q_heads * kHeadDim < (1L << 32);
 }
 
 static size_t workspace_bytes_for(const kvq_format* f, int batch, int nsplit) {
@@ -337,6 +343,7 @@ static kvq_status decode_quant_impl(const kvq_format* f, const void* q, const kv
   int split_tokens, nsplit;
   st = resolve_splits(f, quant_slots(f), batch, max_len, num_splits, &split_tokens, &nsplit);
   if (st != KVQ_OK) return st;
+  if (nsplit > 1 && !combine_grid_fits(f, batch)) return KVQ_ERR_BAD_SHAPE;
   size_t need = workspace_bytes_for(f, batch, nsplit);
   if (use_scratch) {
     // every check above is host-only; the scratch address is the first HIP call
@@ -438,6 +445,7 @@ kvq_status decode_attention_bf16(const kvq_format* f, const void* q, const void*
   int split_tokens, nsplit;
   st = resolve_splits(f, kBf16Slots, batch, max_len, num_splits, &split_tokens, &nsplit);
   if (st != KVQ_OK) return st;
+  if (nsplit > 1 && !combine_grid_fits(f, batch)) return KVQ_ERR_BAD_SHAPE;
   size_t need = workspace_bytes_for(f, batch, nsplit);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
@@ -554,6 +562,7 @@ kvq_status decode_attention_quant_window(const kvq_format* f, const void* q,
   int split_tokens, nsplit;
   st = resolve_splits(f, quant_slots(f), batch, max_len, num_splits, &split_tokens, &nsplit);
   if (st != KVQ_OK) return st;
+  if (!combine_grid_fits(f, batch)) return KVQ_ERR_BAD_SHAPE;  // the window path always merges
   const size_t need = window_workspace_bytes(f, batch, nsplit);
   if (!workspace || workspace_bytes < need) return KVQ_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KVQ_ERR_MISALIGNED;

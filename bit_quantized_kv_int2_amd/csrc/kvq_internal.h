@@ -91,7 +91,7 @@ struct AppendArgs {
 // whenever X is even. Index counts are padded to whole rounds of 8 rows; the
 // padding work-groups return at once.
 inline long decode_grid_blocks(long rows, int ns) { return ((rows + 7) / 8) * 8 * (long)ns; }
-constexpr long kMaxGridBlocks = 1L << 24;  // 256-thread work-groups in a 32-bit grid
+constexpr long kMaxGridBlocks = 1L << 24;  // 256-thread work-groups: a grid must stay below it (32-bit work-item count)
 struct WorkItem {
   int sp, h, b;
   bool live;

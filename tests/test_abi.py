@@ -119,11 +119,12 @@ def test_split_plan_and_workspace(L):
     assert kvq.kvq_workspace_size(f, 2, 32768, 3) == 2 * 32 * 3 * 130 * 4
     with pytest.raises(kvq.KvqError):
         kvq.kvq_workspace_size(f, 2, 1024, 5)
-    # a decode launch is a 1-D grid of at most 2^24 work-groups: splits x rows,
-    # rows (sequences x KV heads) padded to a multiple of 8
-    assert kvq.kvq_workspace_size(f, 4096, 1 << 20, 512) == 4096 * 32 * 512 * 130 * 4
+    # a decode launch is a 1-D grid of fewer than 2^24 work-groups of 256
+    # work-items (a 32-bit count): splits x rows, rows (sequences x KV heads)
+    # padded to a multiple of 8
+    assert kvq.kvq_workspace_size(f, 4096, 1 << 20, 256) == 4096 * 32 * 256 * 130 * 4
     with pytest.raises(kvq.KvqError):
-        kvq.kvq_workspace_size(f, 4096, 1 << 20, 1024)
+        kvq.kvq_workspace_size(f, 4096, 1 << 20, 512)
     with pytest.raises(kvq.KvqError):
         kvq.kvq_workspace_size(f, 2, 1024, -1)
 
@@ -208,6 +209,27 @@ def test_decode_validation_without_gpu(L):
                         max_len=4096) == BADSHAPE
     bad = kvq.make_format(3, "channel", "token", 1)
     assert _call_decode(L, bad, cache=(A, A, A, A), lens=A, out=A, q=A) == BADFMT
+
+
+def test_grid_limits_without_gpu(L):
+    """Grids must count their work-items in 32 bits, checked before any launch:
+    2^24 decode work-groups of 256 work-items is one grid too many, and the
+    merge of the window path (always launched) needs batch * Hq * 128 < 2^32."""
+    A = 4096
+    c = kvq.Cache(A, A, A, A)
+    n = ctypes.c_size_t()
+    f = kvq.make_format(2, "channel", "token", 64)
+    # 32768 sequences x 64 KV heads x 8 splits of 256 tokens = 2^24 work-groups
+    assert L.kvq_workspace_size(ctypes.byref(f), 32768, 2048, 8, ctypes.byref(n)) == BADSHAPE
+    assert L.kvq_workspace_size(ctypes.byref(f), 32768, 2048, 7, ctypes.byref(n)) == OK
+    assert L.decode_attention_quant(ctypes.byref(f), A, ctypes.byref(c), A, None, 0, 32768, 2048,
+                                    ctypes.c_float(0.1), A, 0, 8, A, 1 << 40, None) == BADSHAPE
+    # one split: 65535 x 129 KV heads is 8.45 M decode work-groups (fits), but
+    # the window path's merge would run 65535 x 516 rows of 128 work-items
+    fw = kvq.make_format(2, "channel", "token", 129)
+    assert L.decode_attention_quant_window(ctypes.byref(fw), A, ctypes.byref(c), A, A, A, None, 0,
+                                           65535, 128, ctypes.c_float(0.1), A, 0, 1, A, 1 << 40,
+                                           None) == BADSHAPE
 
 
 def test_noalloc_limit_without_gpu(L):
