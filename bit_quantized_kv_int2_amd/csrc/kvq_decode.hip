@@ -13,8 +13,9 @@
 //
 // gfx950 mapping
 //   * Matrix unit: v_mfma_f32_16x16x32_f16. A = codes (16 rows x 32 k),
-//     B = folded query / probabilities (32 k x 16 columns); the 4 query heads
-//     of a KV head fill columns 0-3 and are repeated in columns 4-15.
+//     B = folded query / probabilities (32 k x 16 columns). In q.K^T the
+//     columns are 4 heads x 4 token quarters (block diagonal over k); in P.V
+//     the 4 query heads of a KV head fill columns 0-3 and the others are zero.
 //   * Operand construction: a 2- or 4-bit code ANDed out of its packed 32-bit
 //     word, left at its bit offset inside a 16-bit lane with every other bit
 //     zero, is the binary16 subnormal c * 2^k * 2^-24 (k = the code's bit
@@ -784,11 +785,18 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
           pk[0] = pack_f16x2(P[0] * cw[0], P[1] * cw[0]);
           pk[1] = pack_f16x2(P[2] * cw[1], P[3] * cw[1]);
         }
+        // B columns 0-3 carry the four heads; the other twelve only repeated
+        // them and nothing reads their results: zeros there cost 8 selects
+        // per iteration and take switching power off the matrix unit, whose
+        // clock this loop follows (measured 2 % faster, results unchanged)
         u4 bp[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k)
 #pragma unroll
-          for (int m = 0; m < 4; ++m) bp[k][m] = (uint32_t)__builtin_amdgcn_ds_bpermute(src[k][m >> 1], (int)pk[m & 1]);
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute(src[k][m >> 1], (int)pk[m & 1]);
+            bp[k][m] = mn_ < 4 ? v : 0u;
+          }
 
         // PV: 8 channel tiles + the extra tile, 2 k-steps of 32 tokens
         if (VAX == KVQ_TOKEN_WISE) {

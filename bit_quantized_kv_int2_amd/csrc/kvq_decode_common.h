@@ -203,7 +203,10 @@ __device__ inline uint32_t cpl(uint32_t sel, uint32_t b) {
   // (S0 ? S1 : S2) with S1 = 0: truth table indexed by 4 S0 + 2 S1 + S2.
   // Not inline asm: the compiler does not see into asm, so it would not
   // insert the wait states a VALU write needs after a matrix instruction
-  // that still reads the register.
+  // that still reads the register. The mask is held in a scalar register
+  // (the instruction takes one): left to itself the compiler keeps it in a
+  // vector register, which the tightest kernels cannot spare.
+  asm("" : "+s"(b));
   return (uint32_t)__builtin_amdgcn_bitop3_b32((int)sel, 0, (int)b, 0x0A);
 }
 // unpack2 / unpack4 with the odd slots mirrored (P.V A operands)
