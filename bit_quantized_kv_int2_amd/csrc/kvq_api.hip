@@ -293,6 +293,10 @@ kvq_status kv_quantize_pack(const kvq_format* f, const float* k, const float* v,
   st = check_common(f, seq_lens, page_table, max_pages_per_seq, batch, max_len);
   if (st != KVQ_OK) return st;
   if (batch == 0 || max_len == 0) return KVQ_OK;
+  // one work-group per 128-token tile of a (sequence, KV head), counted in 31
+  // bits (2^31 tiles would be 128 TiB of fp32 input per tensor)
+  if ((long)batch * f->num_kv_heads * (padded_len(max_len) / kGroup) >= (1L << 31))
+    return KVQ_ERR_BAD_SHAPE;
   PackArgs a;
   memset(&a, 0, sizeof a);
   a.k = k;

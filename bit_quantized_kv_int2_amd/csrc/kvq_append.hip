@@ -67,16 +67,16 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
         mn = mx = bf16_f32(row[gi % G]);
         for (int e = 1; e < G; ++e) {
           const float v = bf16_f32(row[(gi + e) % G]);
-          mn = fminf(mn, v);
-          mx = fmaxf(mx, v);
+          mn = __builtin_elementwise_minimum(mn, v);
+          mx = __builtin_elementwise_maximum(mx, v);
         }
         p = pair_token(g, b, h, g0 + t, j, ng);
       } else {  // group = channel gi over the 128 tokens
         mn = mx = bf16_f32(w[gi]);
         for (int t = 1; t < kGroup; ++t) {
           const float v = bf16_f32(w[t * kHeadDim + gi]);
-          mn = fminf(mn, v);
-          mx = fmaxf(mx, v);
+          mn = __builtin_elementwise_minimum(mn, v);
+          mx = __builtin_elementwise_maximum(mx, v);
         }
         p = pair_channel(g, b, h, g0, gi);
       }

@@ -1,7 +1,7 @@
 // Device-side quantiser and cache addressing shared by the bulk pack and the
 // append kernels (internal). The rule is the one kv_quantize_pack documents:
-// min/max in fp32, s = fp16((max - min) / (2^b - 1)) with an IEEE fp32
-// division, z = fp16(min), code = clamp(rint((x - z) / s), 0, 2^b - 1) from
+// min/max in fp32 (-0 below +0), s = fp16((max - min) / (2^b - 1)) with an
+// IEEE fp32 division, z = fp16(min), code = clamp(rint((x - z) / s), 0, 2^b - 1) from
 // the stored fp16 s and z, code 0 when s == 0.
 #pragma once
 

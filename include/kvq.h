@@ -50,7 +50,8 @@
  *                           its first token (the other page's slot is unused).
  *   Quantisation of a group: s = fp16((max - min) / (2^b - 1)) with an fp32
  *   division, z = fp16(min), c = clamp(rint((x - z) / s), 0, 2^b - 1) in fp32
- *   with the stored s and z (c = 0 when s == 0). Codes of tokens at or past a
+ *   with the stored s and z (c = 0 when s == 0); min and max order -0 below
+ *   +0, and the values are finite. Codes of tokens at or past a
  *   sequence's length, within the written extent, are 0.
  */
 #ifndef KVQ_H

@@ -23,7 +23,8 @@
  * storage, tie-breaking, the bit layout) follow the library's documented
  * format: s = fp16((max - min) / (2^b - 1)) with an fp32 division, z =
  * fp16(min), c = clamp(rint((x - z) / s), 0, 2^b - 1) in fp32 using the
- * stored fp16 s and z, c = 0 when s == 0.
+ * stored fp16 s and z, c = 0 when s == 0; min and max order -0 below +0
+ * (finite values).
  *
  * Packed layout, version 2 (little-endian; Lp = max_len rounded up to 128;
  * paged caches use 64-token pages and a page table). Codes live in 64-token
@@ -137,11 +138,14 @@ double orc_bf16_to_f64(uint16_t h) {
 void orc_quantize_group(const float* x, long stride, int n, int bits, uint16_t* s_out,
                         uint16_t* z_out, uint8_t* codes, long cstride) {
   const int qmax = (1 << bits) - 1;
+  /* min and max as a total order on the (finite) values with -0 below +0,
+   * so that the stored z of a group holding both zeros does not depend on
+   * the order the group is scanned in */
   float mn = x[0], mx = x[0];
   for (int i = 1; i < n; ++i) {
     float v = x[(long)i * stride];
-    if (v < mn) mn = v;
-    if (v > mx) mx = v;
+    if (v < mn || (v == mn && signbit(v))) mn = v;
+    if (v > mx || (v == mx && !signbit(v))) mx = v;
   }
   volatile float range = mx - mn;          /* fp32 subtraction */
   volatile float s32 = range / (float)qmax; /* fp32 IEEE division */

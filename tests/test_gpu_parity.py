@@ -66,6 +66,60 @@ def test_constant_groups(bits, k_axis, v_axis):
     _check(inp, GpuRun(inp), label=f"const_int{bits}_{k_axis[0]}{v_axis[0]}")
 
 
+def _tie_values(rng, shape, z, s, qmax, G):
+    """z + m s / 2 for m in [0, 2 qmax] (odd m: exactly on a rounding tie of
+    the grid z + c s), some moved one ulp up or down; rows 128 k and channels
+    G j hold z, rows 128 k + 1 and channels G j + 1 hold z + qmax s, so that
+    every group's min and max are z and z + qmax s and its stored (s, z) are
+    exactly s and z."""
+    m = rng.integers(0, 2 * qmax + 1, size=shape)
+    x = (np.float32(z) + m.astype(np.float32) * np.float32(s / 2)).astype(np.float32)
+    step = rng.integers(-1, 2, size=shape)
+    step[m == 0] = np.maximum(step[m == 0], 0)              # never below the min
+    step[m == 2 * qmax] = np.minimum(step[m == 2 * qmax], 0)  # never above the max
+    x = np.where(step > 0, np.nextafter(x, np.float32(np.inf)),
+                 np.where(step < 0, np.nextafter(x, np.float32(-np.inf)), x)).astype(np.float32)
+    t = np.arange(shape[-2])[:, None]
+    d = np.arange(shape[-1])[None, :]
+    lo = (t % 128 == 0) | (d % G == 0)
+    hi = ((t % 128 == 1) | (d % G == 1)) & ~lo
+    x[..., lo] = np.float32(z)
+    x[..., hi] = np.float32(z + qmax * s)
+    return x
+
+
+@pytest.mark.parametrize("bits,k_axis,v_axis,group,page", [
+    (2, "channel", "token", 128, 0), (4, "token", "channel", 128, 0),
+    (2, "token", "token", 32, 0), (4, "token", "token", 64, 0),
+    (2, "channel", "channel", 128, 64), (4, "channel", "token", 128, 64)])
+def test_pack_exact_ties_and_signed_zeros(bits, k_axis, v_axis, group, page):
+    """Values on and one ulp beside the rounding ties of their group's grid,
+    and groups holding zeros of both signs, pack byte for byte as the oracle
+    packs them: the pack's multiply-by-1/s shortcut must hand every such
+    element to the IEEE division, and its min/max must order -0 below +0."""
+    lens = [300, 129, 64]
+    extra = {"group": group} if group != 128 else {}
+    w = synth.Workload("ties", len(lens), 2, 8, 128, lens, bits, k_axis, v_axis, seed=73,
+                       page_size=page, extra=extra)
+    inp = Inputs(w)
+    qmax = (1 << bits) - 1
+    rng = np.random.default_rng(7300 + bits)
+    for name in ("k", "v"):
+        x = getattr(inp, name)
+        for h, (z, s) in enumerate([(-1.0, 0.25), (0.375, 0.0625)]):
+            x[:2, h] = _tie_values(rng, x[:2, h].shape, z, s, qmax, group)
+        # sequence 2: zeros of both signs among a few positive values
+        x[2] = rng.choice(np.array([0.0, -0.0, 0.5, 1.0], np.float32), size=x[2].shape,
+                          p=[0.45, 0.05, 0.25, 0.25])
+    run = GpuRun(inp)
+    orc = oracle_pack(inp)
+    ok, msg = cache_bytes_equal(run.cache_host(), orc)
+    assert ok, msg
+    # the test is not vacuous: exact ties occur, and some stored z are -0
+    sz = np.concatenate([orc[2].ravel(), orc[3].ravel()])
+    assert (sz[1::2] == 0x8000).any() and (sz[1::2] == 0).any()
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 def test_split_invariance_and_determinism(bits):
     w = synth.Workload("splits", 2, 2, 8, 128, [4096, 3000], bits, "channel", "token", seed=51,

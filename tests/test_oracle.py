@@ -74,6 +74,17 @@ def test_quantizer_hand_cases(orc):
     x = np.linspace(0.0, 1.0, 128).astype(np.float32)
     s, z, c = orc.quantize_group(x, 2)
     assert s == np.float16(np.float32(1.0) / np.float32(3.0)).view(np.uint16)
+    # min and max order -0 below +0 (IEEE 754-2019 minimum / maximum), so z
+    # does not depend on where the zeros sit in the group
+    for vals in ([0.0, -0.0, 1.0], [-0.0, 0.0, 1.0], [1.0, 0.0, -0.0], [1.0, -0.0, 0.0, -0.0]):
+        s, z, c = orc.quantize_group(np.array(vals, np.float32), 2)
+        assert z == 0x8000 and s == np.float16(1.0 / 3.0).view(np.uint16), vals
+    for vals in ([0.0, 0.0, 1.0], [1.0, 0.0]):
+        s, z, c = orc.quantize_group(np.array(vals, np.float32), 2)
+        assert z == 0x0000, vals
+    # a group of zeros of both signs is a constant group: s = 0, z = -0
+    s, z, c = orc.quantize_group(np.array([0.0, -0.0, 0.0], np.float32), 4)
+    assert s == 0 and z == 0x8000 and not c.any()
 
 
 @pytest.mark.parametrize("bits", [2, 4])
