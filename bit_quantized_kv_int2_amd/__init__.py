@@ -80,6 +80,7 @@ def lib():
         L.kvq_cache_sizes.argtypes = [FP, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]
         L.kvq_plan_splits.argtypes = [FP, _I, _I, ctypes.POINTER(ctypes.c_int32)]
         L.kvq_plan_splits_for_lengths.argtypes = [FP, _I, _I, _P, ctypes.POINTER(ctypes.c_int32)]
+        L.kvq_auto_plan.argtypes = [FP, _I, _I, _P] + [ctypes.POINTER(ctypes.c_int32)] * 3
         L.kvq_workspace_size.argtypes = [FP, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]
         L.kv_quantize_pack.argtypes = [FP, _P, _P, _P, _P, _I, _I, _I, ctypes.POINTER(Cache), _P]
         L.decode_attention_quant.argtypes = [FP, _P, ctypes.POINTER(Cache), _P, _P, _I, _I, _I,
@@ -96,7 +97,7 @@ def lib():
                                                     _I, _I, _I, ctypes.c_float, _P, _I, _I, _P,
                                                     ctypes.c_size_t, _P]
         for fn in ("kvq_check_format", "kvq_cache_sizes", "kvq_plan_splits",
-                   "kvq_plan_splits_for_lengths", "kvq_workspace_size",
+                   "kvq_plan_splits_for_lengths", "kvq_auto_plan", "kvq_workspace_size",
                    "kv_quantize_pack", "decode_attention_quant", "decode_attention_quant_fp8",
                    "decode_attention_quant_noalloc", "decode_attention_bf16",
                    "kvq_stream_read", "kv_append", "kvq_window_workspace_size",
@@ -140,6 +141,18 @@ def kvq_plan_splits_for_lengths(fmt: Format, seq_lens, max_len: int) -> int:
                                              lens.ctypes.data_as(ctypes.c_void_p),
                                              ctypes.byref(n)), "kvq_plan_splits_for_lengths")
     return int(n.value)
+
+
+def kvq_auto_plan(fmt: Format, seq_lens, max_len: int):
+    """(split_tokens, items, grid) of the quantised decode's auto plan for these
+    lengths (host copy of the rule the decode applies on the device)."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    out = [ctypes.c_int32() for _ in range(3)]
+    _check(lib().kvq_auto_plan(ctypes.byref(fmt), int(lens.size), int(max_len),
+                               lens.ctypes.data_as(ctypes.c_void_p), *[ctypes.byref(o) for o in out]),
+           "kvq_auto_plan")
+    return tuple(int(o.value) for o in out)
 
 
 def kvq_workspace_size(fmt: Format, batch: int, max_len: int, num_splits: int = 0) -> int:

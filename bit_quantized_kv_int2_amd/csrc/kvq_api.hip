@@ -240,6 +240,67 @@ static size_t workspace_bytes_for(const kvq_format* f, int batch, int nsplit) {
   return rows * nsplit * (kHeadDim + 2) * sizeof(float);
 }
 
+// The auto plan of the quantised decode runs on the device (lengths_split)
+// when the max_len plan splits the rows (ns_auto >= 2); with one split per
+// row (a batch that fills the chip by its rows) the decode keeps that plan.
+// The host fixes the device plan's grid and workspace from batch and max_len
+// alone. Workspace: a 16-byte header (the split chosen, the plan mode), the
+// first work-item of each (sequence, KV head) row, then per work-item
+// partials O [4][D] and (m, l) [4] (mode 0 uses them as [row][ns_auto]).
+struct AutoPlan {
+  int auto_tokens;  // the max_len plan's split
+  int ns_auto;      // its split count
+  bool device;      // the plan is made on the device
+  long items;       // grid (device plan: a bound on the plan's work-items)
+  size_t bytes;     // workspace
+  size_t row_first_off, part_o_off, part_ml_off;
+};
+
+static kvq_status auto_plan_for(const kvq_format* f, int batch, int max_len, AutoPlan* p) {
+  const long slots = quant_slots(f);
+  p->auto_tokens = plan_split_tokens(slots, batch, f->num_kv_heads, max_len, 0);
+  p->ns_auto = splits_for(max_len, p->auto_tokens);
+  const long rows = (long)batch * f->num_kv_heads;
+  p->device = p->ns_auto >= 2;
+  p->items = p->device ? plan_item_bound(rows, p->ns_auto, slots) : decode_grid_blocks(rows, p->ns_auto);
+  if (p->items >= kMaxGridBlocks) return KVQ_ERR_BAD_SHAPE;
+  p->row_first_off = 16;
+  p->part_o_off = p->row_first_off + (((size_t)rows * 4 + 15) / 16) * 16;
+  p->part_ml_off = p->part_o_off + (size_t)p->items * kGqa * kHeadDim * sizeof(float);
+  p->bytes = p->device ? p->part_ml_off + (size_t)p->items * kGqa * 2 * sizeof(float) : 0;
+  return KVQ_OK;
+}
+
+kvq_status kvq_auto_plan(const kvq_format* f, int32_t batch, int32_t max_len,
+                         const int32_t* seq_lens_host, int32_t* split_tokens, int32_t* items,
+                         int32_t* grid) {
+  kvq_status st = kvq_check_format(f);
+  if (st != KVQ_OK) return st;
+  if (!split_tokens || !items || !grid || (batch > 0 && !seq_lens_host)) return KVQ_ERR_NULL_POINTER;
+  if (batch < 0 || max_len < 0) return KVQ_ERR_BAD_SHAPE;
+  AutoPlan p;
+  st = auto_plan_for(f, batch, max_len, &p);
+  if (st != KVQ_OK) return st;
+  long long total = 0;
+  int longest = 0;
+  for (int b = 0; b < batch; ++b) {
+    int L = seq_lens_host[b] < 0 ? 0 : (seq_lens_host[b] > max_len ? max_len : seq_lens_host[b]);
+    total += L;
+    if (L > longest) longest = L;
+  }
+  const int S = p.device ? lengths_split(total, longest, batch, f->num_kv_heads, quant_slots(f), p.auto_tokens)
+                         : p.auto_tokens;
+  long n = 0;
+  for (int b = 0; b < batch; ++b) {
+    int L = seq_lens_host[b] < 0 ? 0 : (seq_lens_host[b] > max_len ? max_len : seq_lens_host[b]);
+    n += L > 0 ? (long)f->num_kv_heads * ((L + S - 1) / S) : 0;
+  }
+  *split_tokens = S;
+  *items = (int32_t)n;
+  *grid = (int32_t)p.items;
+  return KVQ_OK;
+}
+
 kvq_status kvq_workspace_size(const kvq_format* f, int32_t batch, int32_t max_len,
                               int32_t num_splits, size_t* bytes) {
   kvq_status st = kvq_check_format(f);
@@ -253,6 +314,12 @@ kvq_status kvq_workspace_size(const kvq_format* f, int32_t batch, int32_t max_le
   st = resolve_splits(f, kBf16Slots, batch, max_len, num_splits, &split_tokens, &nb);
   if (st != KVQ_OK) return st;
   *bytes = workspace_bytes_for(f, batch, nq > nb ? nq : nb);
+  if (num_splits == 0) {  // the quantised decode's plan on the device
+    AutoPlan p;
+    st = auto_plan_for(f, batch, max_len, &p);
+    if (st != KVQ_OK) return st;
+    if (p.bytes > *bytes) *bytes = p.bytes;
+  }
   return KVQ_OK;
 }
 
@@ -347,8 +414,15 @@ static kvq_status decode_quant_impl(const kvq_format* f, const void* q, const kv
   int split_tokens, nsplit;
   st = resolve_splits(f, quant_slots(f), batch, max_len, num_splits, &split_tokens, &nsplit);
   if (st != KVQ_OK) return st;
-  if (nsplit > 1 && !combine_grid_fits(f, batch)) return KVQ_ERR_BAD_SHAPE;
-  size_t need = workspace_bytes_for(f, batch, nsplit);
+  AutoPlan ap;
+  bool dev_plan = false;
+  if (num_splits == 0) {
+    st = auto_plan_for(f, batch, max_len, &ap);
+    if (st != KVQ_OK) return st;
+    dev_plan = ap.device;
+  }
+  if ((dev_plan || nsplit > 1) && !combine_grid_fits(f, batch)) return KVQ_ERR_BAD_SHAPE;
+  size_t need = dev_plan ? ap.bytes : workspace_bytes_for(f, batch, nsplit);
   if (use_scratch) {
     // every check above is host-only; the scratch address is the first HIP call
     if (need > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
@@ -386,7 +460,18 @@ static kvq_status decode_quant_impl(const kvq_format* f, const void* q, const kv
   a.direct_out = nsplit == 1;
   a.part_stride = nsplit;
   a.fp8_qk = fp8_qk;
-  if (nsplit > 1) {
+  if (dev_plan) {
+    unsigned char* w = (unsigned char*)workspace;
+    a.dev_plan = 1;
+    a.split_tokens = ap.auto_tokens;
+    a.num_splits = ap.ns_auto;
+    a.plan_items = (int)ap.items;
+    a.plan_slots = (int)quant_slots(f);
+    a.plan_hdr = (int*)w;
+    a.row_first = (int*)(w + ap.row_first_off);
+    a.part_o = (float*)(w + ap.part_o_off);
+    a.part_ml = (float*)(w + ap.part_ml_off);
+  } else if (nsplit > 1) {
     const size_t rows = (size_t)batch * f->num_q_heads;
     a.part_o = (float*)workspace;
     a.part_ml = a.part_o + rows * nsplit * kHeadDim;
@@ -394,7 +479,9 @@ static kvq_status decode_quant_impl(const kvq_format* f, const void* q, const kv
   hipStream_t s = (hipStream_t)stream;
   clear_stale_error();
   st = hip_status(launch_decode_quant(*f, a, s));
-  if (st != KVQ_OK || nsplit == 1) return st;
+  if (st != KVQ_OK) return st;
+  if (dev_plan) return hip_status(launch_combine_plan(a, s));
+  if (nsplit == 1) return st;
   return hip_status(launch_combine(a.part_o, a.part_ml, batch * f->num_q_heads, nsplit, out,
                                    a.out_bf16, s));
 }

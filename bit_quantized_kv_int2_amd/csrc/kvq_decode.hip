@@ -65,26 +65,27 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   // work-item and work-group ids straight from the builtins: this file is
   // built with the IEEE mode bit cleared, which keeps the device library's
   // id helpers from being inlined
-  const WorkItem wi = work_item(__builtin_amdgcn_workgroup_id_x(), a.num_kv_heads, a.batch, a.num_splits);
-  if (!wi.live) return;  // padding to whole rounds of 8 rows
-  const int sp = wi.sp, h = wi.h, b = wi.b;
+  static_assert(M::TOTAL >= (8 + kThreads) * 4, "find_split borrows the start of the LDS");
+  const Split ws = find_split(a, (int*)lds);
+  if (!ws.live) return;  // padding, or past the plan's work-items
+  const int sp = ws.sp, h = ws.h, b = ws.b;
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keeps addressing scalar
   const int H = a.num_kv_heads, Hq = H * kGqa;
   int L = min(max(a.seq_lens[b], 0), a.max_len);  // contract: 0 <= len <= max_len
   if (a.len_mode == 1) L -= L % kGroup;  // whole groups only (the rest is a residual window)
-  const int tb = sp * a.split_tokens;
-  const int te = min(tb + a.split_tokens, L);
+  const int tb = sp * ws.S;
+  const int te = min(tb + ws.S, L);
   const long row0 = (long)b * Hq + (long)h * kGqa;  // first query head row of this KV head
 
   if (te <= tb) {  // nothing in this split (or an empty sequence)
     for (int e = tid; e < kGqa * kHeadDim; e += kThreads) {
       int hh = e / kHeadDim, d = e % kHeadDim;
-      if (a.direct_out) {
+      if (ws.direct) {
         if (a.out_bf16) ((uint16_t*)a.out)[(row0 + hh) * kHeadDim + d] = 0;
         else ((float*)a.out)[(row0 + hh) * kHeadDim + d] = 0.f;
       } else {
-        const long pr = (row0 + hh) * a.part_stride + a.part_base + sp;
+        const long pr = ws.pbase + hh * ws.pmul;
         a.part_o[pr * kHeadDim + d] = 0.f;
         if (d == 0) {
           a.part_ml[pr * 2] = -INFINITY;
@@ -961,7 +962,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float o0 = n0 * inv, o1 = n1 * inv;
     const long row = row0 + qh;
-    if (a.direct_out) {
+    if (ws.direct) {
       if (a.out_bf16) {
         __bf16 b0 = (__bf16)o0, b1 = (__bf16)o1;
         uint32_t pk = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
@@ -971,7 +972,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         *(float2*)((float*)a.out + row * kHeadDim + d) = make_float2(o0, o1);
       }
     } else {
-      const long pr = row * a.part_stride + a.part_base + sp;
+      const long pr = ws.pbase + qh * ws.pmul;
       *(float2*)(a.part_o + pr * kHeadDim + d) = make_float2(o0, o1);
       if (d == 0) {
         // m in log2 units, l in units of 2^(S - m)
@@ -982,32 +983,75 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   }
 }
 
-// LSE combine of the split partials: O = sum_i 2^(m_i - M) l_i O_i / sum_i 2^(m_i - M) l_i.
-__global__ void __launch_bounds__(128) combine_kernel(const float* part_o, const float* part_ml,
-                                                      int num_splits, void* out, int out_bf16) {
-  const long row = __builtin_amdgcn_workgroup_id_x();
-  const int d = __builtin_amdgcn_workitem_id_x();
-  const float* ml = part_ml + row * num_splits * 2;
+// LSE merge of n split partials: O = sum_i 2^(m_i - M) l_i O_i / sum_i 2^(m_i - M) l_i
+// over the partials slot(0 .. n-1) (empty ones carry m = -inf and are skipped).
+template <class Slot>
+__device__ inline float merge_parts(const float* part_o, const float* part_ml, int n, int d, Slot slot) {
   float M = -INFINITY;
-  for (int i = 0; i < num_splits; ++i) M = fmaxf(M, ml[2 * i]);
+  for (int i = 0; i < n; ++i) M = fmaxf(M, part_ml[2 * slot(i)]);
   float num = 0.f, den = 0.f;
   if (M != -INFINITY) {
-    for (int i = 0; i < num_splits; ++i) {
-      const float m = ml[2 * i];
+    for (int i = 0; i < n; ++i) {
+      const long p = slot(i);
+      const float m = part_ml[2 * p];
       if (m == -INFINITY) continue;
-      const float w = exp2_fast(m - M) * ml[2 * i + 1];
-      num = fmaf(w, part_o[(row * num_splits + i) * kHeadDim + d], num);
+      const float w = exp2_fast(m - M) * part_ml[2 * p + 1];
+      num = fmaf(w, part_o[p * kHeadDim + d], num);
       den += w;
     }
   }
-  const float o = den > 0.f ? num / den : 0.f;
+  return den > 0.f ? num / den : 0.f;
+}
+
+__device__ inline void store_row(void* out, int out_bf16, long row, int d, float o) {
   if (out_bf16) ((__bf16*)out)[row * kHeadDim + d] = (__bf16)o;
   else ((float*)out)[row * kHeadDim + d] = o;
 }
 
+// LSE combine of a host plan's partials, [row][num_splits] slots per row.
+__global__ void __launch_bounds__(128) combine_kernel(const float* part_o, const float* part_ml,
+                                                      int num_splits, void* out, int out_bf16) {
+  const long row = __builtin_amdgcn_workgroup_id_x();
+  const int d = __builtin_amdgcn_workitem_id_x();
+  const float o = merge_parts(part_o, part_ml, num_splits, d,
+                              [&](int i) { return row * num_splits + i; });
+  store_row(out, out_bf16, row, d, o);
+}
+
+// Combine of a device-planned call. Plan mode 0 (about equal lengths): the
+// max_len plan's partials, [row][ns]. Mode 1 (ragged): row (sequence b, query
+// head hq) has n = ceil(L / S) splits, the work-items row_first .. row_first
+// + n - 1 of its KV head (partial slot item * 4 + hq mod 4); a row with one
+// split was written by the decode, an empty row gets zeros.
+__global__ void __launch_bounds__(128) combine_plan_kernel(DecodeArgs a) {
+  const long row = __builtin_amdgcn_workgroup_id_x();
+  const int d = __builtin_amdgcn_workitem_id_x();
+  const int S = a.plan_hdr[0], mode = a.plan_hdr[1];
+  if (mode == 0) {
+    const int ns = a.num_splits;
+    if (ns == 1) return;
+    const float o = merge_parts(a.part_o, a.part_ml, ns, d, [&](int i) { return row * ns + i; });
+    store_row(a.out, a.out_bf16, row, d, o);
+    return;
+  }
+  const int Hq = a.num_kv_heads * kGqa;
+  const int b = (int)(row / Hq), hq = (int)(row % Hq);
+  int L = min(max(a.seq_lens[b], 0), a.max_len);
+  if (a.len_mode == 1) L -= L % kGroup;
+  const int n = L > 0 ? (L + S - 1) / S : 0;
+  if (n == 1) return;
+  float o = 0.f;
+  if (n > 1) {
+    const long first = a.row_first[(long)b * a.num_kv_heads + hq / kGqa];
+    o = merge_parts(a.part_o, a.part_ml, n, d,
+                    [&](int i) { return (first + i) * kGqa + hq % kGqa; });
+  }
+  store_row(a.out, a.out_bf16, row, d, o);
+}
+
 template <int BITS, int KAX, int VAX, bool PAGED>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)decode_grid_blocks((long)a.batch * a.num_kv_heads, a.num_splits));
+  dim3 grid((unsigned)(a.dev_plan ? a.plan_items : decode_grid_blocks((long)a.batch * a.num_kv_heads, a.num_splits)));
   if (a.fp8_qk) decode_kernel<BITS, KAX, VAX, PAGED, true><<<grid, kThreads, 0, s>>>(a);
   else decode_kernel<BITS, KAX, VAX, PAGED, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
@@ -1034,6 +1078,11 @@ hipError_t launch_b(const kvq_format& f, const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_decode_quant(const kvq_format& f, const DecodeArgs& a, hipStream_t s) {
   if (f.group != kGroup) return launch_decode_quant_tg(f, a, s);
   return f.bits == 4 ? launch_b<4>(f, a, s) : launch_b<2>(f, a, s);
+}
+
+hipError_t launch_combine_plan(const DecodeArgs& a, hipStream_t s) {
+  combine_plan_kernel<<<(unsigned)((long)a.batch * a.num_kv_heads * kGqa), kHeadDim, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const float* part_o, const float* part_ml, int rows, int num_splits,

@@ -21,6 +21,167 @@ constexpr int kWaves = 4;
 constexpr int kThr = 8;          // lazy-max threshold in log2 units: P <= 2^kThr
 constexpr int kMaxGroups = kChunkTokens / kGroup;
 
+// ---- the work-group's split --------------------------------------------
+// A work-group decodes tokens [sp S, min(sp S + S, L)) of KV head h of
+// sequence b. With a host plan the grid is (row, split) in the per-XCD order
+// of work_item. With the device plan (num_splits = 0 on a batch whose max_len
+// plan already splits the rows) every work-group first reads the lengths and
+// applies lengths_split: for about equal lengths the grid's first part is the
+// max_len plan's (row, split) grid, partials [row][ns] (plan mode 0); for a
+// ragged batch work-group i is work-item i of the plan (sequences, then KV
+// heads, then splits), found with a prefix sum over the sequences' item
+// counts, partials per item (plan mode 1). Work-groups past the plan return
+// at once.
+struct Split {
+  int b, h, sp, S;   // sequence, KV head, split index, split tokens
+  bool live;         // false: padding / past the plan's items (return at once)
+  bool direct;       // the row's only split: write the output itself
+  long pbase, pmul;  // partial slot of query head hh of the group: pbase + hh * pmul
+};
+
+__device__ inline int plan_len(const DecodeArgs& a, int b) {
+  int L = min(max(a.seq_lens[b], 0), a.max_len);
+  if (a.len_mode == 1) L -= L % kGroup;
+  return L;
+}
+
+// The split's values in scalar registers (the integer divisions that find
+// them run on the vector unit): loop bounds and addresses derived from them
+// stay scalar.
+__device__ inline Split uniform(Split s) {
+  s.b = __builtin_amdgcn_readfirstlane(s.b);
+  s.h = __builtin_amdgcn_readfirstlane(s.h);
+  s.sp = __builtin_amdgcn_readfirstlane(s.sp);
+  s.S = __builtin_amdgcn_readfirstlane(s.S);
+  return s;
+}
+
+// (row, split) item of a host-style grid: ns splits of S tokens per row,
+// partials [row][stride] from slot base
+__device__ inline Split grid_split(const DecodeArgs& a, int item, int ns, int S, bool direct,
+                                   int stride, int base) {
+  const WorkItem wi = work_item(item, a.num_kv_heads, a.batch, ns);
+  Split s;
+  s.b = wi.b;
+  s.h = wi.h;
+  s.sp = wi.sp;
+  s.S = S;
+  s.live = wi.live;
+  s.direct = direct;
+  s.pbase = ((long)wi.b * a.num_kv_heads + wi.h) * kGqa * stride + base + wi.sp;
+  s.pmul = stride;
+  return uniform(s);
+}
+
+// x from lane (lane ^ m) of the wave (a cross-lane permute through the LDS
+// crossbar; no barrier)
+__device__ inline int lane_xor(int x, int m) {
+  const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  return __builtin_amdgcn_ds_bpermute((lane ^ m) << 2, x);
+}
+__device__ inline int lane_from(int x, int src) { return __builtin_amdgcn_ds_bpermute(src << 2, x); }
+
+// scratch: 16 ints of LDS that the caller uses only after this returns
+// (every thread of the work-group calls it)
+__device__ inline Split find_split(const DecodeArgs& a, int* scratch) {
+  const int item = __builtin_amdgcn_workgroup_id_x();
+  if (!a.dev_plan)
+    return grid_split(a, item, a.num_splits, a.split_tokens, a.direct_out != 0, a.part_stride,
+                      a.part_base);
+  const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63, wv = tid >> 6;
+  const int B = a.batch, H = a.num_kv_heads;
+  // lengths: thread t keeps sequence t (a batch past kThreads is read again below)
+  const int Lt = tid < B ? plan_len(a, tid) : 0;
+  unsigned lo = (unsigned)Lt, hi = 0;  // 64-bit total in two words
+  int lon = Lt;
+  for (int b = tid + kThreads; b < B; b += kThreads) {
+    const int L = plan_len(a, b);
+    const unsigned n = lo + (unsigned)L;
+    hi += n < lo;
+    lo = n;
+    lon = max(lon, L);
+  }
+  for (int m = 1; m < 64; m <<= 1) {
+    const unsigned olo = (unsigned)lane_xor((int)lo, m), ohi = (unsigned)lane_xor((int)hi, m);
+    const unsigned n = lo + olo;
+    hi += ohi + (n < lo);
+    lo = n;
+    lon = max(lon, lane_xor(lon, m));
+  }
+  if (lane == 0) {
+    scratch[3 * wv] = (int)lo;
+    scratch[3 * wv + 1] = (int)hi;
+    scratch[3 * wv + 2] = lon;
+  }
+  __syncthreads();
+  unsigned long long tot = 0;
+  lon = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    tot += (unsigned long long)(unsigned)scratch[3 * w] | ((unsigned long long)(unsigned)scratch[3 * w + 1] << 32);
+    lon = max(lon, scratch[3 * w + 2]);
+  }
+  const int S = __builtin_amdgcn_readfirstlane(
+      lengths_split((long long)tot, __builtin_amdgcn_readfirstlane(lon), B, H, a.plan_slots, a.split_tokens));
+  const bool ragged = S != a.split_tokens;
+  if (item == 0 && tid == 0) {
+    a.plan_hdr[0] = S;
+    a.plan_hdr[1] = ragged;
+  }
+  if (!ragged) {  // the max_len plan's grid and partial layout
+    __syncthreads();  // scratch free for the caller
+    return grid_split(a, item, a.num_splits, S, a.num_splits == 1, a.num_splits, 0);
+  }
+  // item counts H ceil(L_b / S) and their prefix, kThreads sequences at a time
+  int base = 0, hb = -1, hj = 0;
+  for (int b0 = 0; b0 < B; b0 += kThreads) {
+    const int b = b0 + tid;
+    const int L = b0 == 0 ? Lt : (b < B ? plan_len(a, b) : 0);
+    const int c = L > 0 ? H * ((L + S - 1) / S) : 0;
+    int incl = c;  // inclusive prefix within the wave
+    for (int m = 1; m < 64; m <<= 1) {
+      const int v = lane_from(incl, lane >= m ? lane - m : lane);
+      if (lane >= m) incl += v;
+    }
+    __syncthreads();  // the previous round's readers are done with scratch
+    if (lane == 63) scratch[wv] = incl;
+    __syncthreads();
+    int woff = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int t = scratch[w];
+      woff += w < wv ? t : 0;
+      total += t;
+    }
+    const int end = base + woff + incl;
+    if (item < end && item >= end - c) {
+      scratch[8] = b;
+      scratch[9] = item - (end - c);
+    }
+    base += total;
+    if (item < base) {  // every thread: the item lies in this round
+      __syncthreads();
+      hb = scratch[8];
+      hj = scratch[9];
+      break;
+    }
+  }
+  __syncthreads();  // scratch free for the caller
+  Split s;
+  s.S = S;
+  s.live = hb >= 0;
+  s.b = s.live ? __builtin_amdgcn_readfirstlane(hb) : 0;
+  const int n = s.live ? (plan_len(a, s.b) + S - 1) / S : 1;  // the row's splits
+  const int j = s.live ? __builtin_amdgcn_readfirstlane(hj) : 0;
+  s.h = j / n;
+  s.sp = j % n;
+  s.direct = n == 1;
+  s.pbase = (long)item * kGqa;
+  s.pmul = 1;
+  if (s.live && s.sp == 0 && !s.direct && tid == 0) a.row_first[(long)s.b * H + s.h] = item;
+  return uniform(s);
+}
+
 __device__ inline h8 as_h8(u4 v) { return __builtin_bit_cast(h8, v); }
 __device__ inline f4 mfma(u4 a, u4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a), as_h8(b), c, 0, 0, 0);

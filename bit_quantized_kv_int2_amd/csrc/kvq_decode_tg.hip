@@ -60,26 +60,27 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
   float* qs = (float*)(lds + M::QS);
   float* red = (float*)(lds + M::RED);
 
-  const WorkItem wi = work_item(__builtin_amdgcn_workgroup_id_x(), a.num_kv_heads, a.batch, a.num_splits);
-  if (!wi.live) return;  // padding to whole rounds of 8 rows
-  const int sp = wi.sp, h = wi.h, b = wi.b;
+  static_assert(M::TOTAL >= (8 + kThreads) * 4, "find_split borrows the start of the LDS");
+  const Split ws = find_split(a, (int*)lds);
+  if (!ws.live) return;  // padding, or past the plan's work-items
+  const int sp = ws.sp, h = ws.h, b = ws.b;
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.num_kv_heads, Hq = H * kGqa;
   int L = min(max(a.seq_lens[b], 0), a.max_len);
   if (a.len_mode == 1) L -= L % kGroup;
-  const int tb = sp * a.split_tokens;
-  const int te = min(tb + a.split_tokens, L);
+  const int tb = sp * ws.S;
+  const int te = min(tb + ws.S, L);
   const long row0 = (long)b * Hq + (long)h * kGqa;
 
   if (te <= tb) {  // nothing in this split (or an empty sequence)
     for (int e = tid; e < kGqa * kHeadDim; e += kThreads) {
       int hh = e / kHeadDim, d = e % kHeadDim;
-      if (a.direct_out) {
+      if (ws.direct) {
         if (a.out_bf16) ((uint16_t*)a.out)[(row0 + hh) * kHeadDim + d] = 0;
         else ((float*)a.out)[(row0 + hh) * kHeadDim + d] = 0.f;
       } else {
-        const long pr = (row0 + hh) * a.part_stride + a.part_base + sp;
+        const long pr = ws.pbase + hh * ws.pmul;
         a.part_o[pr * kHeadDim + d] = 0.f;
         if (d == 0) {
           a.part_ml[pr * 2] = -INFINITY;
@@ -442,7 +443,7 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const float o0 = n0 * inv, o1 = n1 * inv;
     const long row = row0 + qh;
-    if (a.direct_out) {
+    if (ws.direct) {
       if (a.out_bf16) {
         __bf16 b0 = (__bf16)o0, b1 = (__bf16)o1;
         uint32_t pk = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
@@ -452,7 +453,7 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
         *(float2*)((float*)a.out + row * kHeadDim + d) = make_float2(o0, o1);
       }
     } else {
-      const long pr = row * a.part_stride + a.part_base + sp;
+      const long pr = ws.pbase + qh * ws.pmul;
       *(float2*)(a.part_o + pr * kHeadDim + d) = make_float2(o0, o1);
       if (d == 0) {
         a.part_ml[pr * 2] = ml[(0 * 4 + qh) * 2];
@@ -464,7 +465,7 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
 
 template <int BITS, int NG>
 hipError_t launch_tg(const DecodeArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)decode_grid_blocks((long)a.batch * a.num_kv_heads, a.num_splits));
+  dim3 grid((unsigned)(a.dev_plan ? a.plan_items : decode_grid_blocks((long)a.batch * a.num_kv_heads, a.num_splits)));
   decode_tg_kernel<BITS, NG><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -102,6 +102,35 @@ __device__ inline WorkItem work_item(unsigned i, unsigned H, unsigned B, unsigne
   return WorkItem{(int)(p % ns), (int)(row % H), (int)(row / H), row < H * B};
 }
 
+// ---- the auto plan from the lengths (num_splits = 0) ----------------------
+// When the max_len plan splits the rows (fewer (sequence, KV head) rows than
+// resident work-group slots), the quantised decode with num_splits = 0 plans
+// on the device, from the lengths in seq_lens, with no host synchronisation:
+// every work-group derives the same plan. The split is
+//   * with lengths about equal (longest <= 1.5 x mean, or all empty): the
+//     max_len plan's split `auto_tokens`, on the max_len plan's grid;
+//   * otherwise H sum(L) / (2 slots) tokens rounded up to whole 2048-token
+//     chunks (about two splits per resident work-group slot, so that the
+//     longest sequences leave no tail), when that is below auto_tokens; the
+//     work-items (one per work-group) run over the sequences, then their KV
+//     heads, then a row's splits.
+// The grid covers both: max(the max_len grid, 2 slots + rows); with the
+// length split S >= H sum(L) / (2 slots), sum_b H ceil(L_b / S) <= 2 slots +
+// rows. Work-groups past the plan's items return at once.
+__host__ __device__ inline int lengths_split(long long total, int longest, int batch, int heads,
+                                             long long slots, int auto_tokens) {
+  if (total <= 0 || 2LL * longest * batch <= 3LL * total) return auto_tokens;
+  const long long den = 2LL * slots;
+  const long long t = ((long long)heads * total + den - 1) / den;
+  long long k = (t + kChunkTokens - 1) / kChunkTokens;
+  if (k < 1) k = 1;
+  return k * kChunkTokens < auto_tokens ? (int)(k * kChunkTokens) : auto_tokens;
+}
+inline long plan_item_bound(long rows, int ns_auto, long slots) {
+  const long by_grid = decode_grid_blocks(rows, ns_auto), by_slots = 2 * slots + rows;
+  return by_grid > by_slots ? by_grid : by_slots;
+}
+
 // Launch arguments of the quantised decode (one layer).
 struct DecodeArgs {
   const uint16_t* q;       // bf16 [B][Hq][D]
@@ -128,6 +157,15 @@ struct DecodeArgs {
   int part_base;
   int len_mode;            // 0: L = seq_lens[b]; 1: L rounded down to whole 128-token groups
   int fp8_qk;              // 1: q.K^T on fp8 (E4M3) operands, hi/lo query parts
+  // the auto plan on the device (dev_plan = 1): split_tokens / num_splits are
+  // the max_len plan's, the grid has plan_items work-groups; partials are
+  // [row][num_splits] (plan mode 0) or per work-item (mode 1), part_o
+  // [item][4][D], part_ml [item][4][2]
+  int dev_plan;
+  int plan_items;
+  int plan_slots;          // resident work-group slots of the kernel on the chip
+  int* plan_hdr;           // [0]: the split chosen, [1]: plan mode (written by work-group 0)
+  int* row_first;          // [B][Hkv]: item of a row's first split (mode 1, rows with >= 2 splits)
 };
 
 struct Bf16Args {
@@ -183,6 +221,9 @@ hipError_t launch_decode_quant_tg(const kvq_format& f, const DecodeArgs& a, hipS
 hipError_t launch_decode_bf16(const Bf16Args& a, hipStream_t s);
 hipError_t launch_combine(const float* part_o, const float* part_ml, int rows, int num_splits,
                           void* out, int out_bf16, hipStream_t s);
+// merge of a device-planned call: every (sequence, query head) row with two or
+// more splits; zeros for empty rows (rows with one split were written by the decode)
+hipError_t launch_combine_plan(const DecodeArgs& a, hipStream_t s);
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 // Reads bytes (a multiple of 16) once; the HBM read reference for measurement.

@@ -113,8 +113,10 @@ kvq_status kvq_check_format(const kvq_format* fmt);
 kvq_status kvq_cache_sizes(const kvq_format* fmt, int32_t batch, int32_t max_len,
                            int32_t num_pages, size_t bytes[4]);
 
-/* Split-KV plan: the number of token splits per (sequence, KV head) the
- * decode uses for num_splits = 0 (auto), given batch and max_len. */
+/* Split-KV plan from batch and max_len alone: the number of token splits per
+ * (sequence, KV head) that fills the chip when every sequence is max_len long.
+ * decode_attention_bf16 uses it for num_splits = 0; the quantised decode's
+ * auto plan (kvq_auto_plan) starts from it. */
 kvq_status kvq_plan_splits(const kvq_format* fmt, int32_t batch, int32_t max_len,
                            int32_t* num_splits);
 
@@ -136,8 +138,36 @@ kvq_status kvq_plan_splits(const kvq_format* fmt, int32_t batch, int32_t max_len
 kvq_status kvq_plan_splits_for_lengths(const kvq_format* fmt, int32_t batch, int32_t max_len,
                                        const int32_t* seq_lens_host, int32_t* num_splits);
 
+/* The quantised decode's auto plan (num_splits = 0), which the decode derives
+ * on the device from the lengths in seq_lens, with no host synchronisation
+ * (a drop-in decode step: grafy.ai "How can developers integrate FOSCAR into
+ * their LLM serving stacks?"). Every (sequence, KV head) row is cut into
+ * splits of split_tokens tokens:
+ *   - lengths about equal (the longest at most 1.5x the mean, or all 0): the
+ *     split of kvq_plan_splits (batch, max_len);
+ *   - otherwise H * sum(len) / (2 * work-group slots) tokens rounded up to
+ *     whole 2048-token chunks, when shorter than that split: the longest
+ *     sequences then do not set the call time.
+ * The plan is made on the device when the kvq_plan_splits count is 2 or more
+ * (fewer (sequence, KV head) rows than resident work-groups); with one split
+ * per row the rows alone fill the chip and the decode keeps that plan (no
+ * merge step, no workspace). A row with one split writes its output in the
+ * decode; rows with more are merged by a second kernel. This host copy of the
+ * rule reports the plan for
+ * lengths known on the host: split_tokens, items (the splits, summed over
+ * rows) and grid (the work-groups the call launches, a bound on items that
+ * depends on batch and max_len only). seq_lens_host: [batch] int32 in host
+ * memory, entries clamped to [0, max_len]; may be NULL when batch == 0. Pure
+ * host computation. Errors: KVQ_ERR_NULL_POINTER, KVQ_ERR_BAD_SHAPE, or the
+ * format's. */
+kvq_status kvq_auto_plan(const kvq_format* fmt, int32_t batch, int32_t max_len,
+                         const int32_t* seq_lens_host, int32_t* split_tokens, int32_t* items,
+                         int32_t* grid);
+
 /* Workspace bytes decode_attention_quant / decode_attention_bf16 need for a
- * given split count (0 = the auto plan). */
+ * given split count (0 = the auto plan; when the quantised decode plans on
+ * the device: a 16-byte header, one int32 per (sequence, KV head) and per
+ * work-item partials, grid x 4 x (128 + 2) floats). */
 kvq_status kvq_workspace_size(const kvq_format* fmt, int32_t batch, int32_t max_len,
                               int32_t num_splits, size_t* bytes);
 
@@ -172,7 +202,8 @@ kvq_status kv_quantize_pack(const kvq_format* fmt, const float* k, const float* 
  *   cache       packed cache in fmt's layout.
  *   softmax_scale  multiplies q.K^T (e.g. 1/sqrt(D)).
  *   out         device [batch][Hq][D], fp32 or bf16 per out_dtype.
- *   num_splits  token splits per (sequence, KV head); 0 = automatic plan.
+ *   num_splits  token splits per (sequence, KV head); 0 = the auto plan,
+ *               made on the device from seq_lens (kvq_auto_plan).
  *   workspace   device scratch of at least kvq_workspace_size() bytes.
  */
 kvq_status decode_attention_quant(const kvq_format* fmt, const void* q, const kvq_cache* cache,
@@ -242,8 +273,10 @@ kvq_status decode_attention_quant_noalloc(const kvq_format* fmt, const void* q,
                                           void* stream);
 
 /*
- * decode_attention_bf16 -- the same decode over an unquantised bf16 cache
- * (the comparison baseline; bits and axes of fmt are ignored).
+ * decode_attention_bf16 -- the same decode over an unquantised bf16 cache:
+ * the BF16-cache decode the pages measure the quantised kernels against
+ * (rag-lover.com 既存手法との違い; grafy.ai "What performance gains does
+ * FOSCAR deliver?"). Bits and axes of fmt are ignored.
  *   k, v        device bf16: contiguous [batch][Hkv][max_len][D], paged
  *               [P][Hkv][64][D].
  *   other arguments as decode_attention_quant.
@@ -306,10 +339,11 @@ kvq_status decode_attention_quant_window(const kvq_format* fmt, const void* q,
 
 /*
  * kvq_stream_read -- measurement reference, not part of the method: reads
- * `bytes` of device memory once with 128-bit loads (grid-stride over 256 CUs)
- * and nothing else, giving the practical HBM read rate that the decode
- * kernels' effective rates are compared with (the pages compare against the
- * chip's peak bandwidth: grafy.ai "What did benchmarks show"; rag-lover.com
+ * `bytes` of device memory once with 128-bit non-temporal loads (up to 1024
+ * work-groups, each a contiguous range) and nothing else, giving the
+ * practical HBM read rate that the decode kernels' effective rates are
+ * compared with (the pages compare against the chip's peak bandwidth:
+ * grafy.ai "What performance gains does FOSCAR deliver?"; rag-lover.com
  * TL;DR).
  *   data   device pointer, 16-byte aligned; bytes a multiple of 16.
  *   sink   device uint32; written only if the XOR of all words read equals

@@ -95,11 +95,21 @@ def test_small_token_wise_groups(L):
         assert kvq.kvq_check_format(kvq.make_format(2, "token", "token", 2, group=bad)) == BADFMT
 
 
+def _auto_ws(rows, ns_auto, slots):
+    items = max(-(-rows // 8) * 8 * ns_auto, 2 * slots + rows)
+    return 16 + -(-rows * 4 // 16) * 16 + items * 4 * 130 * 4
+
+
 def test_split_plan_and_workspace(L):
     f = kvq.make_format(2, "channel", "token", 8)
     ns = kvq.kvq_plan_splits(f, 128, 32768)
     assert 1 <= ns <= 128
-    assert kvq.kvq_workspace_size(f, 128, 32768) == (0 if ns == 1 else 128 * 32 * ns * 130 * 4)
+    # one split per row: no merge, no workspace (the rows fill the chip)
+    assert ns == 1 and kvq.kvq_workspace_size(f, 128, 32768) == 0
+    # a split plan runs on the device: a 16-byte header, one int32 per
+    # (sequence, KV head) row, and partials (4 x 130 floats) for each of the
+    # grid's max(rows * ns, 2 slots + rows) work-items
+    assert kvq.kvq_workspace_size(f, 16, 4096) == _auto_ws(16 * 8, 8, 1024)
     # a single sequence is split finely enough to occupy the chip
     assert kvq.kvq_plan_splits(kvq.make_format(4, num_kv_heads=1), 1, 32768) >= 64
     assert kvq.kvq_plan_splits(kvq.make_format(4, num_kv_heads=1), 1, 1024) == 4
@@ -112,8 +122,11 @@ def test_split_plan_and_workspace(L):
     assert kvq.kvq_plan_splits(share4, 128, 32768) == 6
     assert kvq.kvq_plan_splits(kvq.make_format(2, "channel", "channel", 1), 128, 32768) == 8
     assert kvq.kvq_plan_splits(kvq.make_format(4, "channel", "channel", 1), 128, 32768) == 6
-    # the workspace also covers the bf16 decode's plan (1024 work-groups: 8 splits)
-    assert kvq.kvq_workspace_size(share4, 128, 32768) == 128 * 4 * 8 * 130 * 4
+    # the workspace also covers the bf16 decode's plan (1024 work-groups: 8
+    # splits), and with explicit counts it is the (row, split) partials alone
+    assert kvq.kvq_workspace_size(share4, 128, 32768) == max(_auto_ws(128, 6, 768),
+                                                            128 * 4 * 8 * 130 * 4)
+    assert kvq.kvq_workspace_size(share4, 128, 32768, 6) == 128 * 4 * 6 * 130 * 4
     # explicit splits: any count from 1 to ceil(L / 256); one split needs no workspace
     assert kvq.kvq_workspace_size(f, 2, 32768, 1) == 0
     assert kvq.kvq_workspace_size(f, 2, 32768, 3) == 2 * 32 * 3 * 130 * 4
@@ -127,6 +140,76 @@ def test_split_plan_and_workspace(L):
         kvq.kvq_workspace_size(f, 4096, 1 << 20, 512)
     with pytest.raises(kvq.KvqError):
         kvq.kvq_workspace_size(f, 2, 1024, -1)
+
+
+def test_auto_plan_rule(L):
+    """The quantised decode's auto plan (made on the device; kvq_auto_plan is
+    its host copy): the max_len plan's split for about equal lengths, whole
+    2048-token chunks of about H sum(L) / (2 slots) tokens for a ragged batch,
+    and never more work-items than the grid the call launches."""
+    import numpy as np
+    import synth
+    for bits in (2, 4):
+        slots = 256 * (4 if bits == 2 else 3)
+        f = kvq.make_format(bits, "channel", "token", 8)
+        # 1024 rows fill the chip: one split per row whatever the lengths
+        assert kvq.kvq_auto_plan(f, [32768] * 128, 32768) == (32768, 1024, 1024)
+        assert kvq.kvq_auto_plan(f, [32768] + [100] * 127, 32768) == (32768, 1024, 1024)
+        # 16 x 8 rows: the max_len plan splits them, so the plan is made on the
+        # device; equal lengths and a mild spread keep the max_len split
+        S, items, grid = kvq.kvq_auto_plan(f, [4096] * 16, 4096)
+        ns = kvq.kvq_plan_splits(f, 16, 4096)
+        assert ns == -(-slots // 128) and S == -(-16 // ns) * 256
+        assert items == 128 * -(-4096 // S) and grid == max(128 * ns, 2 * slots + 128)
+        assert kvq.kvq_auto_plan(f, list(range(3000, 3000 + 16 * 20, 20)), 3320)[0] == \
+            -(-(-(-3320 // 256)) // kvq.kvq_plan_splits(f, 16, 3320)) * 256
+        # the long-context paged batch: 64 sequences log-uniform in [1K, 128K]
+        fp = kvq.make_format(bits, "channel", "token", 8, page_size=64)
+        lens = synth.paged_long(0).seq_lens
+        Lmax = max(lens)
+        S, items, grid = kvq.kvq_auto_plan(fp, lens, Lmax)
+        t = -(-8 * sum(lens) // (2 * slots))
+        assert S == 2048 * max(1, -(-t // 2048))
+        assert items == sum(8 * -(-L // S) for L in lens) <= grid
+        ns = kvq.kvq_plan_splits(fp, 64, Lmax)
+        assert ns >= 2 and grid == max(64 * 8 * ns, 2 * slots + 64 * 8)
+        # one long sequence among short ones, empty and clamped lengths
+        assert kvq.kvq_auto_plan(f, [131072] + [1024] * 63, 131072)[0] == 2048
+        assert kvq.kvq_auto_plan(f, [0] * 8, 4096)[1] == 0
+        assert kvq.kvq_auto_plan(f, [-5, 99999999] + [32768] * 126, 32768) == \
+            kvq.kvq_auto_plan(f, [0, 32768] + [32768] * 126, 32768)
+        # many random batches: the items always fit the grid; the split is the
+        # auto split or whole chunks below it
+        rng = np.random.default_rng(bits)
+        for trial in range(300):
+            B = int(rng.integers(1, 300))
+            H = int(rng.choice([1, 2, 8]))
+            Lmax = int(rng.integers(1, 300000))
+            ff = kvq.make_format(bits, "channel", "token", H)
+            kind = trial % 3
+            if kind == 0:
+                lens = rng.integers(0, Lmax + 1, B)
+            elif kind == 1:
+                lens = np.exp(rng.uniform(0, np.log(Lmax + 1), B)).astype(np.int64)
+            else:
+                lens = np.where(rng.random(B) < 0.1, Lmax, rng.integers(0, max(1, Lmax // 50), B))
+            lens = np.minimum(lens, Lmax)
+            S, items, grid = kvq.kvq_auto_plan(ff, lens, Lmax)
+            ns = kvq.kvq_plan_splits(ff, B, Lmax)
+            auto_S = -(-(-(-Lmax // 256)) // ns) * 256
+            assert items <= grid, (B, H, Lmax, S, items, grid)
+            assert items == sum(H * -(-int(L) // S) for L in lens if L > 0)
+            if ns == 1:
+                assert S == auto_S and grid == -(-B * H // 8) * 8
+            else:
+                assert S == auto_S or (S % 2048 == 0 and S < auto_S)
+                assert grid == max(-(-B * H // 8) * 8 * ns, 2 * slots + B * H)
+    z = ctypes.c_int32()
+    f = kvq.make_format(2, "channel", "token", 8)
+    assert L.kvq_auto_plan(ctypes.byref(f), 4, 1024, None, ctypes.byref(z), ctypes.byref(z),
+                           ctypes.byref(z)) == NULLP
+    assert L.kvq_auto_plan(ctypes.byref(f), 0, 1024, None, ctypes.byref(z), ctypes.byref(z),
+                           ctypes.byref(z)) == OK
 
 
 def test_split_plan_for_known_lengths(L):

@@ -120,6 +120,51 @@ def test_pack_exact_ties_and_signed_zeros(bits, k_axis, v_axis, group, page):
     assert (sz[1::2] == 0x8000).any() and (sz[1::2] == 0).any()
 
 
+@pytest.mark.parametrize("bits,k_axis,v_axis,page", [
+    (2, "channel", "token", 0), (4, "token", "channel", 64),
+    (2, "channel", "channel", 64), (4, "token", "token", 0)])
+def test_device_auto_plan_on_ragged_lengths(bits, k_axis, v_axis, page):
+    """num_splits = 0: the decode plans on the device from the lengths. A
+    ragged batch is cut into whole 2048-token splits; the split the decode
+    records in its workspace header is the one kvq_auto_plan (the host copy of
+    the rule) gives; rows with one split are written by the decode, longer rows
+    merged, the empty row is zero; the output meets the oracle gate, agrees
+    with a host-planned call, repeats bit for bit, and does not depend on the
+    workspace's prior contents."""
+    import torch
+    import bit_quantized_kv_int2_amd as kvq
+    lens = [40000, 300, 0, 39000, 2047, 1, 12000, 128]
+    w = synth.Workload("autoplan", len(lens), 8, 32, 128, lens, bits, k_axis, v_axis, seed=83,
+                       outliers=True, page_size=page)
+    inp = Inputs(w)
+    run = GpuRun(inp)
+    S, items, grid = kvq.kvq_auto_plan(run.fmt, lens, w.max_len)
+    ns_auto = kvq.kvq_plan_splits(run.fmt, w.batch, w.max_len)
+    auto_S = -(-(-(-w.max_len // 256)) // ns_auto) * 256
+    assert S % 2048 == 0 and S < auto_S and items <= grid  # the length rule is in use
+    ref = oracle_attention(inp, oracle_pack(inp))
+    outs = []
+    for fill in (0xA5, 0x00):
+        nbytes = kvq.kvq_workspace_size(run.fmt, w.batch, w.max_len, 0)
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device="cuda")
+        out = torch.full((w.batch, w.num_q_heads, w.head_dim), float("nan"), device="cuda")
+        kvq.decode_attention_quant(run.fmt, run.q, run.cache, run.lens, w.max_len, SCALE, out,
+                                   page_table=run.table, num_splits=0, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32)[0]) == S
+        outs.append(out.cpu().numpy().astype(np.float64))
+    o = outs[0]
+    assert np.array_equal(outs[0], outs[1])
+    assert not o[2].any() and np.isfinite(o).all()
+    e2, ea = rel_l2(o, ref), max_abs(o, ref)
+    host = run.decode(num_splits=kvq.kvq_plan_splits_for_lengths(run.fmt, lens, w.max_len))
+    d = rel_l2(o, host)
+    print(f"auto plan int{bits} {k_axis[0]}{v_axis[0]} page {page}: split {S}, {items} items "
+          f"(grid {grid}); rel_l2={e2:.3e} max_abs={ea:.3e}; vs host plan {d:.2e}")
+    assert e2 <= REL_L2_TOL and ea <= MAX_ABS_TOL
+    assert d < 5e-4
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 def test_split_invariance_and_determinism(bits):
     w = synth.Workload("splits", 2, 2, 8, 128, [4096, 3000], bits, "channel", "token", seed=51,

@@ -5,7 +5,8 @@ against decode_attention_quant with a caller workspace, through the C ABI.
 Same kernels and split plan, so the outputs must be equal bit for bit; each
 is also within the oracle gate. Two calls in a row, the second smaller, so
 the second reads the scratch the first left behind in its unused tail; then
-a call with one split, which needs no scratch."""
+a call with one split, which needs no scratch; then two calls with the auto
+plan (num_splits = 0), which the decode makes on the device from the lengths."""
 import numpy as np
 import pytest
 
@@ -35,7 +36,7 @@ def _both(run, num_splits):
     return outs
 
 
-@pytest.mark.parametrize("case", ["large_then_small", "one_split"])
+@pytest.mark.parametrize("case", ["large_then_small", "one_split", "auto_plan"])
 def test_noalloc_equals_workspace_entry_point(case):
     import bit_quantized_kv_int2_amd as kvq
     if case == "large_then_small":
@@ -45,9 +46,16 @@ def test_noalloc_equals_workspace_entry_point(case):
             (synth.Workload("noalloc_b", 2, 1, 4, 128, [900, 5000], 2, "token", "channel", seed=72,
                             page_size=64), 5),
         ]
-    else:
+    elif case == "one_split":
         calls = [(synth.Workload("noalloc_c", 3, 2, 8, 128, [4096, 77, 1000], 2, "channel", "token",
                                  seed=73), 1)]
+    else:  # the device-side auto plan on ragged lengths (whole-chunk splits, merged rows)
+        calls = [
+            (synth.Workload("noalloc_d", 6, 2, 8, 128, [30000, 64, 0, 9000, 2049, 300], 2, "channel",
+                            "token", seed=74, outliers=True), 0),
+            (synth.Workload("noalloc_e", 3, 1, 4, 128, [7000, 1, 2500], 4, "token", "channel",
+                            seed=75, page_size=64), 0),
+        ]
     sizes = []
     for w, ns in calls:
         inp = Inputs(w)
@@ -61,7 +69,7 @@ def test_noalloc_equals_workspace_entry_point(case):
         print(f"noalloc {w.name} splits {ns} scratch {need} B: rel_l2={e2:.3e} max_abs={ea:.3e}")
         assert np.array_equal(o_ws, o_na)
         assert e2 <= REL_L2_TOL and ea <= MAX_ABS_TOL
-    if case == "large_then_small":
+    if case in ("large_then_small", "auto_plan"):
         assert sizes[1] < sizes[0]
     else:
         assert sizes == [0]
