@@ -60,8 +60,9 @@ def parse():
                    help="skip the graph-replayed timings of the short calls")
     p.add_argument("--no-groups", action="store_true",
                    help="skip the token-wise G = 128 / 64 / 32 timings")
-    p.add_argument("--only", choices=["int2", "int4", "bf16"], default=None,
-                   help="time one bit width (or only the bf16 decode) (profiling runs)")
+    p.add_argument("--only", choices=["int2", "int4", "bf16", "pack"], default=None,
+                   help="time one bit width, or only the bf16 decode, or only kv_quantize_pack "
+                        "(profiling runs)")
     p.add_argument("--no-small", action="store_true",
                    help="skip the tiny / mid configurations (cache-resident and cold timings)")
     p.add_argument("--no-pack", action="store_true", help="skip the kv_quantize_pack timing")
@@ -556,6 +557,10 @@ def main():
     B, L = args.batch, args.seq_len
     H, Hq, D = 8, 32, 128
     scale = 1.0 / math.sqrt(D)
+    if args.only == "pack":  # the producer alone (profiling runs): its timing as one JSON line
+        print(json.dumps({"kv_quantize_pack": pack_timings(B, L, dev, stream, steps=args.steps)}),
+              flush=True)
+        return
     only_bf16 = args.only == "bf16"
     widths = [2] if only_bf16 else ([int(args.only[-1])] if args.only else [2, 4])
     need_bf16 = not args.no_bf16 and args.only in (None, "bf16")
