@@ -37,10 +37,11 @@
 //     then stream 64 tokens per iteration each: whole-line 1 KB wave loads of
 //     the codes one iteration ahead, online softmax with a lazily moved
 //     maximum; the (m, l, O) of the four waves are merged through LDS.
-//   * Extra PV tile: a 9th A tile whose rows hold hi/lo fp16 parts of the
-//     token-wise-V offset coefficient (or the subnormal "code 1" pattern for
-//     channel-wise V) gives sum_t P_t r_t (or sum_t P_t) from the same rounded
-//     P that feeds the data tiles.
+//   * Offset terms from the same rounded P that feeds the code tiles:
+//     token-wise V sums P''_t (w rho)_t on the vector unit (four fmas per
+//     lane and iteration; on gfx950 a matrix product and vector work do not
+//     overlap, so an extra tile would cost more); channel-wise V takes
+//     sum_t P''_t from a 9th A tile of the subnormal "code 1" pattern.
 #include <math.h>
 
 #include "kvq_internal.h"
@@ -253,7 +254,9 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   f4 O[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) O[c] = f4{0.f, 0.f, 0.f, 0.f};
-  f4 X = f4{0.f, 0.f, 0.f, 0.f};  // extra tile accumulator
+  // token-wise V: this lane's part of its head's offset sum, in X[0] (held as
+  // a 4-vector: with a scalar the INT4 fp8 kernels' registers spill)
+  f4 X = f4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY;
   float lsum = 0.f;
   // fp16 token-wise V: the running output starts from kSeedV (set when the
@@ -281,11 +284,10 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     // a DPP row share a group
     const int gl = wv + 4 * (pl >> 4);
     const bool glive = gl < ng;
-    // token-wise (s, z): lane l owns the 8 tokens of one A-operand block of
-    // the extra PV tile (iteration 2 gl + (l/8)%2, k-step (l/4)%2, lane group
-    // l%4) as two runs of 4 tokens, tb_run[r] .. +3
+    // token-wise (s, z): lane l owns 8 tokens of iteration 2 gl + (l/8)%2
+    // of its group as two runs of 4 tokens, tb_run[r] .. +3 (run starts at
+    // multiples of 4 tokens: a run's token e sits in code slot e % SLOTS)
     const int pit = 2 * gl + ((pl >> 3) & 1);
-    const int pblk = pit * 8 + (pl & 7);  // the block's index in A-operand order
     int tb_run[2];
     {
       const int ks = (pl >> 2) & 1, gg = pl & 3;
@@ -300,43 +302,99 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     const int ck_s = pl & 15;  // channel-wise K: k-step of group gl; channel-wise V: channels 8 ck_s ..
 
     // ---- prologue: (s, z) loads -------------------------------------------
-    u4 vz[2] = {u4{0u, 0u, 0u, 0u}, u4{0u, 0u, 0u, 0u}};  // V (s, z): 2 runs of 4 tokens, or 8 pairs
-    u4 kz[2] = {u4{0u, 0u, 0u, 0u}, u4{0u, 0u, 0u, 0u}};  // K (s, z): 2 runs of 4 tokens, or 8 channels
-    if (VAX == KVQ_TOKEN_WISE) {
+    // Contiguous caches: (s, z) pairs of one (sequence, KV head) are one run
+    // per token (token-wise) or per (group, channel) (channel-wise), so the
+    // chunk's pairs sit at a base shared by the wave plus a 32-bit lane offset
+    // (groups start at multiples of 128 tokens: the chunk's first group is
+    // cb / 128)
+    const long gbase = (unit * (a.padded_len / kGroup) + cb / kGroup) * (long)kHeadDim;
+    const unsigned char* ksz_c = (const unsigned char*)a.k_sz + 4 * (KAX == KVQ_TOKEN_WISE ? unit * a.padded_len + cb : gbase);
+    const unsigned char* vsz_c = (const unsigned char*)a.v_sz + 4 * (VAX == KVQ_TOKEN_WISE ? unit * a.padded_len + cb : gbase);
+    // byte offsets within the chunk's run fit 32 bits (a wave-shared base plus
+    // one offset register per load)
+    auto ksz_tok_c = [&](int r) -> const void* { return PAGED ? (const void*)ksz_tok(cb + r) : ksz_c + (uint32_t)(4 * r); };
+    auto vsz_tok_c = [&](int r) -> const void* { return PAGED ? (const void*)vsz_tok(cb + r) : vsz_c + (uint32_t)(4 * r); };
+    // channel-wise (s, z): lanes of groups past the end (a partial chunk)
+    // read the chunk's last group instead, so every lane loads and none needs
+    // a mask; only the lanes of live groups write fold operands
+    const int glc = min(gl, ng - 1);
+    auto ksz_chan_c = [&](int d) -> const void* {  // group glc of the chunk, channel d
+      return PAGED ? (const void*)ksz_chan(cb + glc * kGroup, d) : ksz_c + (uint32_t)(4 * (glc * kHeadDim + d));
+    };
+    auto vsz_chan_c = [&](int d) -> const void* {
+      return PAGED ? (const void*)vsz_chan(cb + glc * kGroup, d) : vsz_c + (uint32_t)(4 * (glc * kHeadDim + d));
+    };
+    u4 vz[2];  // V (s, z): 2 runs of 4 tokens, or 8 pairs
+    u4 kz[2];  // K (s, z): 2 runs of 4 tokens, or 8 channels
+    // FULL: a whole chunk (every token run of the lane is inside the split,
+    // no masks); otherwise token runs past the end read as (0, 0)
+    auto load_sz = [&](auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
+      if (!FULL) {
+        vz[0] = vz[1] = u4{0u, 0u, 0u, 0u};
+        kz[0] = kz[1] = u4{0u, 0u, 0u, 0u};
+      }
+      if (VAX == KVQ_TOKEN_WISE) {
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        if (tb_run[rr] < ntok) {
-          vz[rr] = *(const u4*)vsz_tok(cb + tb_run[rr]);
-          if (tb_run[rr] + 4 > ntok) {  // tokens past the end contribute (s, z) = (0, 0)
+        for (int rr = 0; rr < 2; ++rr) {
+          if (FULL || tb_run[rr] < ntok) {
+            vz[rr] = *(const u4*)vsz_tok_c(tb_run[rr]);
+            if (!FULL && tb_run[rr] + 4 > ntok) {  // tokens past the end contribute (s, z) = (0, 0)
 #pragma unroll
-            for (int e = 1; e < 4; ++e)
-              if (tb_run[rr] + e >= ntok) vz[rr][e] = 0u;
+              for (int e = 1; e < 4; ++e)
+                if (tb_run[rr] + e >= ntok) vz[rr][e] = 0u;
+            }
           }
         }
+      } else {
+        const u4* p = (const u4*)vsz_chan_c(8 * ck_s);
+        vz[0] = p[0];
+        vz[1] = p[1];
       }
-    } else if (glive) {
-      const u4* p = (const u4*)vsz_chan(cb + gl * kGroup, 8 * ck_s);
-      vz[0] = p[0];
-      vz[1] = p[1];
-    }
-    if (KAX == KVQ_TOKEN_WISE) {
+      if (KAX == KVQ_TOKEN_WISE) {
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr)
-        if (tb_run[rr] < ntok) kz[rr] = *(const u4*)ksz_tok(cb + tb_run[rr]);
-    } else if (glive && FP8) {
-      // the 8 channels of B-operand positions 8 ck_s .. + 7: pair e = 2 b + t
-      // is channel ch8(ck_s, t, b)
-      if (BITS == 4) {
+        for (int rr = 0; rr < 2; ++rr)
+          if (FULL || tb_run[rr] < ntok) kz[rr] = *(const u4*)ksz_tok_c(tb_run[rr]);
+      } else if (FP8) {
+        // the 8 channels of B-operand positions 8 ck_s .. + 7: pair e = 2 b + t
+        // is channel ch8(ck_s, t, b)
+        if (BITS == 4) {
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) kz[hf] = *(const u4*)ksz_chan(cb + gl * kGroup, 8 * ck_s + 4 * hf);
-      } else {  // every other channel of 16
+          for (int hf = 0; hf < 2; ++hf) kz[hf] = *(const u4*)ksz_chan_c(8 * ck_s + 4 * hf);
+        } else {  // every other channel of 16
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kz[e >> 2][e & 3] = *(const uint32_t*)ksz_chan(cb + gl * kGroup, C::ch8(ck_s, e & 1, e >> 1));
+          for (int e = 0; e < 8; ++e) kz[e >> 2][e & 3] = *(const uint32_t*)ksz_chan_c(C::ch8(ck_s, e & 1, e >> 1));
+        }
+      } else {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) kz[hf] = *(const u4*)ksz_chan_c(C::k_run(ck_s, hf));
       }
-    } else if (glive) {
+    };
+    if (ntok == kChunkTokens) load_sz(BoolC<true>{});
+    else load_sz(BoolC<false>{});
+
+    // Scales of 0 (a constant group or token, or the (0, 0) read for what
+    // lies past the end) stand for a stand-in scale in the fold formulas. The
+    // waves that hold one patch it into the (s, z) words before the common
+    // formulas, which then need no selects; smallest_s is the lane's smallest
+    // scale bit pattern (sign cleared) over its 8 words.
+    auto smallest_s = [](const u4 (&z)[2]) {
+      uint32_t m = 0x7FFFu;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) kz[hf] = *(const u4*)ksz_chan(cb + gl * kGroup, C::k_run(ck_s, hf));
-    }
+      for (int e = 0; e < 8; ++e) m = min(m, z[e >> 2][e & 3] & 0x7FFFu);
+      return m;
+    };
+    auto patch_zero_s = [](u4 (&z)[2], uint32_t one) {  // one: binary16 bits of the stand-in
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t u = z[e >> 2][e & 3];
+        if ((u & 0x7FFFu) == 0u) z[e >> 2][e & 3] = (u & 0xFFFF0000u) | one;
+      }
+    };
+    // the channel-wise stand-in 2^(es - 1), es = ((max scale bits) >> 10) - 14:
+    // binary16 exponent field (max bits) >> 10, or 2^-15 (0x0200) below the
+    // normal range
+    auto half_top_s = [](uint32_t mb) { return (mb & 0x7C00u) ? (mb & 0x7C00u) : 0x0200u; };
 
     // ---- prologue: fold operands into this wave's LDS slots -----------------
     // the previous chunk's main loop of this wave has issued all its reads
@@ -345,7 +403,18 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     if (VAX == KVQ_TOKEN_WISE) {
       // every scale of this wave's tokens < 2^Fs (scales of 0 are replaced by
       // 1, hence Fs >= 1; bit patterns of scales >= 0 order as values)
-      const uint32_t mb = wave_max_u(max_lo16(vz[0], vz[1]));
+      uint32_t smax = 0u, smin = 0x7FFFu;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sb = vz[e >> 2][e & 3] & 0x7FFFu;
+        smax = max(smax, sb);
+        smin = min(smin, sb);
+      }
+      const uint32_t mb = wave_max_u(smax);
+      // sigma = s, or 1 where s == 0 (a constant token, or the (0, 0) of a
+      // token past the end): the rare waves that hold such a scale patch it
+      // to 1 here, so the common path needs no selects
+      if (__any(smin == 0u)) patch_zero_s(vz, 0x3C00u);
       // (fp8 P.V: P'' < 2^8 for E4M3, six binades lower)
       const int Fc = max((int)(mb >> 10) - 14, 1) + kThr - 14 + (PV8 ? 6 : 0);
       if (cb == tb) {
@@ -359,11 +428,10 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         F = Fc;
       }
       const float two_mF = ldexpf(1.f, -F);
-      // coef[t] = sigma * 2^-F / w(t); extra-tile rows hold w(t) * rho as hi + lo
-      // fp16 (sigma = s, or 1 where s == 0; rho = z / sigma). Runs start at a
+      // coef[t] = sigma * 2^-F / w(t) and the offset weight w(t) * rho in fp32
+      // (sigma = s, or 1 where s == 0; rho = z / sigma). Runs start at a
       // multiple of 4 tokens, so token e of a run has slot e % SLOTS.
       unsigned char* coef = lds + M::VA;
-      _Float16* rh = (_Float16*)(lds + M::VR);
       float rw[2][4];
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
@@ -374,43 +442,36 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
           // its E4M3 byte's bit offset (INT2 tokens 4b + 1, 4b + 3: 4)
           const float wt = PV8 ? ((BITS == 2 && (e & 1)) ? 4.f : 1.f)
                                : (float)(1 << (BITS * (e % C::SLOTS)));
-          const float sv = f16lo(vz[rr][e]), zv = f16hi(vz[rr][e]);
-          const float sg = sv != 0.f ? sv : 1.f;
+          const float sg = f16lo(vz[rr][e]), zv = f16hi(vz[rr][e]);
           // fp16 P.V: tokens of the odd slots (e odd) enter mirrored, with
-          // the scale negated and the offset z + qmax s
+          // the scale negated and the offset z + qmax s. wt / sigma is the
+          // reciprocal of sigma / wt (a power-of-two scaling: the same bits
+          // as the reciprocal of sigma times wt)
           const bool mir = !PV8 && (e & 1);
-          cf[e] = mir ? -(sg * (two_mF / wt)) : sg * (two_mF / wt);
-          rw[rr][e] = mir ? -((zv * __builtin_amdgcn_rcpf(sg) + (float)((1 << BITS) - 1)) * wt)
-                          : zv * (__builtin_amdgcn_rcpf(sg) * wt);
+          cf[e] = sg * ((mir ? -1.f : 1.f) * (two_mF / wt));
+          const float rs = __builtin_amdgcn_rcpf(sg * (1.f / wt));
+          // (a product as an fma with +0 added: read straight from the binary16
+          // z; only the sign of a zero product can differ, which no sum sees)
+          rw[rr][e] = fmaf(zv, mir ? -rs : rs, mir ? -(float)((1 << BITS) - 1) * wt : 0.f);
         }
         *(float4*)(coef + coef_off<BITS>(tb_run[rr] / 2)) = make_float4(cf[0], cf[1], cf[2], cf[3]);
-        if (PV8)  // fp32 w * rho per token, addressed like coef
-          *(float4*)(lds + M::VR + coef_off<BITS>(tb_run[rr] / 2)) =
-              make_float4(rw[rr][0], rw[rr][1], rw[rr][2], rw[rr][3]);
+        // fp32 w * rho per token, addressed like coef
+        *(float4*)(lds + M::VR + coef_off<BITS>(tb_run[rr] / 2)) = make_float4(rw[rr][0], rw[rr][1], rw[rr][2], rw[rr][3]);
       }
-      // A-operand element 2 m + hf of this block is token run hf, slot m
-      if (!PV8) {
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float a0 = rw[0][m], a1 = rw[1][m];
-          hi[m] = pack_f16x2(a0, a1);
-          lo[m] = pack_f16x2(a0 - f16lo(hi[m]), a1 - f16hi(hi[m]));
-        }
-        ((u4*)rh)[pblk] = u4{hi[0], hi[1], hi[2], hi[3]};
-        ((u4*)(rh + M::VR_LO))[pblk] = u4{lo[0], lo[1], lo[2], lo[3]};
-      }
-    } else if (glive) {
-      // (sigma, rho) of two channels per float4; fp16 P.V takes rho - kKappa
-      // (the products start from kKappa * sum P'')
+    } else {
+      // (sigma, rho) of two channels per float4 (sigma = s, or 1 where s == 0;
+      // rho = z / sigma); fp16 P.V takes rho - kKappa (the products start
+      // from kKappa * sum P'')
+      if (__any(smallest_s(vz) == 0u)) patch_zero_s(vz, 0x3C00u);
       const float kap = PV8 ? 0.f : kKappa;
+      if (glive) {
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const uint32_t p0 = vz[e >> 2][e & 3], p1 = vz[e >> 2][(e + 1) & 3];
-        const float s0 = f16lo(p0), z0 = f16hi(p0), s1 = f16lo(p1), z1 = f16hi(p1);
-        *(float4*)(lds + M::VA + vg_off<KAX, VAX>(gl, 8 * ck_s + e)) =
-            make_float4(s0 != 0.f ? s0 : 1.f, (s0 != 0.f ? z0 * __builtin_amdgcn_rcpf(s0) : z0) - kap,
-                        s1 != 0.f ? s1 : 1.f, (s1 != 0.f ? z1 * __builtin_amdgcn_rcpf(s1) : z1) - kap);
+        for (int e = 0; e < 8; e += 2) {
+          const uint32_t p0 = vz[e >> 2][e & 3], p1 = vz[e >> 2][(e + 1) & 3];
+          const float s0 = f16lo(p0), z0 = f16hi(p0), s1 = f16lo(p1), z1 = f16hi(p1);
+          *(float4*)(lds + M::VA + vg_off<KAX, VAX>(gl, 8 * ck_s + e)) =
+              make_float4(s0, z0 * __builtin_amdgcn_rcpf(s0) - kap, s1, z1 * __builtin_amdgcn_rcpf(s1) - kap);
+        }
       }
     }
     if (KAX == KVQ_CHANNEL_WISE && FP8) {
@@ -420,19 +481,20 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       // and S = alpha 2^(es + Eq - 8) acc + alpha 2^Eq sum (hi + lo/16) rho8.
       const uint32_t mb = row_max_u(max_lo16(kz[0], kz[1]));
       const int es = (int)(mb >> 10) - 14;
+      if (__any(smallest_s(kz) == 0u)) patch_zero_s(kz, half_top_s(mb));
       const float up = ldexpf(1.f, 8 - es), dn = ldexpf(1.f, es - 8);
       float sp[8], rho[8];  // index e = 2 b + t
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t pr = kz[e >> 2][e & 3];
         const float sv = f16lo(pr), zv = f16hi(pr);
-        const bool nz = sv != 0.f;
         const float wt = C::w8(C::ch8(ck_s, e & 1, e >> 1));
-        sp[e] = nz ? sv * up : 128.f;
-        rho[e] = zv * (nz ? __builtin_amdgcn_rcpf(sv) * (wt * dn) : wt * (1.f / 128.f));
+        sp[e] = sv * up;
+        rho[e] = fmaf(zv, __builtin_amdgcn_rcpf(sv) * (wt * dn), 0.f);
       }
       float2* kb = (float2*)(lds + M::KB);
       const u4* qh = (const u4*)(lds + M::QS);
+      float hb = 0.f;  // lanes ck_s < 4: the bias sum of head ck_s (every lane of a row holds each sum)
 #pragma unroll 1
       for (int qh_i = 0; qh_i < 4; ++qh_i) {
         const u4 qv = qh[qh_i * 16 + ck_s];  // positions 8 ck_s + 4 t + b
@@ -462,10 +524,11 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
           *(u2*)(qrow + 128 + 8 * ck_s) = u2{lw[0], lw[1]};
         }
         bias = row_sum(bias);
-        if (glive && ck_s == 0) {
-          const int Eq = (int)redu[qh_i];
-          kb[gl * 4 + qh_i] = make_float2(alpha * ldexpf(1.f, es + Eq - 8), alpha * ldexpf(bias, Eq));
-        }
+        hb = ck_s == qh_i ? bias : hb;
+      }
+      if (glive && ck_s < 4) {
+        const int Eq = (int)redu[ck_s];
+        kb[gl * 4 + ck_s] = make_float2(alpha * ldexpf(1.f, es + Eq - 8), alpha * ldexpf(hb, Eq));
       }
     } else if (KAX == KVQ_CHANNEL_WISE) {
       // s' = s * 2^(14 - es) with every s of the group < 2^es (s' < 2^14), and
@@ -477,6 +540,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       // rounded q'' in both terms, so rounding moves only the weight of x^.
       const uint32_t mb = row_max_u(max_lo16(kz[0], kz[1]));
       const int es = (int)(mb >> 10) - 14;
+      if (__any(smallest_s(kz) == 0u)) patch_zero_s(kz, half_top_s(mb));
       const float up = ldexpf(1.f, 14 - es), dn = ldexpf(1.f, es - 14);
       uint32_t spk[4];
       float rho[8];
@@ -487,15 +551,15 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
             const float sv = f16lo(kz[hf][m]), zv = f16hi(kz[hf][m]);
-            const bool nz = sv != 0.f;
-            sp8[4 * hf + m] = nz ? sv * up : 8192.f;
-            rho[4 * hf + m] = zv * (nz ? __builtin_amdgcn_rcpf(sv) * (C::w(m) * dn) : C::w(m) * (1.f / 8192.f));
+            sp8[4 * hf + m] = sv * up;
+            rho[4 * hf + m] = fmaf(zv, __builtin_amdgcn_rcpf(sv) * (C::w(m) * dn), 0.f);  // product, from binary16 z
           }
 #pragma unroll
         for (int m = 0; m < 4; ++m) spk[m] = pack_f16x2(sp8[m], sp8[4 + m]);
       }
       float2* kb = (float2*)(lds + M::KB);
       const u4* qh = (const u4*)(lds + M::QS);
+      float hb = 0.f;  // lanes ck_s < 4: the bias sum of head ck_s (every lane of a row holds each sum)
 #pragma unroll 1
       for (int qh_i = 0; qh_i < 4; ++qh_i) {  // one head at a time keeps few registers live
         const u4 qv = qh[qh_i * 16 + ck_s];
@@ -508,10 +572,11 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         }
         if (glive) ((u4*)(lds + M::QB + gl * M::GROUP_STRIDE + qh_i * M::HEAD_STRIDE))[ck_s] = wds;
         bias = row_sum(bias);
-        if (glive && ck_s == 0) {
-          const int Eq = (int)redu[qh_i];
-          kb[gl * 4 + qh_i] = make_float2(alpha * ldexpf(1.f, 10 + es + Eq), alpha * ldexpf(bias, Eq));
-        }
+        hb = ck_s == qh_i ? bias : hb;
+      }
+      if (glive && ck_s < 4) {
+        const int Eq = (int)redu[ck_s];
+        kb[gl * 4 + ck_s] = make_float2(alpha * ldexpf(1.f, 10 + es + Eq), alpha * ldexpf(hb, Eq));
       }
     } else {
       float4* ktok = (float4*)(lds + M::KB);  // (s', z'') of two tokens per float4
@@ -579,10 +644,6 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       }
       asrc[qd] = 4 * ls;
     }
-    const _Float16* rbase = (const _Float16*)(lds + M::VR);
-    // extra-tile rows: even = hi part, odd = lo part; only rows 0 and 1 of
-    // the accumulator are used, the others repeat them
-    const int rrow = (mn_ & 1) * M::VR_LO + 8 * mg;
     // channel-wise V with fp8 P.V: 2^-F / E4M3 weight of the even / odd tokens
     const float cw8[2] = {ldexpf(1.f, -F), ldexpf(1.f, -F) / (BITS == 2 ? 4.f : 1.f)};
     float cw[2];  // channel-wise V: 2^-F / weight of the compact values' tokens
@@ -593,6 +654,12 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       cw[aa] = (aa ? -1.f : 1.f) * ldexpf(1.f, -F) / (float)(1 << (BITS * (slot % C::SLOTS)));
     }
     const float Qh = KAX == KVQ_TOKEN_WISE ? red[20 + mhh] : 0.f;
+    // token-wise V: byte offsets of this lane's coefficient pairs within an
+    // iteration. An iteration starts at a multiple of 64 tokens (32 pairs,
+    // two whole 16-pair blocks), so pair rel / 2 + r sits at 4 rel + the
+    // offset of pair r, and r < 32 for both of the lane's pairs
+    static_assert(C::TIT == 64, "coefficient pair blocks");  // tk0 + D2 < 64: r < 32
+    const int cfo0 = coef_off<BITS>(tk0 / 2), cfo1 = coef_off<BITS>((tk0 + C::D2) / 2);
 
     // ---- main loop over this wave's iterations of the chunk: the next
     // iteration's codes are in flight while this one is computed
@@ -615,6 +682,9 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
 
       // QK^T over 16 k-steps of 8 channels per k-group: 64 tokens x 4 heads
       float S[4];
+      f4 acc;
+      float2 sb;       // channel-wise K: the group's (scale, bias)
+      float4 p0, p1;   // token-wise K: (s', z'') of the lane's tokens
       {
         const u4* qb = (const u4*)(lds + (qlive ? M::QB + (KAX == KVQ_CHANNEL_WISE ? gi : 0) * M::GROUP_STRIDE +
                                                       mhh * M::HEAD_STRIDE
@@ -656,20 +726,30 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
             else c0 = mfma(av, qb[s], c0);
           }
         }
-        const f4 acc = c0 + c1;
+        acc = c0 + c1;
+        // S[j]: the score less the running maximum, the subtraction folded
+        // into the score's affine map (one add per iteration, not four);
+        // score(j) is the score itself, for the rare moves of the maximum
         if (KAX == KVQ_CHANNEL_WISE) {
-          const float2 sb = ((const float2*)(lds + M::KB))[gi * 4 + mhh];  // scale, bias
+          sb = ((const float2*)(lds + M::KB))[gi * 4 + mhh];
+          const float nb = sb.y - m_run;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) S[j] = fmaf(acc[j], sb.x, sb.y);
+          for (int j = 0; j < 4; ++j) S[j] = fmaf(acc[j], sb.x, nb);
         } else {
           const float4* kt = (const float4*)(lds + M::KB);  // (s', z'') per token, two per float4
-          const float4 p0 = kt[(rel + tk0) / 2], p1 = kt[(rel + tk0 + C::D2) / 2];
-          S[0] = fmaf(acc[0], p0.x, p0.y * Qh);  // token tk0
-          S[1] = fmaf(acc[1], p1.x, p1.y * Qh);  // tk0 + D2
-          S[2] = fmaf(acc[2], p0.z, p0.w * Qh);  // tk0 + 1
-          S[3] = fmaf(acc[3], p1.z, p1.w * Qh);  // tk0 + D2 + 1
+          p0 = kt[(rel + tk0) / 2];
+          p1 = kt[(rel + tk0 + C::D2) / 2];
+          S[0] = fmaf(acc[0], p0.x, fmaf(p0.y, Qh, -m_run));  // token tk0
+          S[1] = fmaf(acc[1], p1.x, fmaf(p1.y, Qh, -m_run));  // tk0 + D2
+          S[2] = fmaf(acc[2], p0.z, fmaf(p0.w, Qh, -m_run));  // tk0 + 1
+          S[3] = fmaf(acc[3], p1.z, fmaf(p1.w, Qh, -m_run));  // tk0 + D2 + 1
         }
       }
+      auto score = [&](int j) {
+        if (KAX == KVQ_CHANNEL_WISE) return fmaf(acc[j], sb.x, sb.y);
+        const float4 p = (j & 1) ? p1 : p0;
+        return (j & 2) ? fmaf(acc[j], p.z, p.w * Qh) : fmaf(acc[j], p.x, p.y * Qh);
+      };
       if (t0 + C::TIT > te) {  // the split's partial last iteration only
         // (an instruction with side effects keeps this a branch: speculated,
         // the masks would cost 8 vector instructions in every iteration)
@@ -680,10 +760,16 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       }
       // m_run is the same in all lanes of a head, so a lane's own maximum
       // past m_run + kThr is the same test as its head's: the cross-lane
-      // reduction is needed only when the running maximum moves
+      // reduction is needed only when the running maximum moves (and at a
+      // wave's first scores, which stand at +inf against m_run = -inf)
       const float lmx = fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3]));
-      if (__any(lmx > m_run + (float)kThr)) {
-        const float mn = fmaxf(m_run, head_max(lmx));
+      if (__any(lmx > (float)kThr)) {
+        float Sr[4];  // the scores themselves (masked tokens stay -inf)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Sr[j] = S[j] == -INFINITY ? -INFINITY : score(j);
+        const float mn = fmaxf(m_run, head_max(fmaxf(fmaxf(Sr[0], Sr[1]), fmaxf(Sr[2], Sr[3]))));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[j] = Sr[j] - mn;
         const float sc = exp2_fast(m_run - mn);
         if (SEED) {
           // the first scores of this wave (sc = 0) plant the seed
@@ -703,7 +789,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       }
       float P[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) P[j] = exp2_fast(S[j] - m_run);
+      for (int j = 0; j < 4; ++j) P[j] = exp2_fast(S[j]);
 
       if (PV8) {
         // P'' = P * coef as an E4M3 pair hi + lo / 16 in bytes [jj0, jj1, jj2, jj3]
@@ -711,8 +797,8 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         float x0, x1, x2, x3;
         if (VAX == KVQ_TOKEN_WISE) {
           const unsigned char* cf = lds + M::VA;
-          const float2 c0 = *(const float2*)(cf + coef_off<BITS>((rel + tk0) / 2));
-          const float2 c1 = *(const float2*)(cf + coef_off<BITS>((rel + tk0 + C::D2) / 2));
+          const float2 c0 = *(const float2*)(cf + 4 * rel + cfo0);
+          const float2 c1 = *(const float2*)(cf + 4 * rel + cfo1);
           x0 = P[0] * c0.x, x1 = P[1] * c1.x, x2 = P[2] * c0.y, x3 = P[3] * c1.y;
         } else {  // P'' = P 2^-F / w8 (tk0 is even: INT2 tokens tk0 + 1, tk0 + D2 + 1 weigh 4)
           x0 = P[0] * cw8[0], x1 = P[1] * cw8[0], x2 = P[2] * cw8[1], x3 = P[3] * cw8[1];
@@ -726,8 +812,8 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
           // offset sum from the same rounded P'' (consistent offsets)
           const f2 l01 = fp8x2_val<false>(lw), l23 = fp8x2_val<true>(lw);
           const unsigned char* rb = lds + M::VR;
-          const float2 r0 = *(const float2*)(rb + coef_off<BITS>((rel + tk0) / 2));
-          const float2 r1 = *(const float2*)(rb + coef_off<BITS>((rel + tk0 + C::D2) / 2));
+          const float2 r0 = *(const float2*)(rb + 4 * rel + cfo0);
+          const float2 r1 = *(const float2*)(rb + 4 * rel + cfo1);
           float ox = X[0];
           ox = fmaf(fmaf(l01.x, 0.0625f, h01.x), r0.x, ox);
           ox = fmaf(fmaf(l01.y, 0.0625f, h01.y), r1.x, ox);
@@ -777,11 +863,24 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         uint32_t pk[2];
         if (VAX == KVQ_TOKEN_WISE) {
           const unsigned char* cf = lds + M::VA;
-          const float2 c0 = *(const float2*)(cf + coef_off<BITS>((rel + tk0) / 2));
-          const float2 c1 = *(const float2*)(cf + coef_off<BITS>((rel + tk0 + C::D2) / 2));
+          const float2 c0 = *(const float2*)(cf + 4 * rel + cfo0);
+          const float2 c1 = *(const float2*)(cf + 4 * rel + cfo1);
           pk[0] = pack_f16x2(P[0] * c0.x, P[1] * c1.x);
           pk[1] = pack_f16x2(P[2] * c0.y, P[3] * c1.y);
           lsum += (P[0] + P[1]) + (P[2] + P[3]);
+          // offset sum over the same rounded P'' (consistent offsets): the
+          // lane's four tokens times their fp32 w * rho, addressed like coef.
+          // Four VALU operations in place of an extra matrix tile (two
+          // products per iteration, which the vector unit waits out).
+          const unsigned char* rb = lds + M::VR;
+          const float2 r0 = *(const float2*)(rb + 4 * rel + cfo0);
+          const float2 r1 = *(const float2*)(rb + 4 * rel + cfo1);
+          float ox = X[0];
+          ox = fmaf(f16lo(pk[0]), r0.x, ox);  // token tk0
+          ox = fmaf(f16hi(pk[0]), r1.x, ox);  // tk0 + D2
+          ox = fmaf(f16lo(pk[1]), r0.y, ox);  // tk0 + 1
+          ox = fmaf(f16hi(pk[1]), r1.y, ox);  // tk0 + D2 + 1
+          X[0] = ox;
         } else {
           pk[0] = pack_f16x2(P[0] * cw[0], P[1] * cw[0]);
           pk[1] = pack_f16x2(P[2] * cw[1], P[3] * cw[1]);
@@ -799,7 +898,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
             bp[k][m] = mn_ < 4 ? v : 0u;
           }
 
-        // PV: 8 channel tiles + the extra tile, 2 k-steps of 32 tokens
+        // PV: 8 channel tiles, 2 k-steps of 32 tokens
         if (VAX == KVQ_TOKEN_WISE) {
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
@@ -809,8 +908,6 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
               const u4 av = BITS == 4 ? unpack4v(w) : unpack2v(w, k);
               O[c] = mfma(av, bp[k], O[c]);
             }
-            const int pos = ((rel / C::TIT) * C::NK + k) * 32;  // wave-uniform part
-            X = mfma(*(const u4*)(rbase + rrow + pos), bp[k], X);
           }
         } else {
           // offset weights from the extra tile: row 0 holds +-w 2^-14 (minus
@@ -900,7 +997,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     lw = lsum;
   } else if (VAX == KVQ_TOKEN_WISE) {
     lsum = head_sum(lsum);
-    const float off = __shfl(X[0] + X[1], n);
+    const float off = head_sum(X[0]);  // head n & 3's offset sum (every lane of the head)
     const float s24 = ldexpf(1.f, F + 24), sF = ldexpf(1.f, F);
     // (O - kseed) 2^(F + 24) + off 2^F
     const float offk = fmaf(-kseed, s24, off * sF);

@@ -182,6 +182,12 @@ __device__ inline Split find_split(const DecodeArgs& a, int* scratch) {
   return uniform(s);
 }
 
+// a compile-time flag as a value (selects a specialisation of a generic lambda)
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 __device__ inline h8 as_h8(u4 v) { return __builtin_bit_cast(h8, v); }
 __device__ inline f4 mfma(u4 a, u4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a), as_h8(b), c, 0, 0, 0);
@@ -525,9 +531,8 @@ struct Lds {
   static constexpr int VG_BLOCK = 32 * 8 + 16;                   // chan-V: 32 channels' (sigma, rho) + 16 B padding
   static constexpr int VG_GROUP = 4 * VG_BLOCK;                  // chan-V: one 128-token group
   static constexpr int VA_BYTES = VAX == KVQ_TOKEN_WISE ? kChunkTokens * 4 : kMaxGroups * VG_GROUP;
-  static constexpr int VR = VA + VA_BYTES;                       // tok-V rho hi, lo rows, fp16, A-operand order
-  static constexpr int VR_LO = kChunkTokens + 32;                // lo row offset in halfwords (64 B off the hi row's banks)
-  static constexpr int VR_BYTES = VAX == KVQ_TOKEN_WISE ? 2 * VR_LO * 2 : 0;
+  static constexpr int VR = VA + VA_BYTES;                       // tok-V fp32 w * rho [tokens], addressed like coef
+  static constexpr int VR_BYTES = VAX == KVQ_TOKEN_WISE ? kChunkTokens * 4 : 0;
   static constexpr int RED = VR + VR_BYTES;                      // float [32] reductions
   static constexpr int TOTAL = RED + 32 * 4;
   // merge area reuses the front of LDS after the main loop
