@@ -60,9 +60,9 @@ def parse():
                    help="skip the graph-replayed timings of the short calls")
     p.add_argument("--no-groups", action="store_true",
                    help="skip the token-wise G = 128 / 64 / 32 timings")
-    p.add_argument("--only", choices=["int2", "int4", "bf16", "pack"], default=None,
-                   help="time one bit width, or only the bf16 decode, or only kv_quantize_pack "
-                        "(profiling runs)")
+    p.add_argument("--only", choices=["int2", "int4", "bf16", "pack", "probe"], default=None,
+                   help="time one bit width, or only the bf16 decode, or only kv_quantize_pack, or "
+                        "only the matrix/vector issue probe (profiling runs)")
     p.add_argument("--no-small", action="store_true",
                    help="skip the tiny / mid configurations (cache-resident and cold timings)")
     p.add_argument("--no-pack", action="store_true", help="skip the kv_quantize_pack timing")
@@ -305,6 +305,33 @@ def share_timings(B, L, widths, args, dev, stream):
                     "stall inside the timed blocks, not kernel time")
                 log(f"warning: TP-8 share INT{bits} eager {us:.1f} us vs graph {usg:.1f} us")
     res["shape"] = f"B={B} x {L} tokens, 1 KV head x 4 query heads (decode + combine)"
+    return res
+
+
+def issue_probe(dev, stream, iters=4000, reps=3):
+    """Do matrix products and vector instructions of one SIMD overlap? kvq_issue_probe at four
+    work-groups of 256 per CU (four waves per SIMD): ns per step of 8 products (mode 0), 32 fmas
+    (mode 1), both in every wave (mode 2), one kind per wave (mode 3); medians of `reps` timed
+    calls after one warm-up each. Without overlap, modes 2 and 3 take about the sum of 0 and 1."""
+    import torch
+    import bit_quantized_kv_int2_amd as kvq
+    blocks = 1024
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    res = {}
+    for mode, name in enumerate(("mfma_only", "valu_only", "both_per_wave", "split_waves")):
+        kvq.kvq_issue_probe(mode, 100, blocks, out)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            kvq.kvq_issue_probe(mode, iters, blocks, out)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e6 / iters)
+        res[name + "_ns_per_step"] = round(float(np.median(ts)), 2)
+    res["sum_of_alone_ns"] = round(res["mfma_only_ns_per_step"] + res["valu_only_ns_per_step"], 2)
+    res["what"] = ("per wave and step: 8 v_mfma_f32_16x16x32_f16 and/or 32 v_fma_f32, 4 waves per "
+                   "SIMD, 1024 work-groups, %d steps" % iters)
     return res
 
 
@@ -557,6 +584,9 @@ def main():
     B, L = args.batch, args.seq_len
     H, Hq, D = 8, 32, 128
     scale = 1.0 / math.sqrt(D)
+    if args.only == "probe":  # the issue probe alone, as one JSON line
+        print(json.dumps({"issue_probe": issue_probe(dev, stream)}), flush=True)
+        return
     if args.only == "pack":  # the producer alone (profiling runs): its timing as one JSON line
         print(json.dumps({"kv_quantize_pack": pack_timings(B, L, dev, stream, steps=args.steps)}),
               flush=True)
@@ -713,6 +743,7 @@ def main():
     pack = None
     if not args.no_pack and args.only is None:
         pack = pack_timings(B, L, dev, stream)
+    probe = issue_probe(dev, stream) if args.only is None else None
 
     # ---- CPU oracle on a bounded sample (rank 0, one GPU) --------------------
     cpu = None
@@ -844,6 +875,7 @@ def main():
         "paged_long_context": paged,
         "fp8_qk": fp8 or None,
         "kv_quantize_pack": pack,
+        "issue_probe": probe,
         "small_configs": small,
         "provenance": provenance(),
     }

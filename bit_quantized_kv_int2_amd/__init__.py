@@ -91,6 +91,7 @@ def lib():
         L.decode_attention_bf16.argtypes = [FP, _P, _P, _P, _P, _P, _I, _I, _I, ctypes.c_float,
                                             _P, _I, _I, _P, ctypes.c_size_t, _P]
         L.kvq_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _P]
+        L.kvq_issue_probe.argtypes = [_I, _I, _I, _P, _P]
         L.kv_append.argtypes = [FP, _P, _P, _P, _P, _I, _I, _I, ctypes.POINTER(Cache), _P, _P, _P]
         L.kvq_window_workspace_size.argtypes = [FP, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]
         L.decode_attention_quant_window.argtypes = [FP, _P, ctypes.POINTER(Cache), _P, _P, _P, _P,
@@ -100,7 +101,7 @@ def lib():
                    "kvq_plan_splits_for_lengths", "kvq_auto_plan", "kvq_workspace_size",
                    "kv_quantize_pack", "decode_attention_quant", "decode_attention_quant_fp8",
                    "decode_attention_quant_noalloc", "decode_attention_bf16",
-                   "kvq_stream_read", "kv_append", "kvq_window_workspace_size",
+                   "kvq_stream_read", "kvq_issue_probe", "kv_append", "kvq_window_workspace_size",
                    "decode_attention_quant_window"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
@@ -326,3 +327,14 @@ def kvq_stream_read(buf, sink, nbytes=None, stream=None):
     _require_gpu(buf, sink)
     n = buf.numel() * buf.element_size() if nbytes is None else nbytes
     _check(lib().kvq_stream_read(_ptr(buf), n, _ptr(sink), _stream(stream)), "kvq_stream_read")
+
+
+def kvq_issue_probe(mode, iters, blocks, out, stream=None):
+    """Measurement: matrix-product / vector-instruction overlap probe (modes 0-3); out is a
+    float32 device tensor of at least blocks * 256 elements."""
+    import torch
+    _require_gpu(out)
+    if out.dtype != torch.float32 or out.numel() < blocks * 256:
+        raise ValueError("kvq_issue_probe: out must be float32 with blocks * 256 elements")
+    _check(lib().kvq_issue_probe(int(mode), int(iters), int(blocks), _ptr(out), _stream(stream)),
+           "kvq_issue_probe")

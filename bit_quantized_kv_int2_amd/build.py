@@ -22,7 +22,10 @@ HIPCC_FLAGS = [
 # bit can be cleared, so float max needs no operand canonicalisation and a
 # DPP row rotation folds into the max itself.
 EXTRA_FLAGS = {"kvq_decode.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
-               "kvq_decode_tg.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+               "kvq_decode_tg.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+               # the issue probe's products keep their accumulators in VGPRs
+               # (no accumulator-register copies inside its timed loops)
+               "kvq_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(hipcc, src, obj):

@@ -723,4 +723,12 @@ kvq_status kvq_stream_read(const void* data, size_t bytes, uint32_t* sink, void*
   return hip_status(launch_stream_read(data, bytes, sink, (hipStream_t)stream));
 }
 
+kvq_status kvq_issue_probe(int mode, int iters, int blocks, float* out, void* stream) {
+  if (!out) return KVQ_ERR_NULL_POINTER;
+  if ((uintptr_t)out & 3u) return KVQ_ERR_MISALIGNED;
+  if (mode < 0 || mode > 3 || iters < 1 || blocks < 1 || blocks > 65535) return KVQ_ERR_BAD_SHAPE;
+  clear_stale_error();
+  return hip_status(launch_issue_probe(mode, iters, blocks, out, (hipStream_t)stream));
+}
+
 }  // extern "C"

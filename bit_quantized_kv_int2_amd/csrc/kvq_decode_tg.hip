@@ -11,7 +11,10 @@
 //   P.V, operand-fold per channel group:
 //     O_d = sum_t (P_t s_{t,j(d)}) c_{t,d} + sum_t P_t z_{t,j(d)}
 //     every 16-channel tile lies in one group (tile c = channels 16c..16c+15)
-//     and takes that group's P'' operand; one offset tile per group.
+//     and takes that group's P'' operand; the offset sum of each group runs
+//     on the vector unit over the same rounded P'' (four fmas per group and
+//     iteration in place of two matrix products, which the vector unit would
+//     wait out on gfx950).
 // Everything else (block-diagonal QK^T, token maps, subnormal operands,
 // consistent offsets, lazy softmax, wave-local chunks) is as in the G = 128
 // kernel; a chunk holds 2048 / NG tokens so its fold operands fit the same LDS.
@@ -32,10 +35,8 @@ struct TgLds {
   static constexpr int KB_BYTES = CHUNK * NG * 8 + CHUNK;    // + 16 B per 16-token run
   static constexpr int VA = KB + KB_BYTES;                   // float coef [NG][CHUNK], pairs XOR-permuted
   static constexpr int VA_GROUP = CHUNK * 4;
-  static constexpr int VR = VA + NG * VA_GROUP;              // fp16 offset-tile rows [NG][hi, lo][VR_LO]
-  static constexpr int VR_LO = CHUNK + 32;                   // halfwords (lo row 64 B off the hi row's banks)
-  static constexpr int VR_GROUP = 2 * VR_LO;                 // halfwords per group
-  static constexpr int RED = VR + NG * VR_GROUP * 2;         // float [32]: q max per head, q sums per (head, group)
+  static constexpr int VR = VA + NG * VA_GROUP;              // float w * rho [NG][CHUNK], addressed like coef
+  static constexpr int RED = VR + NG * VA_GROUP;             // float [32]: q max per head, q sums per (head, group)
   static constexpr int TOTAL = RED + 32 * 4;
   static constexpr int MO = 0;                               // merge area (after the main loop)
   static constexpr int ML = MO + 4 * 4 * 128 * 4;
@@ -169,10 +170,11 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
   f4 O[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) O[c] = f4{0.f, 0.f, 0.f, 0.f};
-  f4 X[NG];  // offset tile per group
+  float X[NG];  // this lane's part of its head's offset sum, per group
 #pragma unroll
-  for (int j = 0; j < NG; ++j) X[j] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NG; ++j) X[j] = 0.f;
   float m_run = -INFINITY;
+  float mneg = 0.f;  // -m_run once the first scores are in (0 before)
   float lsum = 0.f;
   int F = 0;  // P'' = P * s * 2^-F / w, running per wave
   float kseed = 0.f;  // the running output's start value (kSeedV), scaled along
@@ -188,7 +190,6 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
     const int lb = pl % (64 / NG), pj = pl / (64 / NG);
     const int bu = lb & 15;
     const int pit = 2 * (wv + 4 * (lb >> 4)) + (bu >> 3);
-    const int pblk = pit * 8 + (bu & 7);
     int tb_run[2];
     {
       const int ks = (bu >> 2) & 1, gg = bu & 3;
@@ -213,12 +214,25 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     {
       // every scale of this wave's tokens < 2^Fs (scales of 0 count as 1)
-      uint32_t mb = 0;
+      uint32_t mb = 0, smin = 0x7FFFu;
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mb = max(mb, vz[rr][e] & 0x7FFFu);
+        for (int e = 0; e < 4; ++e) {
+          mb = max(mb, vz[rr][e] & 0x7FFFu);
+          smin = min(smin, vz[rr][e] & 0x7FFFu);
+        }
       mb = wave_max_u(mb);
+      // sigma = s, or 1 where s == 0 (a constant token group, or the (0, 0)
+      // read past the end): patched into the words by the rare waves that
+      // hold one, so the common formulas need no selects
+      if (__any(smin == 0u)) {
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if ((vz[rr][e] & 0x7FFFu) == 0u) vz[rr][e] = (vz[rr][e] & 0xFFFF0000u) | 0x3C00u;
+      }
       const int Fc = max((int)(mb >> 10) - 14, 1) + kThr - 14;
       if (cb == tb) {
         F = Fc;
@@ -233,34 +247,24 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
       }
       const float two_mF = ldexpf(1.f, -F);
       unsigned char* coef = lds + M::VA + pj * M::VA_GROUP;
-      _Float16* rh = (_Float16*)(lds + M::VR) + pj * M::VR_GROUP;
-      float rw[2][4];
+      unsigned char* rwp = lds + M::VR + pj * M::VA_GROUP;
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
-        float cf[4];
+        float cf[4], rw[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float wt = (float)(1 << (BITS * (e % C::SLOTS)));
-          const float sv = f16lo(vz[rr][e]), zv = f16hi(vz[rr][e]);
-          const float sg = sv != 0.f ? sv : 1.f;
+          const float sg = f16lo(vz[rr][e]), zv = f16hi(vz[rr][e]);
           // tokens of the odd slots (e odd) enter mirrored: scale negated,
-          // offset z + qmax s
+          // offset z + qmax s; wt / sigma as the reciprocal of sigma / wt
           const bool mir = e & 1;
-          cf[e] = mir ? -(sg * (two_mF / wt)) : sg * (two_mF / wt);
-          rw[rr][e] = mir ? -((zv * __builtin_amdgcn_rcpf(sg) + (float)((1 << BITS) - 1)) * wt)
-                          : zv * (__builtin_amdgcn_rcpf(sg) * wt);
+          cf[e] = sg * ((mir ? -1.f : 1.f) * (two_mF / wt));
+          const float rs = __builtin_amdgcn_rcpf(sg * (1.f / wt));
+          rw[e] = fmaf(zv, mir ? -rs : rs, mir ? -(float)((1 << BITS) - 1) * wt : 0.f);
         }
         *(float4*)(coef + coef_off<BITS>(tb_run[rr] / 2)) = make_float4(cf[0], cf[1], cf[2], cf[3]);
+        *(float4*)(rwp + coef_off<BITS>(tb_run[rr] / 2)) = make_float4(rw[0], rw[1], rw[2], rw[3]);
       }
-      uint32_t hi[4], lo[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float a0 = rw[0][m], a1 = rw[1][m];
-        hi[m] = pack_f16x2(a0, a1);
-        lo[m] = pack_f16x2(a0 - f16lo(hi[m]), a1 - f16hi(hi[m]));
-      }
-      ((u4*)rh)[pblk] = u4{hi[0], hi[1], hi[2], hi[3]};
-      ((u4*)(rh + M::VR_LO))[pblk] = u4{lo[0], lo[1], lo[2], lo[3]};
       // token-wise K: (s', z'') of (token, group pj)
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr)
@@ -287,7 +291,11 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
         const int sg = BITS == 2 ? 2 * k + m2 : 2 * (mg & 1) + m2;
         src[k][m2] = 4 * (mhh + 4 * sq + 16 * sg);
       }
-    const int rrow = (mn_ & 1) * M::VR_LO + 8 * mg;
+    // byte offsets of the lane's coefficient pairs within an iteration
+    // (iterations start at multiples of 64 tokens: pair rel / 2 + r sits at
+    // 4 rel + the offset of pair r, r < 32)
+    static_assert(C::TIT == 64, "coefficient pair blocks");
+    const int cfo0 = coef_off<BITS>(tk0 / 2), cfo1 = coef_off<BITS>((tk0 + C::D2) / 2);
     float Qs[NG];
 #pragma unroll
     for (int j = 0; j < NG; ++j) Qs[j] = red[16 + mhh * 4 + j];
@@ -320,7 +328,7 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
         for (int q4 = 0; q4 < 4; ++q4) {
           const int t = rel + tk0 + (q4 >> 1) + C::D2 * (q4 & 1);  // S[q4]'s token
           const float4* kt = (const float4*)(lds + M::KB + M::kb_off(t));  // two groups per float4
-          float sv = 0.f;
+          float sv = mneg;  // the score less the running maximum
 #pragma unroll
           for (int j2 = 0; j2 < NG; j2 += 2) {
             const float4 p = kt[j2 / 2];
@@ -338,10 +346,17 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
       }
       // m_run is the same in all lanes of a head, so a lane's own maximum
       // past m_run + kThr is the same test as its head's: the cross-lane
-      // reduction is needed only when the running maximum moves
+      // reduction is needed only when the running maximum moves, and for
+      // the wave's first scores
       const float lmx = fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3]));
-      if (__any(lmx > m_run + (float)kThr)) {
-        const float mn = fmaxf(m_run, head_max(lmx));
+      if (m_run == -INFINITY || __any(lmx > (float)kThr)) {
+        float Sr[4];  // the scores (to the rounding of S - mneg); masked stay -inf
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Sr[j] = S[j] == -INFINITY ? -INFINITY : S[j] - mneg;
+        const float mn = fmaxf(m_run, head_max(fmaxf(fmaxf(Sr[0], Sr[1]), fmaxf(Sr[2], Sr[3]))));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S[j] = Sr[j] - mn;
+        mneg = -mn;
         const float sc = exp2_fast(m_run - mn);
         // the first scores of this wave (sc = 0) plant the seed
         const float k0 = m_run == -INFINITY ? kSeedV : 0.f;
@@ -357,25 +372,35 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
       }
       float P[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) P[j] = exp2_fast(S[j] - m_run);
+      for (int j = 0; j < 4; ++j) P[j] = exp2_fast(S[j]);
       lsum += (P[0] + P[1]) + (P[2] + P[3]);
 
       // PV, one channel group at a time: its P'' operand, its tiles, its offset tile
 #pragma unroll
       for (int j = 0; j < NG; ++j) {
         const unsigned char* cf = lds + M::VA + j * M::VA_GROUP;
-        const float2 c0 = *(const float2*)(cf + coef_off<BITS>((rel + tk0) / 2));
-        const float2 c1 = *(const float2*)(cf + coef_off<BITS>((rel + tk0 + C::D2) / 2));
+        const float2 c0 = *(const float2*)(cf + 4 * rel + cfo0);
+        const float2 c1 = *(const float2*)(cf + 4 * rel + cfo1);
         uint32_t pk[2];
         pk[0] = pack_f16x2(P[0] * c0.x, P[1] * c1.x);
         pk[1] = pack_f16x2(P[2] * c0.y, P[3] * c1.y);
+        {  // the group's offset sum over the same rounded P''
+          const unsigned char* rb = lds + M::VR + j * M::VA_GROUP;
+          const float2 r0 = *(const float2*)(rb + 4 * rel + cfo0);
+          const float2 r1 = *(const float2*)(rb + 4 * rel + cfo1);
+          float ox = X[j];
+          ox = fmaf(f16lo(pk[0]), r0.x, ox);  // token tk0
+          ox = fmaf(f16hi(pk[0]), r1.x, ox);  // tk0 + D2
+          ox = fmaf(f16lo(pk[1]), r0.y, ox);  // tk0 + 1
+          ox = fmaf(f16hi(pk[1]), r1.y, ox);  // tk0 + D2 + 1
+          X[j] = ox;
+        }
         u4 bp[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k)
 #pragma unroll
           for (int m = 0; m < 4; ++m)
             bp[k][m] = (uint32_t)__builtin_amdgcn_ds_bpermute(src[k][m >> 1], (int)pk[m & 1]);
-        const _Float16* rbase = (const _Float16*)(lds + M::VR) + j * M::VR_GROUP;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
 #pragma unroll
@@ -385,8 +410,6 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
             const u4 av = BITS == 4 ? unpack4v(w) : unpack2v(w, k);
             O[c] = mfma(av, bp[k], O[c]);
           }
-          const int pos = ((rel / C::TIT) * C::NK + k) * 32;
-          X[j] = mfma(*(const u4*)(rbase + rrow + pos), bp[k], X[j]);
         }
       }
       cur = nxt;
@@ -400,7 +423,7 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
     const float s24 = ldexpf(1.f, F + 24), sF = ldexpf(1.f, F);
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
-      const float off = __shfl(X[j][0] + X[j][1], n);  // rows 0, 1 live in lane group 0
+      const float off = head_sum(X[j]);  // head n & 3's offset sum of group j
       const float offk = fmaf(-kseed, s24, off * sF);    // (O - kseed) 2^(F + 24) + off 2^F
 #pragma unroll
       for (int ct = 0; ct < TPG; ++ct)

@@ -228,5 +228,6 @@ hipError_t launch_combine_plan(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 // Reads bytes (a multiple of 16) once; the HBM read reference for measurement.
 hipError_t launch_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_issue_probe(int mode, int iters, int blocks, float* out, hipStream_t s);
 
 }  // namespace kvq

@@ -1,7 +1,16 @@
-// Streaming-read reference kernel: reads a buffer once with 128-bit
-// non-temporal loads (as the decode kernels stream their codes). It is the
-// practical HBM read ceiling that the decode rates are compared against
-// (same byte count, no arithmetic beyond an XOR per word).
+// Measurement kernels, not part of the method.
+//  * Streaming-read reference: reads a buffer once with 128-bit non-temporal
+//    loads (as the decode kernels stream their codes). It is the practical
+//    HBM read ceiling that the decode rates are compared against (same byte
+//    count, no arithmetic beyond an XOR per word).
+//  * Issue probe: whether matrix products and vector instructions of the
+//    same SIMD overlap. Each wave runs `iters` steps of 8 independent
+//    16x16x32 fp16 products (mode 0), of 32 independent-chain fp32 fmas
+//    (mode 1), of both interleaved 4 fmas : 1 product (mode 2), or of one
+//    kind per wave, alternating between the waves of a work-group (mode 3).
+//    Four work-groups of 256 per CU give 4 waves per SIMD; if the two
+//    overlapped, modes 2 and 3 would take about as long as the longer of
+//    modes 0 and 1.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -37,7 +46,69 @@ __global__ void __launch_bounds__(kStreamThreads) stream_read_kernel(const u4* _
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+template <int MODE>
+__global__ void __launch_bounds__(256) issue_probe_kernel(float* out, int iters) {
+  const int lane = threadIdx.x & 63;
+  const int par = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6) & 1);
+  h8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (_Float16)((lane + i) & 7);
+    b[i] = (_Float16)((lane * 3 + i) & 7);
+  }
+  f4 acc[8];
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    acc[j] = f4{0.f, 0.f, 0.f, 0.f};
+    x[j] = (float)(lane + j) * 0.001f;
+  }
+  const float c = 0.999f, d = 0.0001f;
+  const bool dom = MODE == 0 || MODE == 2 || (MODE == 3 && par == 0);
+  const bool dov = MODE == 1 || MODE == 2 || (MODE == 3 && par == 1);
+  if (dom && dov) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[(j + u) & 7] = fmaf(x[(j + u) & 7], c, d);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
+      }
+    }
+  } else if (dom) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
+    }
+  } else if (dov) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[(j + u) & 7] = fmaf(x[(j + u) & 7], c, d);
+    }
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sum += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3] + x[j];
+  out[blockIdx.x * 256 + threadIdx.x] = sum;
+}
+
 }  // namespace
+
+hipError_t launch_issue_probe(int mode, int iters, int blocks, float* out, hipStream_t s) {
+  const dim3 grid((unsigned)blocks), block(256);
+  switch (mode) {
+    case 0: issue_probe_kernel<0><<<grid, block, 0, s>>>(out, iters); break;
+    case 1: issue_probe_kernel<1><<<grid, block, 0, s>>>(out, iters); break;
+    case 2: issue_probe_kernel<2><<<grid, block, 0, s>>>(out, iters); break;
+    default: issue_probe_kernel<3><<<grid, block, 0, s>>>(out, iters); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void* data, size_t bytes, uint32_t* sink, hipStream_t s) {
   const size_t n16 = bytes / 16;

@@ -353,6 +353,25 @@ kvq_status decode_attention_quant_window(const kvq_format* fmt, const void* q,
  */
 kvq_status kvq_stream_read(const void* data, size_t bytes, uint32_t* sink, void* stream);
 
+/*
+ * kvq_issue_probe -- measurement, not part of the method: whether a SIMD
+ * overlaps matrix products with vector instructions. It decides how the
+ * decode kernels trade one for the other (an extra 16x16x32 product against
+ * a few fmas). `blocks` work-groups of 256 work-items (1024 = four per CU,
+ * four waves per SIMD) each run `iters` steps of
+ *   mode 0: 8 independent v_mfma_f32_16x16x32_f16 per wave,
+ *   mode 1: 32 fp32 fmas (8 independent chains) per wave,
+ *   mode 2: both in every wave, 4 fmas before each product,
+ *   mode 3: mode 0 in even waves, mode 1 in odd waves.
+ *   out    device float[blocks * 256], written once per work-item (a sum that
+ *          keeps the work alive).
+ * Time it with events around the call. Returns KVQ_ERR_NULL_POINTER /
+ * KVQ_ERR_MISALIGNED / KVQ_ERR_BAD_SHAPE (mode outside 0..3, iters < 1,
+ * blocks outside 1..65535) with nothing launched, KVQ_ERR_HIP on a failed
+ * launch.
+ */
+kvq_status kvq_issue_probe(int mode, int iters, int blocks, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

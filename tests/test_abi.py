@@ -48,6 +48,16 @@ def test_stream_read_validation_without_gpu(L):
     assert f(A, 0, A, None) == OK  # nothing to read, nothing launched
 
 
+def test_issue_probe_validation_without_gpu(L):
+    f = L.kvq_issue_probe
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    A = 4096
+    assert f(0, 10, 4, None, None) == NULLP
+    assert f(0, 10, 4, A + 2, None) == MISALIGNED
+    for mode, iters, blocks in [(-1, 10, 4), (4, 10, 4), (0, 0, 4), (1, 10, 0), (2, 10, 65536)]:
+        assert f(mode, iters, blocks, A, None) == BADSHAPE, (mode, iters, blocks)
+
+
 def test_layout_version_and_status_strings(L):
     assert L.kvq_layout_version() == kvq.LAYOUT_VERSION
     for s in range(7):
