@@ -96,9 +96,6 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
   // ---- cache addressing (contiguous caches) -----------------------------
   const long unit = (long)b * H + h;
   auto chunk_of = [&](int t) -> long { return unit * (a.padded_len / kPage) + t / kPage; };
-  auto pair_at = [&](const uint16_t* sz, int t, int j) -> const uint32_t* {
-    return (const uint32_t*)(sz + ((chunk_of(t) * kPage + t % kPage) * NG + j) * 2);
-  };
 
   const int n = lane & 15, g = lane >> 4, hh = n & 3;
   const int ri = lane & 15;
@@ -183,44 +180,49 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
     const int ce = min(cb + M::CHUNK, te);
     const int ntok = ce - cb;
 
-    // ---- prologue: lane l builds group pj = l / (64/NG) of the 8-token
-    // A-operand block lb = l % (64/NG) of this wave's tokens ----------------
+    // ---- prologue: lane l takes TPL = 8 / NG consecutive tokens of this
+    // wave's blocks (128-token blocks wv, wv + 4, .. of the chunk), all NG
+    // channel groups of each: one contiguous 4 NG-byte (s, z) row per token
+    // and tensor. The lane's first token t0 is a multiple of TPL, so a
+    // token's code slot within its 4-token run is (t0 & 3) + u.
+    constexpr int TPL = 8 / NG;
     int pl = lane;
     asm volatile("" : "+v"(pl));
-    const int lb = pl % (64 / NG), pj = pl / (64 / NG);
-    const int bu = lb & 15;
-    const int pit = 2 * (wv + 4 * (lb >> 4)) + (bu >> 3);
-    int tb_run[2];
-    {
-      const int ks = (bu >> 2) & 1, gg = bu & 3;
-      if (BITS == 2) {
-        tb_run[0] = pit * C::TIT + 16 * gg + 4 * ks;
-        tb_run[1] = tb_run[0] + 8;
-      } else {
-        tb_run[0] = pit * C::TIT + 32 * ks + 8 * gg;
-        tb_run[1] = tb_run[0] + 4;
+    const int tw = pl * TPL;  // index into the wave's tokens of the chunk
+    const int t0 = 128 * (wv + 4 * (tw >> 7)) + (tw & 127);
+    typedef uint32_t row_t __attribute__((ext_vector_type(NG)));
+    // the chunk's rows sit at a base shared by the wave plus a 32-bit lane offset
+    const long szb = (unit * a.padded_len + cb) * (long)(4 * NG);
+    const unsigned char* krow = (const unsigned char*)a.k_sz + szb;
+    const unsigned char* vrow = (const unsigned char*)a.v_sz + szb;
+    row_t kz[TPL], vz[TPL];
+    if (ntok == M::CHUNK) {  // a whole chunk: no token past the end
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        kz[u] = *(const row_t*)(krow + (uint32_t)(4 * NG * (t0 + u)));
+        vz[u] = *(const row_t*)(vrow + (uint32_t)(4 * NG * (t0 + u)));
+      }
+    } else {  // tokens past the end read as (0, 0)
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        kz[u] = row_t(0u);
+        vz[u] = row_t(0u);
+        if (t0 + u < ntok) {
+          kz[u] = *(const row_t*)(krow + (uint32_t)(4 * NG * (t0 + u)));
+          vz[u] = *(const row_t*)(vrow + (uint32_t)(4 * NG * (t0 + u)));
+        }
       }
     }
-    uint32_t kz[2][4], vz[2][4];
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = tb_run[rr] + e;
-        const bool ok = t < ntok;
-        kz[rr][e] = ok ? *pair_at(a.k_sz, cb + t, pj) : 0u;
-        vz[rr][e] = ok ? *pair_at(a.v_sz, cb + t, pj) : 0u;
-      }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     {
       // every scale of this wave's tokens < 2^Fs (scales of 0 count as 1)
       uint32_t mb = 0, smin = 0x7FFFu;
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr)
+      for (int u = 0; u < TPL; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          mb = max(mb, vz[rr][e] & 0x7FFFu);
-          smin = min(smin, vz[rr][e] & 0x7FFFu);
+        for (int j = 0; j < NG; ++j) {
+          mb = max(mb, (uint32_t)vz[u][j] & 0x7FFFu);
+          smin = min(smin, (uint32_t)vz[u][j] & 0x7FFFu);
         }
       mb = wave_max_u(mb);
       // sigma = s, or 1 where s == 0 (a constant token group, or the (0, 0)
@@ -228,10 +230,12 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
       // hold one, so the common formulas need no selects
       if (__any(smin == 0u)) {
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr)
+        for (int u = 0; u < TPL; ++u)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if ((vz[rr][e] & 0x7FFFu) == 0u) vz[rr][e] = (vz[rr][e] & 0xFFFF0000u) | 0x3C00u;
+          for (int j = 0; j < NG; ++j) {
+            const uint32_t w = vz[u][j];
+            if ((w & 0x7FFFu) == 0u) vz[u][j] = (w & 0xFFFF0000u) | 0x3C00u;
+          }
       }
       const int Fc = max((int)(mb >> 10) - 14, 1) + kThr - 14;
       if (cb == tb) {
@@ -245,33 +249,48 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
         kseed *= sc;
         F = Fc;
       }
-      const float two_mF = ldexpf(1.f, -F);
-      unsigned char* coef = lds + M::VA + pj * M::VA_GROUP;
-      unsigned char* rwp = lds + M::VR + pj * M::VA_GROUP;
+      // slot weight of token t0 + u: 2^(BITS ((t0 & 3) + u) % SLOTS)); with
+      // two tokens per lane (INT2) the lane's pair sits at slots 0, 1 or 2, 3
+      const float lw = (BITS == 2 && TPL == 2 && (t0 & 2)) ? 16.f : 1.f;
+      const float two_mF = ldexpf(1.f, -F) / lw;
+      float cf[NG][TPL], rw[NG][TPL];
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr) {
-        float cf[4], rw[4];
+      for (int u = 0; u < TPL; ++u) {
+        const float wu = (float)(1 << (BITS * (u % C::SLOTS)));  // weight / lw
+        // tokens of the odd slots (u odd) enter mirrored: scale negated,
+        // offset z + qmax s; wt / sigma as the reciprocal of sigma / wt
+        const bool mir = u & 1;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float wt = (float)(1 << (BITS * (e % C::SLOTS)));
-          const float sg = f16lo(vz[rr][e]), zv = f16hi(vz[rr][e]);
-          // tokens of the odd slots (e odd) enter mirrored: scale negated,
-          // offset z + qmax s; wt / sigma as the reciprocal of sigma / wt
-          const bool mir = e & 1;
-          cf[e] = sg * ((mir ? -1.f : 1.f) * (two_mF / wt));
-          const float rs = __builtin_amdgcn_rcpf(sg * (1.f / wt));
-          rw[e] = fmaf(zv, mir ? -rs : rs, mir ? -(float)((1 << BITS) - 1) * wt : 0.f);
+        for (int j = 0; j < NG; ++j) {
+          const float sg = f16lo(vz[u][j]), zv = f16hi(vz[u][j]);
+          cf[j][u] = sg * ((mir ? -1.f : 1.f) * (two_mF / wu));
+          const float rs = __builtin_amdgcn_rcpf(sg * ((1.f / wu) / lw));
+          rw[j][u] = fmaf(zv, mir ? -rs : rs, mir ? -(float)((1 << BITS) - 1) * wu * lw : 0.f);
         }
-        *(float4*)(coef + coef_off<BITS>(tb_run[rr] / 2)) = make_float4(cf[0], cf[1], cf[2], cf[3]);
-        *(float4*)(rwp + coef_off<BITS>(tb_run[rr] / 2)) = make_float4(rw[0], rw[1], rw[2], rw[3]);
       }
-      // token-wise K: (s', z'') of (token, group pj)
+      // coefficient pairs (t0 + u, t0 + u + 1) of each group: TPL / 2 adjacent pairs
 #pragma unroll
-      for (int rr = 0; rr < 2; ++rr)
+      for (int j = 0; j < NG; ++j) {
+        unsigned char* coef = lds + M::VA + j * M::VA_GROUP + coef_off<BITS>(t0 / 2);
+        unsigned char* rwp = lds + M::VR + j * M::VA_GROUP + coef_off<BITS>(t0 / 2);
+        if constexpr (TPL == 4) {
+          *(float4*)coef = make_float4(cf[j][0], cf[j][1], cf[j][2], cf[j][3]);
+          *(float4*)rwp = make_float4(rw[j][0], rw[j][1], rw[j][2], rw[j][3]);
+        } else {
+          *(float2*)coef = make_float2(cf[j][0], cf[j][1]);
+          *(float2*)rwp = make_float2(rw[j][0], rw[j][1]);
+        }
+      }
+      // token-wise K: (s', z'') of (token, group), the NG groups of a token adjacent
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          *(float2*)(lds + M::KB + M::kb_off(tb_run[rr] + e) + 8 * pj) =
-              make_float2(f16lo(kz[rr][e]) * ktok_sc, f16hi(kz[rr][e]) * alpha);
+      for (int u = 0; u < TPL; ++u) {
+        float2 kv[NG];
+#pragma unroll
+        for (int j = 0; j < NG; ++j) kv[j] = make_float2(f16lo(kz[u][j]) * ktok_sc, f16hi(kz[u][j]) * alpha);
+        float4* kd = (float4*)(lds + M::KB + M::kb_off(t0 + u));
+#pragma unroll
+        for (int j2 = 0; j2 < NG; j2 += 2) kd[j2 / 2] = make_float4(kv[j2].x, kv[j2].y, kv[j2 + 1].x, kv[j2 + 1].y);
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
