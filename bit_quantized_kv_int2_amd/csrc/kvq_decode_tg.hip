@@ -294,9 +294,13 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
-    // ---- per-lane constants of the main loop (laundered lane id) ---------
+    // ---- per-lane constants of the main loop: hoisted out of the chunk loop
+    // where the registers allow (chunks of 512 tokens are 2 iterations per
+    // wave, so rebuilding them per chunk costs ~20 VALU per iteration); INT2
+    // with G = 64 fits its 4 work-groups per CU only when they are rebuilt
+    // from a laundered lane id, so none of them is live through the prologue
     int mlane = lane;
-    asm volatile("" : "+v"(mlane));
+    if (BITS == 2 && NG == 2) asm volatile("" : "+v"(mlane));
     const int mn_ = mlane & 15, mg = mlane >> 4, mhh = mn_ & 3, mnq = mn_ >> 2;
     const uint32_t koff = lane_koff(mg, mn_);
     const int tk0 = C::tok(mnq, mg, 0);
