@@ -284,20 +284,17 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     // a DPP row share a group
     const int gl = wv + 4 * (pl >> 4);
     const bool glive = gl < ng;
-    // token-wise (s, z): lane l owns 8 tokens of iteration 2 gl + (l/8)%2
-    // of its group as two runs of 4 tokens, tb_run[r] .. +3 (run starts at
-    // multiples of 4 tokens: a run's token e sits in code slot e % SLOTS)
-    const int pit = 2 * gl + ((pl >> 3) & 1);
+    // token-wise (s, z): the wave's 4 groups are 128 runs of 4 tokens (32
+    // per group); lane l takes runs l and l + 64, tokens tb_run[r] .. +3.
+    // Consecutive lanes then load consecutive 16-byte (s, z) runs and store
+    // consecutive 16-byte coefficient slots (no two lanes on one bank).
+    // Runs start at multiples of 4 tokens: a run's token e sits in code slot
+    // e % SLOTS.
     int tb_run[2];
-    {
-      const int ks = (pl >> 2) & 1, gg = pl & 3;
-      if (BITS == 2) {
-        tb_run[0] = pit * C::TIT + 16 * gg + 4 * ks;
-        tb_run[1] = tb_run[0] + 8;
-      } else {
-        tb_run[0] = pit * C::TIT + 32 * ks + 8 * gg;
-        tb_run[1] = tb_run[0] + 4;
-      }
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+      const int r = pl + 64 * rr;
+      tb_run[rr] = kGroup * (wv + 4 * (r >> 5)) + 4 * (r & 31);
     }
     const int ck_s = pl & 15;  // channel-wise K: k-step of group gl; channel-wise V: channels 8 ck_s ..
 
