@@ -66,6 +66,25 @@ def test_constant_groups(bits, k_axis, v_axis):
     _check(inp, GpuRun(inp), label=f"const_int{bits}_{k_axis[0]}{v_axis[0]}")
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("k_axis,v_axis", [("channel", "token"), ("token", "channel"),
+                                           ("channel", "channel"), ("token", "token")])
+def test_constant_groups_in_whole_chunks(bits, k_axis, v_axis):
+    """s = 0 groups inside whole 2048-token chunks (where the decode loads (s, z)
+    without masks and patches zero scales to their stand-in) and in the last,
+    partial chunk."""
+    w = synth.Workload("const_chunks", 2, 2, 8, 128, [5000, 2048], bits, k_axis, v_axis, seed=43)
+    inp = Inputs(w)
+    inp.k[0, 0, :, 9] = -0.5            # a constant K channel over every chunk
+    inp.k[0, 1, 2100, :] = 1.75         # a constant K token in the second chunk
+    inp.k[1, 0, 640:768, :] = 0.25      # a whole constant K group in a whole chunk
+    inp.v[0, 1, :, 33] = -2.0           # a constant V channel
+    inp.v[0, 0, 1500, :] = 0.75         # a constant V token in the first chunk
+    inp.v[1, 1, 1920:2048, :] = 1.0     # the last group of a whole chunk, constant
+    inp.v[0, 0, 4990, :] = 0.5          # a constant V token in the partial last chunk
+    _check(inp, GpuRun(inp), label=f"const_chunks_int{bits}_{k_axis[0]}{v_axis[0]}")
+
+
 def _tie_values(rng, shape, z, s, qmax, G):
     """z + m s / 2 for m in [0, 2 qmax] (odd m: exactly on a rounding tie of
     the grid z + c s), some moved one ulp up or down; rows 128 k and channels
@@ -450,6 +469,8 @@ def test_token_wise_groups_smaller_than_head_dim(bits, group):
     inp = Inputs(w)
     inp.k[0, 0, 5, :] = 0.25           # a constant token: every group of it has s = 0
     inp.v[1, 1, 0, 32:64] = 1.5        # one constant channel group of a token
+    inp.v[0, 0, 600, :] = -0.5         # a constant V token inside a whole chunk
+    inp.k[3, 1, 1500, :32] = 2.0       # a constant K group inside a whole chunk
     inp.v[0, 1, 2000:2100, 64:] *= 30  # large V scales in some groups of a later chunk
     run = GpuRun(inp)
     out, ref = _check(inp, run, label=f"tg_int{bits}_G{group}")
