@@ -75,7 +75,10 @@ def lib():
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_status_string.argtypes = [ctypes.c_int]
         L.kvq_last_hip_error.restype = ctypes.c_int32
+        L.kvq_debug_inject_hip_error.argtypes = [ctypes.c_int32]
+        L.kvq_debug_inject_hip_error.restype = None
         L.kvq_layout_version.restype = ctypes.c_uint32
+        L.kvq_build_flags.restype = ctypes.c_uint32
         L.kvq_check_format.argtypes = [FP]
         L.kvq_cache_sizes.argtypes = [FP, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]
         L.kvq_plan_splits.argtypes = [FP, _I, _I, ctypes.POINTER(ctypes.c_int32)]
@@ -114,6 +117,12 @@ def _check(status: int, where: str):
 
 
 # ---- host-only queries -----------------------------------------------------
+
+def kvq_debug_inject_hip_error(hip_error: int) -> None:
+    """While non-zero, entry points on this thread fail with KVQ_ERR_HIP and
+    this hipError_t after their host checks, making no HIP call (0: off)."""
+    lib().kvq_debug_inject_hip_error(int(hip_error))
+
 
 def kvq_check_format(fmt: Format) -> int:
     return lib().kvq_check_format(ctypes.byref(fmt))

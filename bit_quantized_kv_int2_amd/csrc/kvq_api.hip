@@ -17,11 +17,20 @@ static kvq_status hip_status(hipError_t e) {
   return KVQ_ERR_HIP;
 }
 
-// The launches below report hipGetLastError() after each kernel. That state is
-// per thread and shared with every other HIP user in the process, so a
-// failure another library left unread (a device query, say) would be blamed
-// on this call's launch. Each entry point clears it right before launching.
-static void clear_stale_error() { (void)hipGetLastError(); }
+// Per-thread HIP error code set by kvq_debug_inject_hip_error (0: none).
+static thread_local int32_t g_inject_hip_error = 0;
+
+// Every entry point calls this once its host checks have passed, right before
+// its first HIP call. The launches below report hipGetLastError() after each
+// kernel. That state is per thread and shared with every other HIP user in the
+// process, so a failure another library left unread (a device query, say)
+// would be blamed on this call's launch: it is cleared here. With an injected
+// code set, no HIP call is made and the entry point fails with that code.
+static kvq_status begin_hip() {
+  if (g_inject_hip_error != 0) return hip_status((hipError_t)g_inject_hip_error);
+  (void)hipGetLastError();
+  return KVQ_OK;
+}
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -69,6 +78,16 @@ const char* kvq_status_string(kvq_status s) {
 }
 
 int32_t kvq_last_hip_error(void) { return g_last_hip_error; }
+
+void kvq_debug_inject_hip_error(int32_t hip_error) { g_inject_hip_error = hip_error; }
+
+uint32_t kvq_build_flags(void) {
+#ifdef KVQ_POISON_LDS
+  return KVQ_BUILD_POISON_LDS;
+#else
+  return 0;
+#endif
+}
 
 uint32_t kvq_layout_version(void) { return KVQ_LAYOUT_VERSION; }
 
@@ -384,7 +403,8 @@ kvq_status kv_quantize_pack(const kvq_format* f, const float* k, const float* v,
   a.v_words = (uint32_t*)out->v_codes;
   a.k_sz = (uint16_t*)out->k_scale_offset;
   a.v_sz = (uint16_t*)out->v_scale_offset;
-  clear_stale_error();
+  st = begin_hip();
+  if (st != KVQ_OK) return st;
   return hip_status(launch_pack(a, (hipStream_t)stream));
 }
 
@@ -428,6 +448,8 @@ static kvq_status decode_quant_impl(const kvq_format* f, const void* q, const kv
     if (need > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
     if (batch == 0) return KVQ_OK;
     if (need > 0) {
+      st = begin_hip();
+      if (st != KVQ_OK) return st;
       st = scratch_address(&workspace);
       if (st != KVQ_OK) return st;
       workspace_bytes = KVQ_NOALLOC_SCRATCH_BYTES;
@@ -477,7 +499,8 @@ static kvq_status decode_quant_impl(const kvq_format* f, const void* q, const kv
     a.part_ml = a.part_o + rows * nsplit * kHeadDim;
   }
   hipStream_t s = (hipStream_t)stream;
-  clear_stale_error();
+  st = begin_hip();
+  if (st != KVQ_OK) return st;
   st = hip_status(launch_decode_quant(*f, a, s));
   if (st != KVQ_OK) return st;
   if (dev_plan) return hip_status(launch_combine_plan(a, s));
@@ -568,7 +591,8 @@ kvq_status decode_attention_bf16(const kvq_format* f, const void* q, const void*
     a.part_ml = a.part_o + rows * nsplit * kHeadDim;
   }
   hipStream_t s = (hipStream_t)stream;
-  clear_stale_error();
+  st = begin_hip();
+  if (st != KVQ_OK) return st;
   st = hip_status(launch_decode_bf16(a, s));
   if (st != KVQ_OK || nsplit == 1) return st;
   return hip_status(launch_combine(a.part_o, a.part_ml, batch * f->num_q_heads, nsplit, out,
@@ -611,7 +635,8 @@ kvq_status kv_append(const kvq_format* f, const void* k_new, const void* v_new,
   a.v_words = (uint32_t*)cache->v_codes;
   a.k_sz = (uint16_t*)cache->k_scale_offset;
   a.v_sz = (uint16_t*)cache->v_scale_offset;
-  clear_stale_error();
+  st = begin_hip();
+  if (st != KVQ_OK) return st;
   return hip_status(launch_append(a, (hipStream_t)stream));
 }
 
@@ -686,7 +711,8 @@ kvq_status decode_attention_quant_window(const kvq_format* f, const void* q,
   a.part_ml = part_ml;
   a.part_stride = slots;
   a.len_mode = 1;  // whole groups from the cache
-  clear_stale_error();
+  st = begin_hip();
+  if (st != KVQ_OK) return st;
   st = hip_status(launch_decode_quant(*f, a, s));
   if (st != KVQ_OK) return st;
 
@@ -719,7 +745,8 @@ kvq_status kvq_stream_read(const void* data, size_t bytes, uint32_t* sink, void*
   if (!aligned16(data) || ((uintptr_t)sink & 3u)) return KVQ_ERR_MISALIGNED;
   if (bytes % 16 != 0) return KVQ_ERR_BAD_SHAPE;
   if (bytes == 0) return KVQ_OK;
-  clear_stale_error();
+  kvq_status st = begin_hip();
+  if (st != KVQ_OK) return st;
   return hip_status(launch_stream_read(data, bytes, sink, (hipStream_t)stream));
 }
 
@@ -727,7 +754,8 @@ kvq_status kvq_issue_probe(int mode, int iters, int blocks, float* out, void* st
   if (!out) return KVQ_ERR_NULL_POINTER;
   if ((uintptr_t)out & 3u) return KVQ_ERR_MISALIGNED;
   if (mode < 0 || mode > 3 || iters < 1 || blocks < 1 || blocks > 65535) return KVQ_ERR_BAD_SHAPE;
-  clear_stale_error();
+  kvq_status st = begin_hip();
+  if (st != KVQ_OK) return st;
   return hip_status(launch_issue_probe(mode, iters, blocks, out, (hipStream_t)stream));
 }
 

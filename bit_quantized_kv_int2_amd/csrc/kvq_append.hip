@@ -47,6 +47,9 @@ __global__ void __launch_bounds__(kAppendThreads) append_kernel(AppendArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t win[kGroup * kHeadDim];
 
   for (int is_k = 1; is_k >= 0; --is_k) {
+    poison_lds<kAppendThreads>(S, sizeof S);
+    poison_lds<kAppendThreads>(Z, sizeof Z);
+    poison_lds<kAppendThreads>(win, sizeof win);
     {
       const u4* src = (const u4*)(is_k ? kw : vw);
       for (int i = tid; i < kGroup * kHeadDim / 8; i += kAppendThreads) ((u4*)win)[i] = src[i];

@@ -46,6 +46,8 @@ template <bool PAGED>
 __global__ void __launch_bounds__(kThreads) bf16_kernel(Bf16Args a) {
   __shared__ __attribute__((aligned(16))) float mo[kWaves * 4 * 128];
   __shared__ float ml[kWaves * 4 * 2];
+  poison_lds<kThreads>(mo, sizeof mo);
+  poison_lds<kThreads>(ml, sizeof ml);
 
   const WorkItem wi = work_item(blockIdx.x, a.num_kv_heads, a.batch, a.num_splits);
   if (!wi.live) return;  // padding to whole rounds of 8 rows

@@ -67,6 +67,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   // built with the IEEE mode bit cleared, which keeps the device library's
   // id helpers from being inlined
   static_assert(M::TOTAL >= (8 + kThreads) * 4, "find_split borrows the start of the LDS");
+  poison_lds<kThreads>(lds, M::TOTAL);
   const Split ws = find_split(a, (int*)lds);
   if (!ws.live) return;  // padding, or past the plan's work-items
   const int sp = ws.sp, h = ws.h, b = ws.b;

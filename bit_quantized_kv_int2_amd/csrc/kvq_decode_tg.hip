@@ -62,6 +62,7 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
   float* red = (float*)(lds + M::RED);
 
   static_assert(M::TOTAL >= (8 + kThreads) * 4, "find_split borrows the start of the LDS");
+  poison_lds<kThreads>(lds, M::TOTAL);
   const Split ws = find_split(a, (int*)lds);
   if (!ws.live) return;  // padding, or past the plan's work-items
   const int sp = ws.sp, h = ws.h, b = ws.b;

@@ -17,6 +17,27 @@ constexpr int kSplitQuantum = 256; // split lengths are multiples of this
 constexpr int kChunkTokens = 2048;    // decode prologue chunk: fold operands in LDS
 constexpr int kComputeUnits = 256;    // MI355X
 
+// ---- LDS poison fill (debug build) -----------------------------------------
+// Built with KVQ_POISON_LDS defined, each kernel fills its LDS with all-ones
+// bytes (NaN in binary16, bf16 and fp32; the largest code in a code byte)
+// before its first write, and again at the top of every pass of a
+// work-group-uniform loop that reuses the LDS. A read of a byte that the
+// kernel (or that pass) did not write first then shows up in the output.
+// Every thread of the work-group must make the call: it holds two barriers.
+// In a normal build it compiles to nothing.
+template <int THREADS>
+__device__ __forceinline__ void poison_lds(void* p, int bytes) {
+#ifdef KVQ_POISON_LDS
+  __syncthreads();  // earlier readers of this LDS are done
+  uint32_t* w = (uint32_t*)p;
+  for (int i = (int)__builtin_amdgcn_workitem_id_x(); i < bytes / 4; i += THREADS) w[i] = ~0u;
+  __syncthreads();
+#else
+  (void)p;
+  (void)bytes;
+#endif
+}
+
 // Resident 256-thread decode work-groups per CU that the register allocation
 // targets (the kernels' launch bounds; 4 leave 128 VGPRs per lane, 3 leave
 // 168): INT2 fits in 128 (with channel-wise V, whose per-group partials take

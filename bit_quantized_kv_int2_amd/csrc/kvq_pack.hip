@@ -160,6 +160,9 @@ __global__ void __launch_bounds__(kPackThreads) pack_kernel(PackArgs a, Geo g, i
     const int t0 = gi * kGroup;
     const int E = g.extent(L);
     if (t0 >= E) continue;  // uniform: nothing of this tile is written
+    poison_lds<kPackThreads>(red, sizeof red);
+    poison_lds<kPackThreads>(krow, sizeof krow);
+    poison_lds<kPackThreads>(pairs, sizeof pairs);
     const int n = L - t0;   // valid rows of the tile (may be <= 0 or > 128)
 
     float4 v[16];

@@ -104,6 +104,22 @@ const char* kvq_status_string(kvq_status s);
 int32_t kvq_last_hip_error(void);
 uint32_t kvq_layout_version(void);
 
+/* Test hook for the failure path, usable without a GPU. While hip_error is
+ * non-zero, every entry point that would call HIP runs its host checks as
+ * usual and then, in place of its first HIP call, returns KVQ_ERR_HIP with
+ * kvq_last_hip_error() == hip_error; it makes no HIP call and launches
+ * nothing. Argument errors still come first. 0 switches the hook off (the
+ * default). Per calling thread. The pages define no failure handling; this
+ * only exercises the library's own error reporting. */
+void kvq_debug_inject_hip_error(int32_t hip_error);
+
+/* Build variant bits (host-only). KVQ_BUILD_POISON_LDS: the debug build in
+ * which every kernel fills its LDS with all-ones bytes before first use, so a
+ * read of LDS that the kernel did not write first turns its output into
+ * NaN or wrong codes; it computes the same results as the normal build. */
+#define KVQ_BUILD_POISON_LDS 1u
+uint32_t kvq_build_flags(void);
+
 /* Checks a format; KVQ_OK if the library supports it. */
 kvq_status kvq_check_format(const kvq_format* fmt);
 

@@ -368,6 +368,73 @@ def test_pack_and_bf16_validation_without_gpu(L):
                                    ctypes.c_float(float("nan")), A, 0, 0, None, 0, None) == BADSHAPE
 
 
+HIP_ERR = 6
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"),
+                    reason="host-only: its fake device addresses must never meet a device")
+def test_injected_hip_failure_without_gpu(L):
+    """The KVQ_ERR_HIP path of every entry point that launches: with an error
+    code injected, each passes its host checks, then reports that code
+    instead of its first HIP call; argument errors still come first."""
+    A = 4096
+    c = kvq.Cache(A, A, A, A)
+    code = 719  # hipErrorLaunchFailure
+    f = kvq.make_format(2, "channel", "token", 8)
+    fp = kvq.make_format(2, "token", "token", 8, page_size=64)
+    big = 1 << 40
+    sf = ctypes.c_float(0.088)
+    calls = {
+        "pack": lambda: L.kv_quantize_pack(ctypes.byref(f), A, A, A, None, 0, 2, 300,
+                                           ctypes.byref(c), None),
+        "pack_paged": lambda: L.kv_quantize_pack(ctypes.byref(fp), A, A, A, A, 8, 2, 300,
+                                                 ctypes.byref(c), None),
+        "decode_one_split": lambda: _call_decode(L, f, cache=(A,) * 4, lens=A, out=A, q=A,
+                                                 max_len=4096, ns=1),
+        "decode_splits": lambda: _call_decode(L, f, cache=(A,) * 4, lens=A, out=A, q=A,
+                                              max_len=4096, ns=4, ws=A, wsb=big),
+        "decode_auto": lambda: _call_decode(L, f, cache=(A,) * 4, lens=A, out=A, q=A,
+                                            max_len=32768, ns=0, ws=A, wsb=big),
+        "decode_fp8": lambda: L.decode_attention_quant_fp8(ctypes.byref(f), A, ctypes.byref(c), A,
+                                                           None, 0, 2, 4096, sf, A, 1, 2, A, big,
+                                                           None),
+        "noalloc_splits": lambda: L.decode_attention_quant_noalloc(
+            ctypes.byref(f), A, ctypes.byref(c), A, None, 0, 2, 4096, sf, A, 0, 4, None),
+        "noalloc_one_split": lambda: L.decode_attention_quant_noalloc(
+            ctypes.byref(f), A, ctypes.byref(c), A, None, 0, 2, 4096, sf, A, 0, 1, None),
+        "bf16": lambda: L.decode_attention_bf16(ctypes.byref(f), A, A, A, A, None, 0, 2, 4096, sf,
+                                                A, 0, 2, A, big, None),
+        "append": lambda: L.kv_append(ctypes.byref(f), A, A, A, None, 0, 2, 4096,
+                                      ctypes.byref(c), A, A, None),
+        "window": lambda: L.decode_attention_quant_window(ctypes.byref(f), A, ctypes.byref(c), A,
+                                                          A, A, None, 0, 2, 4096, sf, A, 0, 2, A,
+                                                          big, None),
+        "stream_read": lambda: L.kvq_stream_read(A, 1 << 20, A, None),
+        "issue_probe": lambda: L.kvq_issue_probe(0, 10, 4, A, None),
+    }
+    try:
+        for i, (name, call) in enumerate(calls.items()):
+            kvq.kvq_debug_inject_hip_error(code + i)  # a new code per call: none is stale
+            assert call() == HIP_ERR, name
+            assert L.kvq_last_hip_error() == code + i, name
+        kvq.kvq_debug_inject_hip_error(code)
+        # argument errors are reported before the HIP step
+        assert _call_decode(L, f, q=None) == NULLP
+        assert L.kvq_stream_read(A, 24, A, None) == BADSHAPE
+        # calls with nothing to launch succeed without reaching it
+        assert L.kvq_stream_read(A, 0, A, None) == OK
+        assert _call_decode(L, f, cache=(A,) * 4, lens=A, out=A, q=A, B=0, ns=1) == OK
+        assert L.kv_quantize_pack(ctypes.byref(f), A, A, A, None, 0, 0, 128, ctypes.byref(c),
+                                  None) == OK
+        # the binding names the injected code
+        assert calls["stream_read"]() == HIP_ERR
+        msg = str(kvq.KvqError(HIP_ERR, "kvq_stream_read"))
+        assert "KVQ_ERR_HIP" in msg and str(code) in msg
+        assert L.kvq_status_string(HIP_ERR) == b"HIP launch failed"
+    finally:
+        kvq.kvq_debug_inject_hip_error(0)
+
+
 def test_calls_without_library_fail_loudly(monkeypatch, tmp_path):
     """The binding has no fallback: with the library missing, calls raise."""
     import importlib
