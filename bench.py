@@ -93,6 +93,11 @@ def measured_traffic(bits):
 
 
 HOST_ISSUE_US = []  # longest host gap between two issued calls of the last time_calls
+# per block of the last time_blocks: the slowest single call (event-timed) and
+# the longest host gap between two issued calls, both in us. A block that is
+# slow because the host stalled shows a gap near the lost time; one that is
+# slow on the GPU shows slow calls with short gaps.
+BLOCK_DETAIL = {}
 
 
 def time_calls(fn, steps, warmup, stream):
@@ -126,12 +131,16 @@ def time_blocks(fn, steps, warmup, stream, blocks=3):
     full benchmark run in four, one block of one format ran 2-3x slow (a state
     that cleared within a second and did not recur when the same sequence was
     rerun); the median keeps such a block from standing for the format."""
-    ts, gaps = [], []
+    ts, gaps, slowest = [], [], []
     for i in range(blocks):
-        _, total_ms = time_calls(fn, steps, warmup if i == 0 else 0, stream)
+        per, total_ms = time_calls(fn, steps, warmup if i == 0 else 0, stream)
         ts.append(total_ms * 1e3 / steps)
         gaps.append(HOST_ISSUE_US[0])
+        slowest.append(float(per.max()))
     HOST_ISSUE_US[:] = [max(gaps)]
+    BLOCK_DETAIL.clear()
+    BLOCK_DETAIL.update(max_call_us=[round(t, 1) for t in slowest],
+                        max_host_gap_us=[round(g, 1) for g in gaps])
     return float(np.median(ts)), [round(t, 2) for t in ts]
 
 
@@ -681,7 +690,7 @@ def main():
 
         us, blocks = time_blocks(callg, args.steps, args.warmup, stream)
         groups[name] = dict(us_per_call=round(us, 2), us_blocks=blocks,
-                            effective_bytes=eff, gbs=round(eff / (us * 1e-6) / 1e9, 1),
+                            blocks_detail=dict(BLOCK_DETAIL), effective_bytes=eff, gbs=round(eff / (us * 1e-6) / 1e9, 1),
                             pct_peak=round(100.0 * eff / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2))
         log(f"{name}: {us:.1f} us/call, {groups[name]['gbs']:.0f} GB/s effective "
             f"({groups[name]['pct_peak']:.1f}%)")
@@ -691,6 +700,7 @@ def main():
 
             us8, blocks8 = time_blocks(callg8, args.steps, args.warmup, stream)
             groups[name].update(fp8_us_per_call=round(us8, 2), fp8_us_blocks=blocks8,
+                                fp8_blocks_detail=dict(BLOCK_DETAIL),
                                 fp8_pct_peak=round(100.0 * eff / (us8 * 1e-6) / 1e9 / PEAK_HBM_GBS, 2))
             log(f"{name}, fp8 operands: {us8:.1f} us/call ({groups[name]['fp8_pct_peak']:.1f}%)")
     del inp["xcaches"]

@@ -177,26 +177,29 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
   int F = 0;  // P'' = P * s * 2^-F / w, running per wave
   float kseed = 0.f;  // the running output's start value (kSeedV), scaled along
 
-  for (int cb = tb; cb < te; cb += M::CHUNK) {
-    const int ce = min(cb + M::CHUNK, te);
-    const int ntok = ce - cb;
-
-    // ---- prologue: lane l takes TPL = 8 / NG consecutive tokens of this
-    // wave's blocks (128-token blocks wv, wv + 4, .. of the chunk), all NG
-    // channel groups of each: one contiguous 4 NG-byte (s, z) row per token
-    // and tensor. The lane's first token t0 is a multiple of TPL, so a
-    // token's code slot within its 4-token run is (t0 & 3) + u.
-    constexpr int TPL = 8 / NG;
+  // ---- (s, z) rows of a chunk: lane l takes TPL = 8 / NG consecutive tokens
+  // of this wave's blocks (128-token blocks wv, wv + 4, .. of the chunk), all
+  // NG channel groups of each: one contiguous 4 NG-byte (s, z) row per token
+  // and tensor. The lane's first token t0 is a multiple of TPL, so a token's
+  // code slot within its 4-token run is (t0 & 3) + u. Where the registers
+  // allow (G = 32), the next chunk's rows are loaded during this chunk's main
+  // loop, so the next prologue does not wait for them.
+  constexpr int TPL = 8 / NG;
+  constexpr bool PREFETCH = NG == 4;
+  typedef uint32_t row_t __attribute__((ext_vector_type(NG)));
+  auto lane_t0 = [&]() {  // from a laundered lane id: nothing of it stays live
     int pl = lane;
     asm volatile("" : "+v"(pl));
     const int tw = pl * TPL;  // index into the wave's tokens of the chunk
-    const int t0 = 128 * (wv + 4 * (tw >> 7)) + (tw & 127);
-    typedef uint32_t row_t __attribute__((ext_vector_type(NG)));
+    return 128 * (wv + 4 * (tw >> 7)) + (tw & 127);
+  };
+  auto load_rows = [&](int cbx, row_t* kz, row_t* vz) {
+    const int t0 = lane_t0();
+    const int ntok = min(cbx + M::CHUNK, te) - cbx;
     // the chunk's rows sit at a base shared by the wave plus a 32-bit lane offset
-    const long szb = (unit * a.padded_len + cb) * (long)(4 * NG);
+    const long szb = (unit * a.padded_len + cbx) * (long)(4 * NG);
     const unsigned char* krow = (const unsigned char*)a.k_sz + szb;
     const unsigned char* vrow = (const unsigned char*)a.v_sz + szb;
-    row_t kz[TPL], vz[TPL];
     if (ntok == M::CHUNK) {  // a whole chunk: no token past the end
 #pragma unroll
       for (int u = 0; u < TPL; ++u) {
@@ -214,6 +217,16 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
         }
       }
     }
+  };
+  row_t kz[TPL], vz[TPL];
+  if constexpr (PREFETCH) load_rows(tb, kz, vz);
+
+  for (int cb = tb; cb < te; cb += M::CHUNK) {
+    const int ce = min(cb + M::CHUNK, te);
+
+    // ---- prologue
+    if constexpr (!PREFETCH) load_rows(cb, kz, vz);
+    const int t0 = lane_t0();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     {
       // every scale of this wave's tokens < 2^Fs (scales of 0 count as 1)
@@ -252,8 +265,10 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
       }
       // slot weight of token t0 + u: 2^(BITS ((t0 & 3) + u) % SLOTS)); with
       // two tokens per lane (INT2) the lane's pair sits at slots 0, 1 or 2, 3
-      const float lw = (BITS == 2 && TPL == 2 && (t0 & 2)) ? 16.f : 1.f;
-      const float two_mF = ldexpf(1.f, -F) / lw;
+      // (powers of two: the divisions by lw are multiplications by 1 / lw)
+      const bool hi_pair = BITS == 2 && TPL == 2 && (t0 & 2);
+      const float lw = hi_pair ? 16.f : 1.f, inv_lw = hi_pair ? 0.0625f : 1.f;
+      const float two_mF = ldexpf(1.f, -F) * inv_lw;
       float cf[NG][TPL], rw[NG][TPL];
 #pragma unroll
       for (int u = 0; u < TPL; ++u) {
@@ -263,9 +278,11 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
         const bool mir = u & 1;
 #pragma unroll
         for (int j = 0; j < NG; ++j) {
+          // products of a binary16 value as fma with a zero addend: one
+          // mixed-precision instruction each (sigma > 0, so no signed zero)
           const float sg = f16lo(vz[u][j]), zv = f16hi(vz[u][j]);
-          cf[j][u] = sg * ((mir ? -1.f : 1.f) * (two_mF / wu));
-          const float rs = __builtin_amdgcn_rcpf(sg * ((1.f / wu) / lw));
+          cf[j][u] = fmaf(sg, (mir ? -1.f : 1.f) * (two_mF / wu), 0.f);
+          const float rs = __builtin_amdgcn_rcpf(fmaf(sg, (1.f / wu) * inv_lw, 0.f));
           rw[j][u] = fmaf(zv, mir ? -rs : rs, mir ? -(float)((1 << BITS) - 1) * wu * lw : 0.f);
         }
       }
@@ -287,7 +304,8 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
       for (int u = 0; u < TPL; ++u) {
         float2 kv[NG];
 #pragma unroll
-        for (int j = 0; j < NG; ++j) kv[j] = make_float2(f16lo(kz[u][j]) * ktok_sc, f16hi(kz[u][j]) * alpha);
+        for (int j = 0; j < NG; ++j)  // (a zero offset may lose its sign: it only ever is added)
+          kv[j] = make_float2(fmaf(f16lo(kz[u][j]), ktok_sc, 0.f), fmaf(f16hi(kz[u][j]), alpha, 0.f));
         float4* kd = (float4*)(lds + M::KB + M::kb_off(t0 + u));
 #pragma unroll
         for (int j2 = 0; j2 < NG; j2 += 2) kd[j2 / 2] = make_float4(kv[j2].x, kv[j2].y, kv[j2 + 1].x, kv[j2 + 1].y);
@@ -324,10 +342,17 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
 #pragma unroll
     for (int j = 0; j < NG; ++j) Qs[j] = red[16 + mhh * 4 + j];
 
+    row_t nkz[TPL], nvz[TPL];
+
     for (int jj = 0;; ++jj) {
       const int it = 2 * (wv + 4 * (jj >> 1)) + (jj & 1);
       const int t0 = cb + it * C::TIT;
       if (t0 >= ce) break;
+      // the next chunk's rows, issued with the first iteration's code loads:
+      // waited for one iteration later, not by this iteration's first product
+      if constexpr (PREFETCH) {
+        if (jj == 0 && cb + M::CHUNK < te) load_rows(cb + M::CHUNK, nkz, nvz);
+      }
       Codes nxt;
       const int t1 = t0 + ((jj & 1) ? 7 : 1) * C::TIT;
       if (t1 < te) load_codes(t1, nxt, koff, mg, mn_);
@@ -437,6 +462,13 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
         }
       }
       cur = nxt;
+    }
+    if constexpr (PREFETCH) {
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        kz[u] = nkz[u];
+        vz[u] = nvz[u];
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   }
