@@ -60,9 +60,11 @@ def parse():
                    help="skip the graph-replayed timings of the short calls")
     p.add_argument("--no-groups", action="store_true",
                    help="skip the token-wise G = 128 / 64 / 32 timings")
-    p.add_argument("--only", choices=["int2", "int4", "bf16", "pack", "probe"], default=None,
+    p.add_argument("--only", choices=["int2", "int4", "bf16", "pack", "probe", "groups"],
+                   default=None,
                    help="time one bit width, or only the bf16 decode, or only kv_quantize_pack, or "
-                        "only the matrix/vector issue probe (profiling runs)")
+                        "only the matrix/vector issue probe, or the INT2 headline and the other "
+                        "group layouts (profiling runs)")
     p.add_argument("--no-small", action="store_true",
                    help="skip the tiny / mid configurations (cache-resident and cold timings)")
     p.add_argument("--no-pack", action="store_true", help="skip the kv_quantize_pack timing")
@@ -601,10 +603,13 @@ def main():
               flush=True)
         return
     only_bf16 = args.only == "bf16"
-    widths = [2] if only_bf16 else ([int(args.only[-1])] if args.only else [2, 4])
+    if only_bf16 or args.only == "groups":
+        widths = [2]
+    else:
+        widths = [int(args.only[-1])] if args.only else [2, 4]
     need_bf16 = not args.no_bf16 and args.only in (None, "bf16")
     extra = []
-    if not args.no_groups and args.only is None:
+    if not args.no_groups and args.only in (None, "groups"):
         for bits in (2, 4):
             # the other fold pairing of the headline: K token-wise (acc-fold),
             # V channel-wise (acc-fold per 128-token group)
