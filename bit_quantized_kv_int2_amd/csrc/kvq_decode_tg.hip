@@ -349,7 +349,10 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
       const int t0 = cb + it * C::TIT;
       if (t0 >= ce) break;
       // the next chunk's rows, issued with the first iteration's code loads:
-      // waited for one iteration later, not by this iteration's first product
+      // waited for one iteration later, not by this iteration's first product.
+      // A next chunk exists only after a whole one, and in a whole chunk every
+      // wave has an iteration jj = 0, so the rows passed on are always loaded.
+      static_assert(M::CHUNK >= 4 * 2 * C::TIT, "every wave iterates in a whole chunk");
       if constexpr (PREFETCH) {
         if (jj == 0 && cb + M::CHUNK < te) load_rows(cb + M::CHUNK, nkz, nvz);
       }
