@@ -88,6 +88,35 @@ def test_headline_sampled(bits, k_axis, v_axis):
         assert np.array_equal(np.ascontiguousarray(g).view(np.uint8), np.ascontiguousarray(o).view(np.uint8))
 
 
+def test_headline_int2_every_unit():
+    """The INT2 headline (K channel-wise, V token-wise) as the benchmark times
+    it, every one of its 128 x 8 (sequence, KV head) units against the oracle:
+    rel-L2 and max-abs over the whole 128 x 32 x 128 output."""
+    import os
+    import bit_quantized_kv_int2_amd as kvq
+    w = synth.headline(2)
+    fmt = gpu_format(w)
+    cache = pack_rowwise(w, fmt)
+    out = _decode(w, fmt, cache).double().cpu().numpy()
+    fmt_o = oracle.fmt_of(w)
+    row = kvq.kvq_cache_sizes(fmt, 1, w.max_len)
+    host = [c.cpu().numpy() for c in cache]
+    threads = min(16, os.cpu_count() or 1)
+    q = w.q_bf16()
+    step = 32
+    for b0 in range(0, w.batch, step):  # 32 rows per oracle call, ~0.6 GB of host cache
+        shapes = oracle.cache_shapes(fmt_o, step, w.max_len)
+        hc = [x[b0 * n:(b0 + step) * n][:int(np.prod(sh)) * np.dtype(dt).itemsize].view(dt).reshape(sh)
+              for x, n, (dt, sh) in zip(host, row, shapes)]
+        ref = oracle.decode_attention(fmt_o, q[b0:b0 + step], hc, w.seq_lens[b0:b0 + step],
+                                      w.max_len, SCALE, threads=threads)
+        got = out[b0:b0 + step]
+        e2, ea = rel_l2(got, ref), max_abs(got, ref)
+        print(f"rows {b0}..{b0 + step - 1}: rel_l2={e2:.3e} max_abs={ea:.3e}", flush=True)
+        assert np.isfinite(got).all()
+        assert e2 <= REL_L2_TOL and ea <= MAX_ABS_TOL, (b0, e2, ea)
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 def test_headline_sampled_fp8(bits):
     """The fp8-operand q.K^T variant at the full headline size (its own bound:
