@@ -23,7 +23,9 @@ pytestmark = pytest.mark.gpu
                                                             (2, "token", "channel", False, 128),
                                                             (4, "channel", "channel", False, 128),
                                                             (2, "token", "token", True, 128),
-                                                            (4, "token", "token", False, 32)])
+                                                            (4, "token", "token", False, 32),
+                                                            (2, "token", "token", False, 64),
+                                                            (2, "token", "token", False, 32)])
 def test_append_then_window_decode(bits, k_axis, v_axis, paged, group):
     import torch
     import bit_quantized_kv_int2_amd as kvq
