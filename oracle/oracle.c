@@ -39,7 +39,8 @@
  *            token-wise:   contiguous [B][Hkv][Lp][D/G][2], paged [P][Hkv][64][D/G][2]
  *            channel-wise: contiguous [B][Hkv][Lp/G][D][2], paged [P][Hkv][D][2]
  *                          (paged: G = 128, a group's pair sits in the page
- *                          holding its first token; the other page's slot is unused).
+ *                          holding its first token; the other page's slot is unused;
+ *                          token-wise pairs of any G sit with their token).
  *
  * parity unpinned: none of the pages prints a worked numeric example, so the
  * end-to-end output is pinned only by the tests' closed forms, brute force
@@ -376,7 +377,12 @@ static int check_format(const orc_format* f) {
     if (f->head_dim % f->group) return -1;
   if (f->k_axis == ORC_CHANNEL_WISE || f->v_axis == ORC_CHANNEL_WISE)
     if (128 % f->group) return -1;
-  if (f->page_size != 0 && (f->page_size != 64 || f->group != 128)) return -1;
+  /* paged: 64-token pages; a channel-wise group (G tokens) spans a page pair,
+   * so G = 128 there, while token-wise pairs live with their token */
+  if (f->page_size != 0) {
+    if (f->page_size != 64) return -1;
+    if ((f->k_axis == ORC_CHANNEL_WISE || f->v_axis == ORC_CHANNEL_WISE) && f->group != 128) return -1;
+  }
   return 0;
 }
 

@@ -415,6 +415,32 @@ def test_paged_equals_contiguous(orc, bits):
     assert np.array_equal(oc, op)
 
 
+@pytest.mark.parametrize("bits,group", [(2, 32), (4, 64)])
+def test_paged_equals_contiguous_token_groups(orc, bits, group):
+    """Token-wise K and V with 32- or 64-channel groups: a token's pairs move
+    with its page, and the paged decode equals the contiguous one exactly."""
+    lens = [200, 64, 1, 333]
+    w = _small_workload(bits, "token", "token", lens, seed=23)
+    table, n_pages = synth.build_page_table(lens, 64, seed=10)
+    k, v = w.kv_all("k"), w.kv_all("v")
+    fc = orc.fmt_of(w, group=group)
+    w.page_size = 64
+    fp = orc.fmt_of(w, group=group)
+    cc = orc.quantize_pack(fc, k, v, lens)
+    cp = orc.quantize_pack(fp, k, v, lens, page_table=table, num_pages=n_pages)
+    for b, L in enumerate(lens):
+        for p in range((L + 63) // 64):
+            ph = table[b, p]
+            for i in range(4):  # codes, words, and both tensors' pairs: one block each
+                src = cc[i][b, :, p] if i < 2 else cc[i][b, :, 64 * p:64 * p + 64]
+                assert np.array_equal(cp[i][ph], src), (b, p, i)
+    q = w.q_bf16()
+    oc = orc.decode_attention(fc, q, cc, lens, w.max_len, 0.088)
+    op = orc.decode_attention(fp, q, cp, lens, w.max_len, 0.088, page_table=table)
+    assert np.array_equal(oc, op)
+    assert np.abs(oc).max() > 0
+
+
 def test_bf16_attention_vs_torch(orc):
     rng = np.random.default_rng(5)
     B, H, L, D = 2, 2, 150, 128
