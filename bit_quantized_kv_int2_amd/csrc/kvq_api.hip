@@ -99,11 +99,11 @@ kvq_status kvq_check_format(const kvq_format* f) {
   if (f->v_axis != KVQ_TOKEN_WISE && f->v_axis != KVQ_CHANNEL_WISE) return KVQ_ERR_BAD_FORMAT;
   if (f->head_dim != kHeadDim) return KVQ_ERR_BAD_FORMAT;
   // 128 everywhere; 32 or 64 channels per group when both axes are token-wise
-  // (the one group size then counts channels for K and V) on a contiguous cache
+  // (the one group size then counts channels for K and V; a token's pairs
+  // sit with the token, in its page for a paged cache)
   if (f->group != kGroup) {
     if (f->group != 32 && f->group != 64) return KVQ_ERR_BAD_FORMAT;
-    if (f->k_axis != KVQ_TOKEN_WISE || f->v_axis != KVQ_TOKEN_WISE || f->page_size != 0)
-      return KVQ_ERR_BAD_FORMAT;
+    if (f->k_axis != KVQ_TOKEN_WISE || f->v_axis != KVQ_TOKEN_WISE) return KVQ_ERR_BAD_FORMAT;
   }
   if (f->num_kv_heads < 1 || f->num_kv_heads > 65535) return KVQ_ERR_BAD_FORMAT;
   if (f->num_q_heads != kGqa * f->num_kv_heads) return KVQ_ERR_BAD_FORMAT;

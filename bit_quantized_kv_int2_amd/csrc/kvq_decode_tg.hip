@@ -50,7 +50,7 @@ struct TgLds {
   __device__ static inline int kb_off(int t) { return t * NG * 8 + 16 * (t >> 4); }
 };
 
-template <int BITS, int NG>
+template <int BITS, int NG, bool PAGED>
 __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_tg_kernel(DecodeArgs a) {
   using C = Cfg<BITS>;
   using M = TgLds<BITS, NG>;
@@ -94,9 +94,12 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
   }
   const float alpha = a.scale_log2;
 
-  // ---- cache addressing (contiguous caches) -----------------------------
+  // ---- cache addressing ---------------------------------------------------
   const long unit = (long)b * H + h;
-  auto chunk_of = [&](int t) -> long { return unit * (a.padded_len / kPage) + t / kPage; };
+  auto chunk_of = [&](int t) -> long {  // 64-token block of token t
+    if (!PAGED) return unit * (a.padded_len / kPage) + t / kPage;
+    return (long)a.page_table[(long)b * a.max_pages + t / kPage] * H + h;
+  };
 
   const int n = lane & 15, g = lane >> 4, hh = n & 3;
   const int ri = lane & 15;
@@ -113,8 +116,7 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
     uint32_t v[NV];
   };
   auto lane_koff = [](int lg, int lr) { return (uint32_t)(16 * (16 * lg + lr)); };
-  auto load_codes = [&](int t0, Codes& cd, uint32_t koff, int lg, int lr) {
-    const long ch = chunk_of(t0);
+  auto load_block = [&](long ch, Codes& cd, uint32_t koff, int lg, int lr) {
     const unsigned char* kb = a.k_codes + ch * (kPage * C::KROW) + koff;
 #pragma unroll
     for (int e = 0; e < C::KDW / 4; ++e) cd.k[e] = __builtin_nontemporal_load((const u4*)(kb + 1024 * e));
@@ -122,12 +124,24 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
 #pragma unroll
     for (int e = 0; e < NV; ++e) cd.v[e] = vb[512 * (e >> 3) + 8 * (e & 7)];
   };
+  // Paged caches: the physical page of a wave's next iteration is read one
+  // iteration before its codes (as in the G = 128 kernel), so the code loads
+  // never wait on a page-table read. A wave's next iteration is 64 tokens on
+  // within its 128-token block, else 448 tokens on.
+  auto next_it = [](int t) { return t + (((t >> 6) & 1) ? 7 : 1) * C::TIT; };
+  auto page_at = [&](int t) -> int {  // (through a vector register: see the G = 128 kernel)
+    int z = 0;
+    asm volatile("" : "+v"(z));
+    return a.page_table[(long)b * a.max_pages + t / kPage + z];
+  };
 
   // wave wv owns the 128-token groups wv, wv + 4, ... (iterations 2G, 2G + 1)
   Codes cur;
+  int pg_next = 0;  // paged: physical page of this wave's next iteration
   {
     const int t0 = tb + 2 * wv * C::TIT;
-    if (t0 < te) load_codes(t0, cur, lane_koff(g, ri), g, ri);
+    if (t0 < te) load_block(chunk_of(t0), cur, lane_koff(g, ri), g, ri);
+    if (PAGED && next_it(t0) < te) pg_next = page_at(next_it(t0));
   }
 
   // ---- query: once per split -------------------------------------------------
@@ -185,7 +199,7 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
   // allow (G = 32), the next chunk's rows are loaded during this chunk's main
   // loop, so the next prologue does not wait for them.
   constexpr int TPL = 8 / NG;
-  constexpr bool PREFETCH = NG == 4;
+  constexpr bool PREFETCH = NG == 4 && !PAGED;
   typedef uint32_t row_t __attribute__((ext_vector_type(NG)));
   auto lane_t0 = [&]() {  // from a laundered lane id: nothing of it stays live
     int pl = lane;
@@ -196,15 +210,24 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
   auto load_rows = [&](int cbx, row_t* kz, row_t* vz) {
     const int t0 = lane_t0();
     const int ntok = min(cbx + M::CHUNK, te) - cbx;
-    // the chunk's rows sit at a base shared by the wave plus a 32-bit lane offset
-    const long szb = (unit * a.padded_len + cbx) * (long)(4 * NG);
+    // the chunk's rows sit at a base shared by the wave plus a 32-bit lane
+    // offset (token ta of that base). In a paged cache a lane's TPL tokens lie
+    // in one page: the base is that page's block (the page of the chunk's
+    // last token for a lane wholly past the end, whose loads are masked), so
+    // every page-table read is of a token inside the sequence.
+    long szb = (unit * a.padded_len + cbx) * (long)(4 * NG);
+    int ta = t0;
+    if (PAGED) {
+      szb = (chunk_of(cbx + min(t0, ntok - 1)) * kPage) * (long)(4 * NG);
+      ta = t0 % kPage;  // (chunks start at multiples of 64 tokens)
+    }
     const unsigned char* krow = (const unsigned char*)a.k_sz + szb;
     const unsigned char* vrow = (const unsigned char*)a.v_sz + szb;
     if (ntok == M::CHUNK) {  // a whole chunk: no token past the end
 #pragma unroll
       for (int u = 0; u < TPL; ++u) {
-        kz[u] = *(const row_t*)(krow + (uint32_t)(4 * NG * (t0 + u)));
-        vz[u] = *(const row_t*)(vrow + (uint32_t)(4 * NG * (t0 + u)));
+        kz[u] = *(const row_t*)(krow + (uint32_t)(4 * NG * (ta + u)));
+        vz[u] = *(const row_t*)(vrow + (uint32_t)(4 * NG * (ta + u)));
       }
     } else {  // tokens past the end read as (0, 0)
 #pragma unroll
@@ -212,8 +235,8 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
         kz[u] = row_t(0u);
         vz[u] = row_t(0u);
         if (t0 + u < ntok) {
-          kz[u] = *(const row_t*)(krow + (uint32_t)(4 * NG * (t0 + u)));
-          vz[u] = *(const row_t*)(vrow + (uint32_t)(4 * NG * (t0 + u)));
+          kz[u] = *(const row_t*)(krow + (uint32_t)(4 * NG * (ta + u)));
+          vz[u] = *(const row_t*)(vrow + (uint32_t)(4 * NG * (ta + u)));
         }
       }
     }
@@ -357,8 +380,15 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
         if (jj == 0 && cb + M::CHUNK < te) load_rows(cb + M::CHUNK, nkz, nvz);
       }
       Codes nxt;
-      const int t1 = t0 + ((jj & 1) ? 7 : 1) * C::TIT;
-      if (t1 < te) load_codes(t1, nxt, koff, mg, mn_);
+      const int t1 = t0 + ((jj & 1) ? 7 : 1) * C::TIT;  // this wave's next iteration
+      if (PAGED) {
+        if (t1 < te) {
+          load_block((long)pg_next * H + h, nxt, koff, mg, mn_);
+          if (next_it(t1) < te) pg_next = page_at(next_it(t1));
+        }
+      } else if (t1 < te) {
+        load_block(chunk_of(t1), nxt, koff, mg, mn_);
+      }
       const int rel = t0 - cb;
 
       // QK^T: k-step s belongs to channel group s * NG / 16; consecutive
@@ -548,7 +578,8 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
 template <int BITS, int NG>
 hipError_t launch_tg(const DecodeArgs& a, hipStream_t s) {
   dim3 grid((unsigned)(a.dev_plan ? a.plan_items : decode_grid_blocks((long)a.batch * a.num_kv_heads, a.num_splits)));
-  decode_tg_kernel<BITS, NG><<<grid, kThreads, 0, s>>>(a);
+  if (a.page_table) decode_tg_kernel<BITS, NG, true><<<grid, kThreads, 0, s>>>(a);
+  else decode_tg_kernel<BITS, NG, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -83,8 +83,8 @@ typedef struct {
   int32_t bits;         /* 2 or 4 */
   int32_t k_axis;       /* kvq_axis of K's groups */
   int32_t v_axis;       /* kvq_axis of V's groups */
-  int32_t group;        /* 128; or 32 / 64 channels per group when K and V are both
-                           token-wise on a contiguous cache (page_size 0) */
+  int32_t group;        /* 128; or 32 / 64 channels per group when K and V are
+                           both token-wise (contiguous or paged) */
   int32_t head_dim;     /* 128 */
   int32_t num_kv_heads; /* >= 1 */
   int32_t num_q_heads;  /* 4 * num_kv_heads (query head hq reads KV head hq / 4) */

@@ -91,16 +91,22 @@ def test_cache_sizes(L):
 
 
 def test_small_token_wise_groups(L):
-    # 32 or 64 channels per group only when K and V are both token-wise, contiguous
+    # 32 or 64 channels per group only when K and V are both token-wise
+    # (contiguous or paged: a token's pairs sit in its page)
     for gsz in (32, 64):
         assert kvq.kvq_check_format(kvq.make_format(2, "token", "token", 2, group=gsz)) == OK
         assert kvq.kvq_check_format(kvq.make_format(4, "channel", "token", 2, group=gsz)) == BADFMT
         assert kvq.kvq_check_format(kvq.make_format(4, "token", "channel", 2, group=gsz)) == BADFMT
-        assert kvq.kvq_check_format(kvq.make_format(2, "token", "token", 2, group=gsz,
+        fp = kvq.make_format(2, "token", "token", 2, group=gsz, page_size=64)
+        assert kvq.kvq_check_format(fp) == OK
+        assert kvq.kvq_check_format(kvq.make_format(2, "token", "channel", 2, group=gsz,
                                                     page_size=64)) == BADFMT
         kc, vc, ks, vs = kvq.kvq_cache_sizes(kvq.make_format(4, "token", "token", 2, group=gsz), 3, 1000)
         assert kc == vc == 3 * 2 * 1024 * 64
         assert ks == vs == 3 * 2 * 1024 * (128 // gsz) * 4
+        kc, vc, ks, vs = kvq.kvq_cache_sizes(fp, 0, 0, 7)  # 7 pages of 64 tokens x 2 heads
+        assert kc == vc == 7 * 2 * 64 * 32
+        assert ks == vs == 7 * 2 * 64 * (128 // gsz) * 4
     for bad in (16, 96, 256):
         assert kvq.kvq_check_format(kvq.make_format(2, "token", "token", 2, group=bad)) == BADFMT
 

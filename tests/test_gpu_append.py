@@ -24,7 +24,7 @@ pytestmark = pytest.mark.gpu
                                                             (4, "channel", "channel", False, 128),
                                                             (2, "token", "token", True, 128),
                                                             (4, "token", "token", False, 32),
-                                                            (2, "token", "token", False, 64),
+                                                            (2, "token", "token", True, 64),
                                                             (2, "token", "token", False, 32)])
 def test_append_then_window_decode(bits, k_axis, v_axis, paged, group):
     import torch

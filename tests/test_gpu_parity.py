@@ -110,7 +110,8 @@ def _tie_values(rng, shape, z, s, qmax, G):
 @pytest.mark.parametrize("bits,k_axis,v_axis,group,page", [
     (2, "channel", "token", 128, 0), (4, "token", "channel", 128, 0),
     (2, "token", "token", 32, 0), (4, "token", "token", 64, 0),
-    (2, "channel", "channel", 128, 64), (4, "channel", "token", 128, 64)])
+    (2, "channel", "channel", 128, 64), (4, "channel", "token", 128, 64),
+    (2, "token", "token", 64, 64)])
 def test_pack_exact_ties_and_signed_zeros(bits, k_axis, v_axis, group, page):
     """Values on and one ulp beside the rounding ties of their group's grid,
     and groups holding zeros of both signs, pack byte for byte as the oracle
@@ -421,15 +422,25 @@ def test_multi_chunk_splits(bits, k_axis, v_axis):
         assert e2 <= REL_L2_TOL and ea <= MAX_ABS_TOL, (ns, e2, ea)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
-def test_paged_equals_contiguous(bits):
+@pytest.mark.parametrize("bits,axes,group", [(2, ("channel", "token"), 128),
+                                              (4, ("channel", "token"), 128),
+                                              (2, ("token", "token"), 32),
+                                              (2, ("token", "token"), 64),
+                                              (4, ("token", "token"), 32),
+                                              (4, ("token", "token"), 64)])
+def test_paged_equals_contiguous(bits, axes, group):
+    """Same values packed into a contiguous cache and into scattered 64-token
+    pages: the paged pack matches the oracle byte for byte, and the decode
+    output is bit-identical (only addresses differ). With 32- or 64-channel
+    groups the 3000-token sequence spans several chunks of the per-group kernel."""
     lens = [3000, 64, 1, 700, 129]
-    w = synth.Workload("paged", len(lens), 2, 8, 128, lens, bits, "channel", "token", seed=61,
-                       outliers=True)
+    extra = {} if group == 128 else {"group": group}
+    w = synth.Workload("paged", len(lens), 2, 8, 128, lens, bits, *axes, seed=61,
+                       outliers=True, extra=extra)
     inp_c = Inputs(w)
     run_c = GpuRun(inp_c)
-    w_p = synth.Workload("paged", len(lens), 2, 8, 128, lens, bits, "channel", "token", seed=61,
-                         outliers=True, page_size=64)
+    w_p = synth.Workload("paged", len(lens), 2, 8, 128, lens, bits, *axes, seed=61,
+                         outliers=True, page_size=64, extra=extra)
     inp_p = Inputs(w_p)
     run_p = GpuRun(inp_p)
     ok, msg = cache_bytes_equal(run_p.cache_host(), oracle_pack(inp_p))

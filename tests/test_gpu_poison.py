@@ -45,6 +45,10 @@ def _quant_cases():
         for g in (32, 64):
             yield synth.Workload(f"tg{bits}_{g}", 3, 2, 8, 128, lens, bits, "token", "token",
                                  seed=104, outliers=True, extra={"group": g})
+    yield synth.Workload("tg_paged2_32", 3, 2, 8, 128, lens, 2, "token", "token", seed=107,
+                         page_size=64, extra={"group": 32})
+    yield synth.Workload("tg_paged4_64", 3, 2, 8, 128, lens, 4, "token", "token", seed=108,
+                         page_size=64, extra={"group": 64})
 
 
 def _run_everything():
