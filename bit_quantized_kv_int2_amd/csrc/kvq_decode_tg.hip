@@ -199,7 +199,7 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
   // allow (G = 32), the next chunk's rows are loaded during this chunk's main
   // loop, so the next prologue does not wait for them.
   constexpr int TPL = 8 / NG;
-  constexpr bool PREFETCH = NG == 4 && !PAGED;
+  constexpr bool PREFETCH = NG == 4;
   typedef uint32_t row_t __attribute__((ext_vector_type(NG)));
   auto lane_t0 = [&]() {  // from a laundered lane id: nothing of it stays live
     int pl = lane;
