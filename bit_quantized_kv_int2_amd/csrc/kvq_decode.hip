@@ -693,12 +693,17 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
           // bytes of half g >> 1 of lane groups 2 (g & 1) and 2 (g & 1) + 1.
           // So column (head, q) takes 16 bytes of its q'' row (offset
           // 16 (mg & 1) in each 32-channel run) into half q >> 1 when
-          // mg >> 1 == q & 1, and zeros everywhere else. Zero reads go to the
-          // bank group next to the rows' (odd or even 16-byte slot).
+          // mg >> 1 == q & 1, and zeros everywhere else. One read of the wave
+          // then fetches 8 distinct live 16-byte chunks, on 8 consecutive
+          // 16-byte bank quads (of the 256-byte bank period) starting at the
+          // group's row base, and 2 zero chunks. The zero chunks are placed on
+          // two of the other 8 quads: a 128-bit read is conflict-free only
+          // when the wave's distinct chunks fall on different quads.
           const bool live = (mg >> 1) == (mnq & 1);
-          const unsigned char* qrow = lds + M::QB + (KAX == KVQ_CHANNEL_WISE ? gi : 0) * M::GROUP_STRIDE +
-                                      mhh * M::HEAD_STRIDE + 16 * (mg & 1);
-          const unsigned char* zrow = lds + M::QZ + 112 * (mg & 1);
+          const int qbase = M::QB + (KAX == KVQ_CHANNEL_WISE ? gi : 0) * M::GROUP_STRIDE;
+          const unsigned char* qrow = lds + qbase + mhh * M::HEAD_STRIDE + 16 * (mg & 1);
+          const int zq = (qbase / 16 + 8 + (mg & 1) - M::QZ / 16) & 15;  // zero row quad offset
+          const unsigned char* zrow = lds + M::QZ + 16 * zq;
           const u4* b0 = (const u4*)(live && mnq < 2 ? qrow : zrow);
           const u4* b1 = (const u4*)(live && mnq >= 2 ? qrow : zrow);
 #pragma unroll

@@ -523,8 +523,12 @@ struct Lds {
   static constexpr int QS = 0;                                   // float [4][128] / binary16 q
   static constexpr int QB = QS + 4 * 128 * 4;                    // u4 [groups][4 heads][18] (16 used)
   static constexpr int QB_BYTES = (KAX == KVQ_CHANNEL_WISE ? kMaxGroups : 1) * GROUP_STRIDE;
-  static constexpr int QZ = QB + QB_BYTES + 16;                  // 384 B of zeros (off-diagonal B)
-  static constexpr int QZ_BYTES = 384;
+  static constexpr int QZ = QB + QB_BYTES + 16;                  // zeros (off-diagonal B)
+  // 896 B: the fp8/fp4 INT2 q.K^T reads its zero rows at up to 240 B in (to
+  // keep them off the live rows' banks) and 240 B on; 512 B more than the 384
+  // the other paths need keeps every later region on the same banks and the
+  // 512-byte offset units of paired LDS reads
+  static constexpr int QZ_BYTES = 896;
   static constexpr int KB = QZ + QZ_BYTES + 112;                 // chan-K (scale, bias) [groups][4] / tok-K (s',z'') [tokens]
   static constexpr int KB_BYTES = KAX == KVQ_CHANNEL_WISE ? kMaxGroups * 4 * 8 : kChunkTokens * 8;
   static constexpr int VA = KB + KB_BYTES;                       // tok-V coef [tokens] / chan-V (sigma,rho) [groups][128]
