@@ -263,6 +263,12 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   // fp16 token-wise V: the running output starts from kSeedV (set when the
   // first scores arrive), scaled along with it; kseed is its current value
   constexpr bool SEED = !PV8 && VAX == KVQ_TOKEN_WISE;
+  // INT2 fp16 token-wise V: P.V on the 2:4-sparse 16x16x64 product, with P''
+  // as its compressed A operand and the V codes as its dense B. Accumulator
+  // tile c of lane (g, n) then holds head g, channel 8 n + c, in rows 0 and 1
+  // (two replicas that split the tokens; rows 2 and 3 repeat them and are
+  // never read)
+  constexpr bool SPV = SEED && BITS == 2;
   float kseed = 0.f;
   // P'' = P * coef * 2^-F with max P'' < 2^14. Token-wise V: F follows the
   // largest scale this wave has seen and only grows (the accumulators are
@@ -615,6 +621,19 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         const int sg = BITS == 2 ? 2 * k + m2 : 2 * (mg & 1) + m2;
         src[k][m2] = 4 * (mhh + 4 * sq + 16 * sg);  // byte address for ds_bpermute
       }
+    // sparse P.V: A row mn_ = 4 x + r holds head x, replica r & 1. Its
+    // compressed dword p pairs with B group m = 2 (g >> 1) + (p & 1) of word
+    // row rw = 2 (g & 1) + (p >> 1), and the index picks that group's VGPR of
+    // unpack half r & 1 (positions 0, 1 or 2, 3): the P'' pair of tokens
+    // 16 rw + 4 (r & 1) + m and + 8, which score lane (2 (r & 1) + (g >> 1),
+    // x + 4 rw) holds in pk[p & 1]
+    int sadr[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int rw = 2 * (mg & 1) + (p >> 1);
+      sadr[p] = 4 * ((mnq + 4 * rw) + 16 * (2 * (mhh & 1) + (mg >> 1)));
+    }
+    const int sidx = (mhh & 1) ? (int)0xEEEEEEEEu : 0x44444444;
     // fp8 P.V: this lane's A row r = mn_ holds head r & 3 for the channel half
     // (r >> 2) & 1, part hi (r < 8) or lo; its 16 probability bytes come from
     // four score lanes (ds_bpermute byte addresses asrc), two per dword
@@ -777,10 +796,12 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         if (SEED) {
           // the first scores of this wave (sc = 0) plant the seed
           const float k0 = m_run == -INFINITY ? kSeedV : 0.f;
+          // sparse P.V: lane (g, n)'s tiles hold head g, whose scale score lane g has
+          const float so = SPV ? __shfl(sc, mg) : sc, ko = SPV ? __shfl(k0, mg) : k0;
 #pragma unroll
           for (int c = 0; c < 8; ++c)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) O[c][j] = fmaf(O[c][j], sc, k0);
+            for (int j = 0; j < 4; ++j) O[c][j] = fmaf(O[c][j], so, ko);
           kseed = fmaf(kseed, sc, k0);
         } else {
 #pragma unroll
@@ -893,16 +914,30 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         // per iteration and take switching power off the matrix unit, whose
         // clock this loop follows (measured 2 % faster, results unchanged)
         u4 bp[2];
+        if (!SPV) {
 #pragma unroll
-        for (int k = 0; k < 2; ++k)
+          for (int k = 0; k < 2; ++k)
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute(src[k][m >> 1], (int)pk[m & 1]);
-            bp[k][m] = mn_ < 4 ? v : 0u;
-          }
+            for (int m = 0; m < 4; ++m) {
+              const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute(src[k][m >> 1], (int)pk[m & 1]);
+              bp[k][m] = mn_ < 4 ? v : 0u;
+            }
+        }
 
-        // PV: 8 channel tiles, 2 k-steps of 32 tokens
-        if (VAX == KVQ_TOKEN_WISE) {
+        if (SPV) {
+          // PV: 8 sparse products of 64 tokens; B group m = (VGPR m of unpack
+          // half 0, VGPR m of half 1) of the lane's word, A from 4 permutes
+          u4 ap;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) ap[p] = (uint32_t)__builtin_amdgcn_ds_bpermute(sadr[p], (int)pk[p & 1]);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const uint32_t w = cur.v[c >> 2][c & 3];
+            const u4 h0 = unpack2v(w, 0), h1 = unpack2v(w, 1);
+            O[c] = smfmac(ap, u8v{h0[0], h1[0], h0[1], h1[1], h0[2], h1[2], h0[3], h1[3]}, O[c], sidx);
+          }
+        } else if (VAX == KVQ_TOKEN_WISE) {
+          // PV: 8 channel tiles, 2 k-steps of 32 tokens
 #pragma unroll
           for (int k = 0; k < 2; ++k) {
 #pragma unroll
@@ -1003,11 +1038,18 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     const float off = head_sum(X[0]);  // head n & 3's offset sum (every lane of the head)
     const float s24 = ldexpf(1.f, F + 24), sF = ldexpf(1.f, F);
     // (O - kseed) 2^(F + 24) + off 2^F
-    const float offk = fmaf(-kseed, s24, off * sF);
+    if (SPV) {
+      // head g's two replica rows, each started from the seed
+      const float offk = __shfl(fmaf(-2.f * kseed, s24, off * sF), g);
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+      for (int c = 0; c < 8; ++c) O[c][0] = fmaf(O[c][0] + O[c][1], s24, offk);
+    } else {
+      const float offk = fmaf(-kseed, s24, off * sF);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) O[c][j] = fmaf(O[c][j], s24, offk);
+      for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) O[c][j] = fmaf(O[c][j], s24, offk);
+    }
     lw = lsum;
   } else {
     const float s24 = ldexpf(1.f, F + 24);
@@ -1039,6 +1081,12 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
 #pragma unroll
         for (int c = 0; c < 4; ++c) mo[(wv * 4 + x) * kHeadDim + 8 * n + 2 * c + g] = O[c][x] * fx[x];
     }
+    if (n < 4 && g == 0) ml[(wv * 4 + n) * 2 + 1] = lw * f;
+  } else if (SPV) {
+    const float fo = __shfl(f, g);  // head g's factor
+    float* dst = mo + (wv * 4 + g) * kHeadDim + 8 * n;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) dst[c] = O[c][0] * fo;
     if (n < 4 && g == 0) ml[(wv * 4 + n) * 2 + 1] = lw * f;
   } else if (n < 4) {
     float* dst = mo + (wv * 4 + n) * kHeadDim + 32 * g;

@@ -192,6 +192,19 @@ __device__ inline h8 as_h8(u4 v) { return __builtin_bit_cast(h8, v); }
 __device__ inline f4 mfma(u4 a, u4 b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(a), as_h8(b), c, 0, 0, 0);
 }
+// 2:4-sparse 16x16x64 fp16 product. A dword p of a lane holds the two nonzero
+// values of its p-th group of four k, low half first, at the positions that
+// index bits 4p..4p+1 and 4p+2..4p+3 name. A lane groups 0 and 2 meet
+// elements 0-7 and 8-15 of B lane groups 0 (pairs 0, 1) and 1 (pairs 2, 3);
+// A lane groups 1 and 3 likewise meet B lane groups 2 and 3. A rows and C are
+// laid out as in the dense product (measured on the device, one nonzero A
+// element at a time). It issues in about the time of one dense 16x16x32
+// product: twice the multiply-adds per issue slot.
+typedef _Float16 h16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u8v __attribute__((ext_vector_type(8)));
+__device__ inline f4 smfmac(u4 a, u8v b, f4 c, int idx) {
+  return __builtin_amdgcn_smfmac_f32_16x16x64_f16(as_h8(a), __builtin_bit_cast(h16, b), c, idx, 0, 0);
+}
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 typedef float f2 __attribute__((ext_vector_type(2)));
