@@ -190,6 +190,11 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
   float lsum = 0.f;
   int F = 0;  // P'' = P * s * 2^-F / w, running per wave
   float kseed = 0.f;  // the running output's start value (kSeedV), scaled along
+  // INT2: P.V on the 2:4-sparse 16x16x64 product (P'' its compressed A, the
+  // V codes its dense B); tile c of lane (g, n) then holds head g, channel
+  // 16 c + n, in rows 0 and 1 (two replicas that split the tokens; rows 2 and
+  // 3 repeat them and are never read)
+  constexpr bool SPV = BITS == 2;
 
   // ---- (s, z) rows of a chunk: lane l takes TPL = 8 / NG consecutive tokens
   // of this wave's blocks (128-token blocks wv, wv + 4, .. of the chunk), all
@@ -356,6 +361,18 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
         const int sg = BITS == 2 ? 2 * k + m2 : 2 * (mg & 1) + m2;
         src[k][m2] = 4 * (mhh + 4 * sq + 16 * sg);
       }
+    // sparse P.V: A row mn_ = 4 x + r holds head x, replica r & 1; its
+    // compressed dword p pairs with B group m = 2 (g >> 1) + (p & 1) of word
+    // row rw = 2 (g & 1) + (p >> 1), where the index picks the VGPR of unpack
+    // half r & 1: the P'' pair of tokens 16 rw + 4 (r & 1) + m and + 8, held
+    // by score lane (2 (r & 1) + (g >> 1), x + 4 rw) in pk[p & 1]
+    int sadr[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int rw = 2 * (mg & 1) + (p >> 1);
+      sadr[p] = 4 * ((mnq + 4 * rw) + 16 * (2 * (mhh & 1) + (mg >> 1)));
+    }
+    const int sidx = (mhh & 1) ? (int)0xEEEEEEEEu : 0x44444444;
     // byte offsets of the lane's coefficient pairs within an iteration
     // (iterations start at multiples of 64 tokens: pair rel / 2 + r sits at
     // 4 rel + the offset of pair r, r < 32)
@@ -442,10 +459,12 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
         const float sc = exp2_fast(m_run - mn);
         // the first scores of this wave (sc = 0) plant the seed
         const float k0 = m_run == -INFINITY ? kSeedV : 0.f;
+        // sparse P.V: lane (g, n)'s tiles hold head g, whose scale score lane g has
+        const float so = SPV ? __shfl(sc, mg) : sc, ko = SPV ? __shfl(k0, mg) : k0;
 #pragma unroll
         for (int c = 0; c < 8; ++c)
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) O[c][q4] = fmaf(O[c][q4], sc, k0);
+          for (int q4 = 0; q4 < 4; ++q4) O[c][q4] = fmaf(O[c][q4], so, ko);
 #pragma unroll
         for (int j = 0; j < NG; ++j) X[j] *= sc;
         kseed = fmaf(kseed, sc, k0);
@@ -476,6 +495,21 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
           ox = fmaf(f16lo(pk[1]), r0.y, ox);  // tk0 + 1
           ox = fmaf(f16hi(pk[1]), r1.y, ox);  // tk0 + D2 + 1
           X[j] = ox;
+        }
+        if (SPV) {
+          // 4 permutes, then one sparse product of 64 tokens per tile; B group
+          // m = (VGPR m of unpack half 0, VGPR m of half 1) of the lane's word
+          u4 ap;
+#pragma unroll
+          for (int p = 0; p < 4; ++p) ap[p] = (uint32_t)__builtin_amdgcn_ds_bpermute(sadr[p], (int)pk[p & 1]);
+#pragma unroll
+          for (int ct = 0; ct < TPG; ++ct) {
+            const int c = j * TPG + ct;
+            const uint32_t w = cur.v[c];
+            const u4 h0 = unpack2v(w, 0), h1 = unpack2v(w, 1);
+            O[c] = smfmac(ap, u8v{h0[0], h1[0], h0[1], h1[1], h0[2], h1[2], h0[3], h1[3]}, O[c], sidx);
+          }
+          continue;
         }
         u4 bp[2];
 #pragma unroll
@@ -513,6 +547,16 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
 #pragma unroll
     for (int j = 0; j < NG; ++j) {
       const float off = head_sum(X[j]);  // head n & 3's offset sum of group j
+      if (SPV) {
+        // head g's two replica rows, each started from the seed
+        const float offk = __shfl(fmaf(-2.f * kseed, s24, off * sF), g);
+#pragma unroll
+        for (int ct = 0; ct < TPG; ++ct) {
+          f4& o = O[j * TPG + ct];
+          o[0] = fmaf(o[0] + o[1], s24, offk);
+        }
+        continue;
+      }
       const float offk = fmaf(-kseed, s24, off * sF);    // (O - kseed) 2^(F + 24) + off 2^F
 #pragma unroll
       for (int ct = 0; ct < TPG; ++ct)
@@ -532,7 +576,13 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
   for (int w = 0; w < kWaves; ++w) mall = fmaxf(mall, ml[(w * 4 + hh) * 2]);
   const float f = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - mall);
   __syncthreads();
-  if (n < 4) {
+  if (SPV) {
+    const float fo = __shfl(f, g);  // head g's factor
+    float* dst = mo + (wv * 4 + g) * kHeadDim + n;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) dst[16 * c] = O[c][0] * fo;
+    if (n < 4 && g == 0) ml[(wv * 4 + n) * 2 + 1] = lsum * f;
+  } else if (n < 4) {
     // lane (n, g) holds rows 4g .. 4g + 3 of every tile: channels 16c + 4g + q4
     float* dst = mo + (wv * 4 + n) * kHeadDim + 4 * g;
 #pragma unroll
