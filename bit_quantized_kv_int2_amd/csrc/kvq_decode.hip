@@ -623,15 +623,18 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       }
     // sparse P.V: A row mn_ = 4 x + r holds head x, replica r & 1. Its
     // compressed dword p pairs with B group m = 2 (g >> 1) + (p & 1) of word
-    // row rw = 2 (g & 1) + (p >> 1), and the index picks that group's VGPR of
-    // unpack half r & 1 (positions 0, 1 or 2, 3): the P'' pair of tokens
-    // 16 rw + 4 (r & 1) + m and + 8, which score lane (2 (r & 1) + (g >> 1),
-    // x + 4 rw) holds in pk[p & 1]
+    // row rw = 2 (g & 1) + (p >> 1): (VGPR m of unpack half 0, VGPR m ^ 2 of
+    // half 1), of which the index picks one (positions 0, 1 or 2, 3), replica
+    // r & 1 the VGPR mr = m ^ 2 (r & 1) of half r & 1. That is the P'' pair
+    // of tokens 16 rw + 4 (r & 1) + mr and + 8, which score lane
+    // (2 (r & 1) + (mr >> 1), x + 4 rw) holds in pk[p & 1] (mr and m share
+    // their parity). The two replicas of a 32-lane half then read source lanes
+    // 16 apart, on different banks of the permute (32 apart would share one)
     int sadr[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int rw = 2 * (mg & 1) + (p >> 1);
-      sadr[p] = 4 * ((mnq + 4 * rw) + 16 * (2 * (mhh & 1) + (mg >> 1)));
+      sadr[p] = 4 * ((mnq + 4 * rw) + 16 * (2 * (mhh & 1) + ((mg >> 1) ^ (mhh & 1))));
     }
     const int sidx = (mhh & 1) ? (int)0xEEEEEEEEu : 0x44444444;
     // fp8 P.V: this lane's A row r = mn_ holds head r & 3 for the channel half
@@ -926,7 +929,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
 
         if (SPV) {
           // PV: 8 sparse products of 64 tokens; B group m = (VGPR m of unpack
-          // half 0, VGPR m of half 1) of the lane's word, A from 4 permutes
+          // half 0, VGPR m ^ 2 of half 1) of the lane's word
           u4 ap;
 #pragma unroll
           for (int p = 0; p < 4; ++p) ap[p] = (uint32_t)__builtin_amdgcn_ds_bpermute(sadr[p], (int)pk[p & 1]);
@@ -934,7 +937,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
           for (int c = 0; c < 8; ++c) {
             const uint32_t w = cur.v[c >> 2][c & 3];
             const u4 h0 = unpack2v(w, 0), h1 = unpack2v(w, 1);
-            O[c] = smfmac(ap, u8v{h0[0], h1[0], h0[1], h1[1], h0[2], h1[2], h0[3], h1[3]}, O[c], sidx);
+            O[c] = smfmac(ap, u8v{h0[0], h1[2], h0[1], h1[3], h0[2], h1[0], h0[3], h1[1]}, O[c], sidx);
           }
         } else if (VAX == KVQ_TOKEN_WISE) {
           // PV: 8 channel tiles, 2 k-steps of 32 tokens

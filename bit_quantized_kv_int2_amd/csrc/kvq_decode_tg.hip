@@ -363,14 +363,16 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
       }
     // sparse P.V: A row mn_ = 4 x + r holds head x, replica r & 1; its
     // compressed dword p pairs with B group m = 2 (g >> 1) + (p & 1) of word
-    // row rw = 2 (g & 1) + (p >> 1), where the index picks the VGPR of unpack
-    // half r & 1: the P'' pair of tokens 16 rw + 4 (r & 1) + m and + 8, held
-    // by score lane (2 (r & 1) + (g >> 1), x + 4 rw) in pk[p & 1]
+    // row rw = 2 (g & 1) + (p >> 1): (VGPR m of unpack half 0, VGPR m ^ 2 of
+    // half 1), where the index picks replica r & 1's VGPR mr = m ^ 2 (r & 1):
+    // the P'' pair of tokens 16 rw + 4 (r & 1) + mr and + 8, held by score lane
+    // (2 (r & 1) + (mr >> 1), x + 4 rw) in pk[p & 1]; the replicas' source
+    // lanes are 16 apart, on different permute banks
     int sadr[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int rw = 2 * (mg & 1) + (p >> 1);
-      sadr[p] = 4 * ((mnq + 4 * rw) + 16 * (2 * (mhh & 1) + (mg >> 1)));
+      sadr[p] = 4 * ((mnq + 4 * rw) + 16 * (2 * (mhh & 1) + ((mg >> 1) ^ (mhh & 1))));
     }
     const int sidx = (mhh & 1) ? (int)0xEEEEEEEEu : 0x44444444;
     // byte offsets of the lane's coefficient pairs within an iteration
@@ -498,7 +500,7 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
         }
         if (SPV) {
           // 4 permutes, then one sparse product of 64 tokens per tile; B group
-          // m = (VGPR m of unpack half 0, VGPR m of half 1) of the lane's word
+          // m = (VGPR m of unpack half 0, VGPR m ^ 2 of half 1) of the lane's word
           u4 ap;
 #pragma unroll
           for (int p = 0; p < 4; ++p) ap[p] = (uint32_t)__builtin_amdgcn_ds_bpermute(sadr[p], (int)pk[p & 1]);
@@ -507,7 +509,7 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
             const int c = j * TPG + ct;
             const uint32_t w = cur.v[c];
             const u4 h0 = unpack2v(w, 0), h1 = unpack2v(w, 1);
-            O[c] = smfmac(ap, u8v{h0[0], h1[0], h0[1], h1[1], h0[2], h1[2], h0[3], h1[3]}, O[c], sidx);
+            O[c] = smfmac(ap, u8v{h0[0], h1[2], h0[1], h1[3], h0[2], h1[0], h0[3], h1[1]}, O[c], sidx);
           }
           continue;
         }
