@@ -263,12 +263,12 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   // fp16 token-wise V: the running output starts from kSeedV (set when the
   // first scores arrive), scaled along with it; kseed is its current value
   constexpr bool SEED = !PV8 && VAX == KVQ_TOKEN_WISE;
-  // INT2 fp16 token-wise V: P.V on the 2:4-sparse 16x16x64 product, with P''
-  // as its compressed A operand and the V codes as its dense B. Accumulator
+  // fp16 token-wise V: P.V on the 2:4-sparse 16x16x64 product, with P'' as
+  // its compressed A operand and the V codes as its dense B. Accumulator
   // tile c of lane (g, n) then holds head g, channel 8 n + c, in rows 0 and 1
   // (two replicas that split the tokens; rows 2 and 3 repeat them and are
   // never read)
-  constexpr bool SPV = SEED && BITS == 2;
+  constexpr bool SPV = SEED;
   float kseed = 0.f;
   // P'' = P * coef * 2^-F with max P'' < 2^14. Token-wise V: F follows the
   // largest scale this wave has seen and only grows (the accumulators are
@@ -630,11 +630,17 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     // (2 (r & 1) + (mr >> 1), x + 4 rw) holds in pk[p & 1] (mr and m share
     // their parity). The two replicas of a 32-lane half then read source lanes
     // 16 apart, on different banks of the permute (32 apart would share one)
+    // INT4: B lane g holds word rows g (unpack half 0) and g + 4 (half 1),
+    // VGPR m of a word codes m and m + 4; replica r's VGPR mr of word row
+    // wr = 2 (g & 1) + (p >> 1) + 4 r is the pair of tokens 8 wr + mr and + 4,
+    // which score lane (2 (p >> 1) + (mr >> 1), x + 4 (g & 1) + 8 r) holds in
+    // pk[p & 1]; sources again 16 apart per 32-lane half
     int sadr[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int rw = 2 * (mg & 1) + (p >> 1);
-      sadr[p] = 4 * ((mnq + 4 * rw) + 16 * (2 * (mhh & 1) + ((mg >> 1) ^ (mhh & 1))));
+      sadr[p] = BITS == 2 ? 4 * ((mnq + 4 * rw) + 16 * (2 * (mhh & 1) + ((mg >> 1) ^ (mhh & 1))))
+                          : 4 * ((mnq + 4 * (mg & 1) + 8 * (mhh & 1)) + 16 * (2 * (p >> 1) + ((mg >> 1) ^ (mhh & 1))));
     }
     const int sidx = (mhh & 1) ? (int)0xEEEEEEEEu : 0x44444444;
     // fp8 P.V: this lane's A row r = mn_ holds head r & 3 for the channel half
@@ -936,7 +942,8 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
             const uint32_t w = cur.v[c >> 2][c & 3];
-            const u4 h0 = unpack2v(w, 0), h1 = unpack2v(w, 1);
+            const u4 h0 = BITS == 4 ? unpack4v(w) : unpack2v(w, 0);
+            const u4 h1 = BITS == 4 ? unpack4v(cur.v[2 + (c >> 2)][c & 3]) : unpack2v(w, 1);
             O[c] = smfmac(ap, u8v{h0[0], h1[2], h0[1], h1[3], h0[2], h1[0], h0[3], h1[1]}, O[c], sidx);
           }
         } else if (VAX == KVQ_TOKEN_WISE) {

@@ -190,11 +190,11 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
   float lsum = 0.f;
   int F = 0;  // P'' = P * s * 2^-F / w, running per wave
   float kseed = 0.f;  // the running output's start value (kSeedV), scaled along
-  // INT2: P.V on the 2:4-sparse 16x16x64 product (P'' its compressed A, the
+  // P.V on the 2:4-sparse 16x16x64 product (P'' its compressed A, the
   // V codes its dense B); tile c of lane (g, n) then holds head g, channel
   // 16 c + n, in rows 0 and 1 (two replicas that split the tokens; rows 2 and
   // 3 repeat them and are never read)
-  constexpr bool SPV = BITS == 2;
+  constexpr bool SPV = true;
 
   // ---- (s, z) rows of a chunk: lane l takes TPL = 8 / NG consecutive tokens
   // of this wave's blocks (128-token blocks wv, wv + 4, .. of the chunk), all
@@ -368,11 +368,15 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
     // the P'' pair of tokens 16 rw + 4 (r & 1) + mr and + 8, held by score lane
     // (2 (r & 1) + (mr >> 1), x + 4 rw) in pk[p & 1]; the replicas' source
     // lanes are 16 apart, on different permute banks
+    // (INT4: word rows g and g + 4 in unpack halves 0 and 1, VGPR m of a word
+    // codes m and m + 4: replica r's pair of word row 2 (g & 1) + (p >> 1) + 4 r
+    // sits in score lane (2 (p >> 1) + (mr >> 1), x + 4 (g & 1) + 8 r))
     int sadr[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int rw = 2 * (mg & 1) + (p >> 1);
-      sadr[p] = 4 * ((mnq + 4 * rw) + 16 * (2 * (mhh & 1) + ((mg >> 1) ^ (mhh & 1))));
+      sadr[p] = BITS == 2 ? 4 * ((mnq + 4 * rw) + 16 * (2 * (mhh & 1) + ((mg >> 1) ^ (mhh & 1))))
+                          : 4 * ((mnq + 4 * (mg & 1) + 8 * (mhh & 1)) + 16 * (2 * (p >> 1) + ((mg >> 1) ^ (mhh & 1))));
     }
     const int sidx = (mhh & 1) ? (int)0xEEEEEEEEu : 0x44444444;
     // byte offsets of the lane's coefficient pairs within an iteration
@@ -508,7 +512,8 @@ __global__ void __launch_bounds__(kThreads, tg_groups_per_cu(BITS, NG)) decode_t
           for (int ct = 0; ct < TPG; ++ct) {
             const int c = j * TPG + ct;
             const uint32_t w = cur.v[c];
-            const u4 h0 = unpack2v(w, 0), h1 = unpack2v(w, 1);
+            const u4 h0 = BITS == 4 ? unpack4v(w) : unpack2v(w, 0);
+            const u4 h1 = BITS == 4 ? unpack4v(cur.v[8 + c]) : unpack2v(w, 1);
             O[c] = smfmac(ap, u8v{h0[0], h1[2], h0[1], h1[3], h0[2], h1[0], h0[3], h1[1]}, O[c], sidx);
           }
           continue;
