@@ -269,6 +269,13 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   // (two replicas that split the tokens; rows 2 and 3 repeat them and are
   // never read)
   constexpr bool SPV = SEED;
+  // INT2 channel-wise V on the sparse product too (SPVC): scalar outputs Oc
+  // (head g, channel 8 n + c of lane (g, n)), folded per iteration; lsum then
+  // follows the tiles' head
+  constexpr bool SPVC = !PV8 && VAX == KVQ_CHANNEL_WISE && BITS == 2;
+  float Oc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) Oc[c] = 0.f;
   float kseed = 0.f;
   // P'' = P * coef * 2^-F with max P'' < 2^14. Token-wise V: F follows the
   // largest scale this wave has seen and only grows (the accumulators are
@@ -812,12 +819,17 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
 #pragma unroll
             for (int j = 0; j < 4; ++j) O[c][j] = fmaf(O[c][j], so, ko);
           kseed = fmaf(kseed, sc, k0);
+        } else if (SPVC) {
+          const float so = __shfl(sc, mg);  // head mg's factor
+#pragma unroll
+          for (int c = 0; c < 8; ++c) Oc[c] *= so;
+          lsum *= so;
         } else {
 #pragma unroll
           for (int c = 0; c < 8; ++c) O[c] *= sc;
         }
         X *= sc;
-        lsum *= sc;
+        if (!SPVC) lsum *= sc;
         m_run = mn;
       }
       float P[4];
@@ -923,7 +935,11 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         // per iteration and take switching power off the matrix unit, whose
         // clock this loop follows (measured 2 % faster, results unchanged)
         u4 bp[2];
-        if (!SPV) {
+        u4 ap;  // sparse P.V A operand: 4 permutes
+        if (SPV || SPVC) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p) ap[p] = (uint32_t)__builtin_amdgcn_ds_bpermute(sadr[p], (int)pk[p & 1]);
+        } else {
 #pragma unroll
           for (int k = 0; k < 2; ++k)
 #pragma unroll
@@ -936,9 +952,6 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         if (SPV) {
           // PV: 8 sparse products of 64 tokens; B group m = (VGPR m of unpack
           // half 0, VGPR m ^ 2 of half 1) of the lane's word
-          u4 ap;
-#pragma unroll
-          for (int p = 0; p < 4; ++p) ap[p] = (uint32_t)__builtin_amdgcn_ds_bpermute(sadr[p], (int)pk[p & 1]);
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
             const uint32_t w = cur.v[c >> 2][c & 3];
@@ -946,6 +959,54 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
             const u4 h1 = BITS == 4 ? unpack4v(cur.v[2 + (c >> 2)][c & 3]) : unpack2v(w, 1);
             O[c] = smfmac(ap, u8v{h0[0], h1[2], h0[1], h1[3], h0[2], h1[0], h0[3], h1[1]}, O[c], sidx);
           }
+        } else if (SPVC) {
+          // sums of P'' per replica row from one product against +-w 2^-14:
+          // column 0 every slot (minus on the mirrored ones), column 1 the
+          // mirrored slots only (minus); the two VGPRs of a B group (m, m ^ 2)
+          // share the slot's parity but not its weight 4^m
+          u8v ob;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int m = (e & 1) ? ((e >> 1) ^ 2) : (e >> 1);
+            const uint32_t hb = (uint32_t)(2 * m + 1) << 10;  // w 2^-14
+            const uint32_t h = mn_ < 2 ? ((m & 1) ? (hb | 0x8000u) : (mn_ == 0 ? hb : 0u)) : 0u;
+            ob[e] = h | (h << 16);
+          }
+          const f4 xs = smfmac(ap, ob, f4{0.f, 0.f, 0.f, 0.f}, sidx);
+          // lane (x, 0): this iteration's sum P'' of head x; lane (x, 1): its mirrored part
+          const float xr = xs[0] + xs[1];
+          const float psum = __shfl(xr, 16 * mg) * 0x1p-10f;
+          const float pneg = __shfl(xr, 16 * mg + 1) * 0x1p-10f;
+          // the start value qmax sum_N P'' + kKappa sum P'' (taken back out
+          // through rho - kKappa): the group's first iteration seeds the two
+          // replica rows with half of its own each; the second adds its own
+          // in the fold
+          const float c0 = fmaf((float)((1 << BITS) - 1), pneg, kKappa * psum);
+          const unsigned char* vgb = lds + M::VA + vg_off<KAX, VAX>(gi, 8 * mn_);
+          // fresh products per iteration, 4 tiles at a time; each replica row
+          // starts from half of the start value; O_d += sigma_d (G_d + rho_d sum P'')
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            float ch = 0.5f * c0;
+            asm volatile("" : "+v"(ch));
+            f4 G4[4];
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+              const int c = 4 * hf + c4;
+              const uint32_t w = cur.v[c >> 2][c & 3];
+              const u4 h0 = unpack2v(w, 0), h1 = unpack2v(w, 1);
+              G4[c4] = smfmac(ap, u8v{h0[0], h1[2], h0[1], h1[3], h0[2], h1[0], h0[3], h1[1]},
+                              f4{ch, ch, 0.f, 0.f}, sidx);
+            }
+#pragma unroll
+            for (int c4 = 0; c4 < 4; c4 += 2) {
+              const int c = 4 * hf + c4;
+              const float4 sr = *(const float4*)(vgb + 8 * c);  // (sigma, rho) of channels 8 n + c, + 1
+              Oc[c] = fmaf(sr.x, fmaf(sr.y, psum, G4[c4][0] + G4[c4][1]), Oc[c]);
+              Oc[c + 1] = fmaf(sr.z, fmaf(sr.w, psum, G4[c4 + 1][0] + G4[c4 + 1][1]), Oc[c + 1]);
+            }
+          }
+          lsum += psum;
         } else if (VAX == KVQ_TOKEN_WISE) {
           // PV: 8 channel tiles, 2 k-steps of 32 tokens
 #pragma unroll
@@ -1061,6 +1122,11 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         for (int j = 0; j < 4; ++j) O[c][j] = fmaf(O[c][j], s24, offk);
     }
     lw = lsum;
+  } else if (SPVC) {
+    const float s24 = ldexpf(1.f, F + 24);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) Oc[c] *= s24;
+    lw = __shfl(lsum, 16 * n) * s24;  // lanes (0, n < 4): head n
   } else {
     const float s24 = ldexpf(1.f, F + 24);
 #pragma unroll
@@ -1092,11 +1158,11 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         for (int c = 0; c < 4; ++c) mo[(wv * 4 + x) * kHeadDim + 8 * n + 2 * c + g] = O[c][x] * fx[x];
     }
     if (n < 4 && g == 0) ml[(wv * 4 + n) * 2 + 1] = lw * f;
-  } else if (SPV) {
+  } else if (SPV || SPVC) {
     const float fo = __shfl(f, g);  // head g's factor
     float* dst = mo + (wv * 4 + g) * kHeadDim + 8 * n;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) dst[c] = O[c][0] * fo;
+    for (int c = 0; c < 8; ++c) dst[c] = (SPVC ? Oc[c] : O[c][0]) * fo;
     if (n < 4 && g == 0) ml[(wv * 4 + n) * 2 + 1] = lw * f;
   } else if (n < 4) {
     float* dst = mo + (wv * 4 + n) * kHeadDim + 32 * g;
