@@ -658,11 +658,18 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     // v_perm selectors of the A row's two halves: byte-interleave two
     // gathered dwords (even / odd A dwords), or 0x0C (a zero byte) in every
     // position for the half of the other channel
+    // INT4: lane groups 1 and 3 gather the dwords of each pair in the other
+    // order (qd ^ 1). Their sources then lie 16 lanes from those of lane
+    // groups 0 and 2 instead of 32, on other banks of the permute; the swap
+    // exchanges the two inputs of each v_perm below, which bit 2 of every
+    // live selector byte undoes
+    const int qsw = BITS == 4 ? (mg & 1) : 0;
+    const uint32_t sflip = qsw ? 0x04040404u : 0u;
     uint32_t asel[2][2];
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      asel[hf][0] = hf == arow_j ? 0x05010400u : 0x0C0C0C0Cu;
-      asel[hf][1] = hf == arow_j ? 0x07030602u : 0x0C0C0C0Cu;
+      asel[hf][0] = hf == arow_j ? 0x05010400u ^ sflip : 0x0C0C0C0Cu;
+      asel[hf][1] = hf == arow_j ? 0x07030602u ^ sflip : 0x0C0C0C0Cu;
     }
     int asrc[4];
 #pragma unroll
@@ -672,7 +679,8 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         const int gi = (qd >> 1) | ((qd & 1) << 1);  // 0, 2, 1, 3
         ls = (mhh + 4 * mg) + 16 * gi;
       } else {
-        const int gi = 2 * (mg & 1) + (qd & 1), nq = (mg >> 1) + 2 * (qd >> 1);
+        const int qs = qd ^ qsw;
+        const int gi = 2 * (mg & 1) + (qs & 1), nq = (mg >> 1) + 2 * (qs >> 1);
         ls = (mhh + 4 * nq) + 16 * gi;
       }
       asrc[qd] = 4 * ls;
