@@ -119,6 +119,18 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   // lane roles: C/B layout column n = head (n & 3) + 4 q, lane group g;
   // A layout row ri
   const int n = lane & 15, g = lane >> 4, hh = n & 3, nq = n >> 2;
+  // INT2 fp16 q.K^T on the 2:4-sparse product (SQK): the score registers
+  // that lane L holds with the dense product sit in lane perm(L), perm
+  // swapping lane bits 5:4 and 1:0; sl is this lane's index in the dense
+  // layout, and everything that follows the scores uses it
+  constexpr bool SQK = BITS == 2 && !FP8;
+  auto perm = [](int l) { return ((l & 3) << 4) | (l & 12) | (l >> 4); };
+  // and lane 16 a + b loads the K row that dense-layout lane 16 (b >> 2) +
+  // 4 (b & 3) + a loads (the token of score slot a in its column b)
+  auto kperm = [](int l) { return ((l & 12) << 2) | ((l & 3) << 2) | (l >> 4); };
+  const int kl = SQK ? kperm(lane) : lane;
+  const int sl = SQK ? perm(lane) : lane;
+  const int sn = sl & 15, sg = sl >> 4, shh = sn & 3;
   const int ri = lane & 15;
 
   // ---- code loads for one 64-token iteration ---------------------------
@@ -174,9 +186,23 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   int pg_next = 0;  // paged: physical page of this wave's next iteration
   {
     const int t0 = tb + 2 * wv * C::TIT;
-    if (t0 < te) load_codes(t0, cur, lane_koff(g, ri), lane_voff(g, ri));
+    if (t0 < te) load_codes(t0, cur, lane_koff(kl >> 4, kl & 15), lane_voff(g, ri));
     if (PAGED && next_it(t0) < te) pg_next = page_at(next_it(t0));
   }
+
+  // q'' row of one head, 16 B per dense k-step s (piece s >> 3, dword
+  // (s >> 1) & 3, unpack half s & 1; VGPR m = 0..3). Sparse q.K^T reads it as
+  // the compressed A operand of product s & 7: A lane group g takes VGPRs
+  // 2 (g >> 1) and + 1 of piece 0, then of piece 1, so a k-step's 16 B go to
+  // two 8-byte places in the 32 B of that product
+  auto put_qrow = [&](unsigned char* row, int ks, u4 w) {
+    if (SQK) {
+      *(u2*)(row + 32 * (ks & 7) + 8 * (ks >> 3)) = u2{w[0], w[1]};
+      *(u2*)(row + 32 * (ks & 7) + 16 + 8 * (ks >> 3)) = u2{w[2], w[3]};
+    } else {
+      ((u4*)row)[ks] = w;
+    }
+  };
 
   // ---- query: once per split -------------------------------------------------
   {
@@ -243,7 +269,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         float v1 = qs[qh * 128 + C::k_run(s, 1) + m] * two_mE * C::inv_w(m);
         wds[m] = pack_f16x2(v0, v1);
       }
-      ((u4*)(lds + M::QB + qh * M::HEAD_STRIDE))[s] = u4{wds[0], wds[1], wds[2], wds[3]};
+      put_qrow(lds + M::QB + qh * M::HEAD_STRIDE, s, u4{wds[0], wds[1], wds[2], wds[3]});
     }
     __syncthreads();
   }
@@ -581,7 +607,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
           wds[m] = mul_f16x2(qv[m], spk[m]);
           bias = fmaf(f16lo(wds[m]), rho[m], fmaf(f16hi(wds[m]), rho[4 + m], bias));
         }
-        if (glive) ((u4*)(lds + M::QB + gl * M::GROUP_STRIDE + qh_i * M::HEAD_STRIDE))[ck_s] = wds;
+        if (glive) put_qrow(lds + M::QB + gl * M::GROUP_STRIDE + qh_i * M::HEAD_STRIDE, ck_s, wds);
         bias = row_sum(bias);
         hb = ck_s == qh_i ? bias : hb;
       }
@@ -612,12 +638,18 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     int mlane = lane;
     asm volatile("" : "+v"(mlane));
     const int mn_ = mlane & 15, mg = mlane >> 4, mhh = mn_ & 3, mnq = mn_ >> 2;
-    const uint32_t koff = lane_koff(mg, mn_), voff = lane_voff(mg, mn_);
-    // compact scores: lane (n, g) holds tokens tk0 + {0, D2, 1, D2 + 1} (j = 0..3)
-    const int tk0 = C::tok(mnq, mg, 0);
+    // the same in the dense score layout (sparse q.K^T: of the permuted lane)
+    const int msl = SQK ? perm(mlane) : mlane;
+    const int smn = msl & 15, smg = msl >> 4, smhh = smn & 3, smnq = smn >> 2;
+    const int mkl = SQK ? kperm(mlane) : mlane;
+    const uint32_t koff = lane_koff(mkl >> 4, mkl & 15), voff = lane_voff(mg, mn_);
+    // compact scores: score lane (n, g) holds tokens tk0 + {0, D2, 1, D2 + 1} (j = 0..3)
+    const int tk0 = C::tok(smnq, smg, 0);
     // B operand of QK^T is block diagonal: column (head, q) is nonzero only in
     // k-group q, so only lanes with g == q read q''; the others read zeros
-    const bool qlive = mg == mnq;
+    // (sparse q.K^T: A row mn_ = 4 x + slot is head x, token slot mhh, whose
+    // tokens lane group g holds when slot >> 1 == g & 1; the others read zeros)
+    const bool qlive = SQK ? (mhh >> 1) == (mg & 1) : mg == mnq;
     // PV B operand VGPR m of k-step k comes from lane src[k][m >> 1], register pk[m & 1]
     int src[2][2];
 #pragma unroll
@@ -646,8 +678,9 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int rw = 2 * (mg & 1) + (p >> 1);
-      sadr[p] = BITS == 2 ? 4 * ((mnq + 4 * rw) + 16 * (2 * (mhh & 1) + ((mg >> 1) ^ (mhh & 1))))
-                          : 4 * ((mnq + 4 * (mg & 1) + 8 * (mhh & 1)) + 16 * (2 * (p >> 1) + ((mg >> 1) ^ (mhh & 1))));
+      const int sd = BITS == 2 ? (mnq + 4 * rw) + 16 * (2 * (mhh & 1) + ((mg >> 1) ^ (mhh & 1)))
+                               : (mnq + 4 * (mg & 1) + 8 * (mhh & 1)) + 16 * (2 * (p >> 1) + ((mg >> 1) ^ (mhh & 1)));
+      sadr[p] = 4 * (SQK ? perm(sd) : sd);  // the score lane's actual index
     }
     const int sidx = (mhh & 1) ? (int)0xEEEEEEEEu : 0x44444444;
     // fp8 P.V: this lane's A row r = mn_ holds head r & 3 for the channel half
@@ -694,7 +727,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       const int slot = (tk0 + aa) % C::TPW;
       cw[aa] = (aa ? -1.f : 1.f) * ldexpf(1.f, -F) / (float)(1 << (BITS * (slot % C::SLOTS)));
     }
-    const float Qh = KAX == KVQ_TOKEN_WISE ? red[20 + mhh] : 0.f;
+    const float Qh = KAX == KVQ_TOKEN_WISE ? red[20 + smhh] : 0.f;
     // token-wise V: byte offsets of this lane's coefficient pairs within an
     // iteration. An iteration starts at a multiple of 64 tokens (32 pairs,
     // two whole 16-pair blocks), so pair rel / 2 + r sits at 4 rel + the
@@ -763,6 +796,35 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
             c0 = mfma8(av, cat8(qb[2 * j], qb[2 * j + 1]), c0, kE8M0One);
             c1 = mfma8(av, cat8(qb[8 + 2 * j], qb[9 + 2 * j]), c1, kE8M0One - 4);
           }
+        } else if (SQK) {
+          // 8 sparse products of 16 channels x 4 tokens per column. Lane group
+          // pairs (0, 1) and (2, 3) trade halves (odd rows of the piece-0
+          // dwords with even rows of the piece-1 dwords): then rows 0 and 2
+          // hold piece 0 and rows 1 and 3 piece 1 of two tokens, x (the even
+          // row's, slots 0 and 2) and y (the odd row's, slots 1 and 3); B group
+          // m is (VGPR m of x, VGPR m of y), and the index takes x or y
+          u4 kx, ky;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const auto r = __builtin_amdgcn_permlane16_swap(cur.k[0][i], cur.k[1][i], false, false);
+            kx[i] = (uint32_t)r[0];
+            ky[i] = (uint32_t)r[1];
+          }
+          const int qbase = M::QB + (KAX == KVQ_CHANNEL_WISE ? gi : 0) * M::GROUP_STRIDE;
+          // read s's 8 live 16-byte chunks fill 8 consecutive bank quads from
+          // the group's base + 2 s; the zero row sits 8 quads on, at zero-region
+          // quad zq + 2 s (zq < 16 and s < 8 stay inside the region)
+          const int zq = (qbase / 16 + 8 - M::QZ / 16) & 15;
+          const unsigned char* abase = qlive ? lds + qbase + mnq * M::HEAD_STRIDE + 16 * (mg >> 1)
+                                             : lds + M::QZ + 16 * zq;
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            const u4 av = *(const u4*)(abase + 32 * s);
+            const u4 x = unpack2(kx[s >> 1], s & 1), y = unpack2(ky[s >> 1], s & 1);
+            const u8v bv = u8v{x[0], y[0], x[1], y[1], x[2], y[2], x[3], y[3]};
+            if (s & 1) c1 = smfmac(av, bv, c1, sidx);
+            else c0 = smfmac(av, bv, c0, sidx);
+          }
         } else {
 #pragma unroll
           for (int s = 0; s < 16; ++s) {
@@ -777,7 +839,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         // into the score's affine map (one add per iteration, not four);
         // score(j) is the score itself, for the rare moves of the maximum
         if (KAX == KVQ_CHANNEL_WISE) {
-          sb = ((const float2*)(lds + M::KB))[gi * 4 + mhh];
+          sb = ((const float2*)(lds + M::KB))[gi * 4 + smhh];
           const float nb = sb.y - m_run;
 #pragma unroll
           for (int j = 0; j < 4; ++j) S[j] = fmaf(acc[j], sb.x, nb);
@@ -813,7 +875,8 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
         float Sr[4];  // the scores themselves (masked tokens stay -inf)
 #pragma unroll
         for (int j = 0; j < 4; ++j) Sr[j] = S[j] == -INFINITY ? -INFINITY : score(j);
-        const float mn = fmaxf(m_run, head_max(fmaxf(fmaxf(Sr[0], Sr[1]), fmaxf(Sr[2], Sr[3]))));
+        const float lm = fmaxf(fmaxf(Sr[0], Sr[1]), fmaxf(Sr[2], Sr[3]));
+        const float mn = fmaxf(m_run, SQK ? row_max(lm) : head_max(lm));
 #pragma unroll
         for (int j = 0; j < 4; ++j) S[j] = Sr[j] - mn;
         const float sc = exp2_fast(m_run - mn);
@@ -821,14 +884,15 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
           // the first scores of this wave (sc = 0) plant the seed
           const float k0 = m_run == -INFINITY ? kSeedV : 0.f;
           // sparse P.V: lane (g, n)'s tiles hold head g, whose scale score lane g has
-          const float so = SPV ? __shfl(sc, mg) : sc, ko = SPV ? __shfl(k0, mg) : k0;
+          const int hsrc = SQK ? 16 * mg : mg;  // the score lane of head mg
+          const float so = SPV ? __shfl(sc, hsrc) : sc, ko = SPV ? __shfl(k0, hsrc) : k0;
 #pragma unroll
           for (int c = 0; c < 8; ++c)
 #pragma unroll
             for (int j = 0; j < 4; ++j) O[c][j] = fmaf(O[c][j], so, ko);
           kseed = fmaf(kseed, sc, k0);
         } else if (SPVC) {
-          const float so = __shfl(sc, mg);  // head mg's factor
+          const float so = __shfl(sc, SQK ? 16 * mg : mg);  // head mg's factor
 #pragma unroll
           for (int c = 0; c < 8; ++c) Oc[c] *= so;
           lsum *= so;
@@ -1113,13 +1177,13 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       for (int x = 0; x < 4; ++x) O[c][x] = (O[c][x] + __shfl_xor(O[c][x], 32) + offx[x]) * sF;
     lw = lsum;
   } else if (VAX == KVQ_TOKEN_WISE) {
-    lsum = head_sum(lsum);
-    const float off = head_sum(X[0]);  // head n & 3's offset sum (every lane of the head)
+    lsum = SQK ? row_sum(lsum) : head_sum(lsum);
+    const float off = SQK ? row_sum(X[0]) : head_sum(X[0]);  // the lane's head's offset sum (every lane of the head)
     const float s24 = ldexpf(1.f, F + 24), sF = ldexpf(1.f, F);
     // (O - kseed) 2^(F + 24) + off 2^F
     if (SPV) {
       // head g's two replica rows, each started from the seed
-      const float offk = __shfl(fmaf(-2.f * kseed, s24, off * sF), g);
+      const float offk = __shfl(fmaf(-2.f * kseed, s24, off * sF), SQK ? 16 * g : g);
 #pragma unroll
       for (int c = 0; c < 8; ++c) O[c][0] = fmaf(O[c][0] + O[c][1], s24, offk);
     } else {
@@ -1134,7 +1198,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     const float s24 = ldexpf(1.f, F + 24);
 #pragma unroll
     for (int c = 0; c < 8; ++c) Oc[c] *= s24;
-    lw = __shfl(lsum, 16 * n) * s24;  // lanes (0, n < 4): head n
+    lw = __shfl(lsum, 16 * sn) * s24;  // score lanes (0, sn < 4): head sn
   } else {
     const float s24 = ldexpf(1.f, F + 24);
 #pragma unroll
@@ -1146,13 +1210,13 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
   __syncthreads();  // main-loop LDS no longer needed
   float* mo = (float*)(lds + M::MO);
   float* ml = (float*)(lds + M::ML);
-  if (n < 4 && g == 0) {
-    ml[(wv * 4 + n) * 2] = m_run;
+  if (sn < 4 && sg == 0) {
+    ml[(wv * 4 + sn) * 2] = m_run;
   }
   __syncthreads();
   float mall = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) mall = fmaxf(mall, ml[(w * 4 + hh) * 2]);
+  for (int w = 0; w < kWaves; ++w) mall = fmaxf(mall, ml[(w * 4 + shh) * 2]);
   const float f = (m_run == -INFINITY) ? 0.f : exp2_fast(m_run - mall);
   __syncthreads();
   if (PV8) {
@@ -1167,11 +1231,11 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
     }
     if (n < 4 && g == 0) ml[(wv * 4 + n) * 2 + 1] = lw * f;
   } else if (SPV || SPVC) {
-    const float fo = __shfl(f, g);  // head g's factor
+    const float fo = __shfl(f, SQK ? 16 * g : g);  // head g's factor
     float* dst = mo + (wv * 4 + g) * kHeadDim + 8 * n;
 #pragma unroll
     for (int c = 0; c < 8; ++c) dst[c] = (SPVC ? Oc[c] : O[c][0]) * fo;
-    if (n < 4 && g == 0) ml[(wv * 4 + n) * 2 + 1] = lw * f;
+    if (sn < 4 && sg == 0) ml[(wv * 4 + sn) * 2 + 1] = lw * f;
   } else if (n < 4) {
     float* dst = mo + (wv * 4 + n) * kHeadDim + 32 * g;
 #pragma unroll
@@ -1180,7 +1244,7 @@ __global__ void __launch_bounds__(kThreads, groups_per_cu(BITS, VAX)) decode_ker
       for (int c = 0; c < 8; ++c) dst[8 * j + c] = O[c][j] * f;
     if (g == 0) ml[(wv * 4 + n) * 2 + 1] = lw * f;
   }
-  if (n < 4 && g == 0) ml[(wv * 4 + n) * 2] = mall;
+  if (sn < 4 && sg == 0) ml[(wv * 4 + sn) * 2] = mall;
   __syncthreads();
   {
     const int qh = tid >> 6, d = (tid & 63) * 2;
