@@ -12,10 +12,14 @@
 //                                    scaled per 128-token group, never across groups.
 //
 // gfx950 mapping
-//   * Matrix unit: v_mfma_f32_16x16x32_f16. A = codes (16 rows x 32 k),
-//     B = folded query / probabilities (32 k x 16 columns). In q.K^T the
-//     columns are 4 heads x 4 token quarters (block diagonal over k); in P.V
-//     the 4 query heads of a KV head fill columns 0-3 and the others are zero.
+//   * Matrix unit. Dense form v_mfma_f32_16x16x32_f16 (INT4 q.K^T, INT4
+//     channel-wise-V P.V, the fp8 variants use scaled fp8 products): A =
+//     codes (16 rows x 32 k), B = folded query / probabilities; in q.K^T the
+//     B columns are 4 heads x 4 token quarters (block diagonal over k). Sparse
+//     form v_smfmac_f32_16x16x64_f16 (INT2 q.K^T and P.V, INT4 token-wise-V
+//     P.V): the block-diagonal operand, q'' or P'', becomes the 2:4-sparse A
+//     (its two nonzeros of every four k and their index) and the codes the
+//     dense B, at twice the multiply-adds per issue slot.
 //   * Operand construction: a 2- or 4-bit code ANDed out of its packed 32-bit
 //     word, left at its bit offset inside a 16-bit lane with every other bit
 //     zero, is the binary16 subnormal c * 2^k * 2^-24 (k = the code's bit
@@ -27,8 +31,9 @@
 //     fp16 operand the matrix unit actually consumed, so rounding q*s or P*s
 //     to fp16 perturbs only the weights, not the cancellation between the
 //     code term and the offset term.
-//   * Token <-> tile maps are chosen so the QK^T accumulator layout is the PV
-//     B-operand layout: no cross-lane shuffles between the two products.
+//   * Token <-> lane maps are chosen so that each score lane's probability
+//     pairs are the token pairs of one packed V VGPR: P'' reaches the P.V
+//     operand with one ds_bpermute per operand dword.
 //   * A work-group takes one split (a multiple of 256 tokens) of one
 //     (sequence, KV head) row, in the per-XCD order of work_item, and walks it
 //     in 2048-token chunks. Per chunk, each wave builds the fold operands of
@@ -41,7 +46,7 @@
 //     token-wise V sums P''_t (w rho)_t on the vector unit (four fmas per
 //     lane and iteration; on gfx950 a matrix product and vector work do not
 //     overlap, so an extra tile would cost more); channel-wise V takes
-//     sum_t P''_t from a 9th A tile of the subnormal "code 1" pattern.
+//     sum_t P''_t from one more product against a fixed "code 1" pattern.
 #include <math.h>
 
 #include "kvq_internal.h"
