@@ -11,11 +11,13 @@
 //   P.V, operand-fold per channel group:
 //     O_d = sum_t (P_t s_{t,j(d)}) c_{t,d} + sum_t P_t z_{t,j(d)}
 //     every 16-channel tile lies in one group (tile c = channels 16c..16c+15)
-//     and takes that group's P'' operand; the offset sum of each group runs
-//     on the vector unit over the same rounded P'' (four fmas per group and
-//     iteration in place of two matrix products, which the vector unit would
-//     wait out on gfx950).
-// Everything else (block-diagonal QK^T, token maps, subnormal operands,
+//     and takes that group's P'' operand, as the compressed A operand of the
+//     2:4-sparse 16x16x64 product (the V codes its dense B; one product per
+//     tile and iteration); the offset sum of each group runs on the vector
+//     unit over the same rounded P'' (four fmas per group and iteration in
+//     place of two matrix products, which the vector unit would wait out on
+//     gfx950).
+// Everything else (block-diagonal dense QK^T, token maps, subnormal operands,
 // consistent offsets, lazy softmax, wave-local chunks) is as in the G = 128
 // kernel; a chunk holds 2048 / NG tokens so its fold operands fit the same LDS.
 #include "kvq_internal.h"
